@@ -1,0 +1,202 @@
+/*
+ * pq.h — C ABI of the MI355X (gfx950) quantized-weight decode library.
+ *
+ * The library implements the weight-streaming hot path of batch-1 and small-M
+ * (speculative-verify) decode through quantized MoE expert weights:
+ *
+ *   - Sionic AI blog, "GPU 커널부터 새로 짜서 GLM-5.2 속도 10배 올리기"
+ *     (GLM-5.2 made ten times faster by rewriting the GPU kernels), cited
+ *     below as [Sionic]: intro (decode streams every active weight from HBM
+ *     once, so it is bandwidth bound), §1 (a batch-1 gate_up launches too few
+ *     blocks; live FP8 activation quantisation must overlap the weight loads;
+ *     split-K across the chip), §2 (one scale per K block must not stall the
+ *     load pipeline), §4 (quantisation fused into the GEMM, few kernels),
+ *     §5-6 (one weight read serves several verified tokens).
+ *   - aiwitness post "GLM 5.3 Flash Q4 @ 60tps / 550tps on M3 Ultra" ([M3]):
+ *     Q4 weight-streaming decode; merging small kernels into few dispatches.
+ *   - rbeckner.com "Qwen 3.8-27B M1 Ultra에서 ..." ([M1]): a 256-expert MoE is
+ *     dispatch bound when each expert op is its own launch.
+ *
+ * Conventions for every call:
+ *   - Data pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *     16-byte aligned, contiguous, row-major.  bf16 and fp16 values are passed
+ *     as their 16-bit patterns (uint16_t).  FP8 is OCP E4M3FN (max 448).
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Every compute call is asynchronous on that stream.
+ *   - The caller owns all buffers (inputs, outputs, workspace).  Outside of
+ *     pq_workspace_init the library allocates nothing and keeps no per-call
+ *     state; distinct workspaces may be used from different threads.  One
+ *     workspace must not be used by two calls that can overlap in time.
+ *   - Arguments are validated on the host before anything is launched.  On a
+ *     validation failure the call returns a negative pq_status, launches
+ *     nothing and leaves every output untouched.  A failing HIP launch returns
+ *     PQ_ERR_HIP and the HIP error code is kept per thread
+ *     (pq_last_hip_error).  Errors raised while a kernel runs (a bad expert id
+ *     in device memory, the spin-wait watchdog) are recorded in the workspace
+ *     and reported by pq_workspace_check.
+ *   - Workspaces must be zeroed once with pq_workspace_init before first use.
+ *     Kernels leave every counter they touch at zero when they finish, so no
+ *     per-call clearing is needed.
+ */
+#ifndef PQ_H
+#define PQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PQ_OK = 0,
+  PQ_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  PQ_ERR_SHAPE = -2,       /* a size is out of range or not a required multiple  */
+  PQ_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned                   */
+  PQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than *_workspace()    */
+  PQ_ERR_UNSUPPORTED = -5, /* the current device is not gfx950, or no device     */
+  PQ_ERR_HIP = -6,         /* a HIP runtime call failed (see pq_last_hip_error)  */
+  PQ_ERR_TIMEOUT = -7,     /* a kernel's bounded spin-wait gave up (workspace)   */
+  PQ_ERR_BAD_EXPERT = -8   /* a top-k expert id in device memory was out of range */
+} pq_status;
+
+typedef enum {
+  PQ_EPI_NONE = 0,
+  /* N = 2*Nh weight rows, rows [0,Nh) gate and [Nh,N) up; the output is
+   * h[m,i] = silu(gate[m,i]) * up[m,i], bf16 [M,Nh]  (fused gate_up epilogue) */
+  PQ_EPI_SILU_MUL = 1
+} pq_epilogue;
+
+/* ------------------------------------------------------------------------- */
+/* Block quantisers (weight preparation and the live activation rule).        */
+/* ------------------------------------------------------------------------- */
+
+/* FP8 block quantisation of `rows` rows of K values, one fp32 scale per 128
+ * consecutive values of a row ([Sionic] §1 live FP8 activation quantisation;
+ * §2 one scale per K block).  For every block: s = fp32(amax / 448) by IEEE
+ * division (s = 1 if amax = 0), code = E4M3(fp32(v / s)) rounded to nearest
+ * even with saturation to +-448; NaN -> 0x7F.
+ *   in      : bf16 [rows,K] if in_is_f32 == 0, fp32 [rows,K] otherwise
+ *   codes   : uint8 [rows,K] (output)       scales : fp32 [rows,K/128] (output)
+ * Constraints: rows >= 1, K >= 128, K % 128 == 0.  Inputs must be finite. */
+int pq_quantize_fp8(const void* in, int in_is_f32, int rows, int K,
+                    uint8_t* codes, float* scales, void* stream);
+
+/* Symmetric int4 quantisation with one fp16 scale per 32 consecutive values
+ * of a row ([M3] Q4 weight-streaming decode).  s = fp16_rne(fp32(amax / 7)),
+ * q = clamp(rne(fp32(w / fp32(s))), -8, 7), q = 0 where s == 0; stored as
+ * offset-binary nibbles u = q + 8, low nibble = even k.
+ *   w      : fp32 [N,K]           packed : uint8 [N,K/2] (output)
+ *   scales : fp16 [N,K/32] (output)
+ * Constraints: N >= 1, K >= 32, K % 32 == 0.  Inputs must be finite. */
+int pq_quantize_q4(const float* w, int N, int K, uint8_t* packed, uint16_t* scales,
+                   void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Block-scaled FP8 weight-streaming GEMV / skinny GEMM with live activation   */
+/* quantisation fused in ([Sionic] §1 and §4; §2 scales per K block).         */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes pq_gemv_fp8 needs for this shape (split-K partials and
+ * completion counters); 0 when no split is used.  Returns 0 for invalid
+ * shapes as well (pq_gemv_fp8 then reports the error). */
+size_t pq_gemv_fp8_workspace(int M, int K, int N, int epi);
+
+/* y = epi(bf16( sum_b s_x[m,b] s_w[n,b] sum_{k in b} q_x[m,k] q_w[n,k] ))
+ * where (q_x, s_x) is the live FP8 quantisation of x (rule of
+ * pq_quantize_fp8), accumulated in fp32.
+ *   x       : bf16 [M,K]                  w : E4M3 [N,K]   w_scale : fp32 [N,K/128]
+ *   y       : bf16 [M,N] (PQ_EPI_NONE) or bf16 [M,N/2] (PQ_EPI_SILU_MUL)
+ *   xq_dbg  : nullable, E4M3 [M,K]  — the quantised activation codes
+ *   xs_dbg  : nullable, fp32 [M,K/128] — the activation scales
+ *   ws      : device workspace of ws_bytes >= pq_gemv_fp8_workspace(...)
+ *             (may be NULL when that is 0), zeroed once by pq_workspace_init.
+ * Constraints: 1 <= M <= 8, K % 128 == 0, 128 <= K <= 16384, N >= 1,
+ * N even under PQ_EPI_SILU_MUL. */
+int pq_gemv_fp8(const uint16_t* x, int M, int K,
+                const uint8_t* w, const float* w_scale, int N,
+                int epi, uint16_t* y,
+                uint8_t* xq_dbg, float* xs_dbg,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* int4 g32 weight-streaming GEMV (W4A16): [M3] Q4 decode.                    */
+/* ------------------------------------------------------------------------- */
+
+size_t pq_gemv_q4_workspace(int M, int K, int N, int epi);
+
+/* y = epi(bf16( sum_g s[n,g] sum_{k in g} x[m,k] q[n,k] )), fp32 accumulation.
+ *   x : bf16 [M,K]    w : nibbles [N,K/2] (layout of pq_quantize_q4)
+ *   w_scale : fp16 [N,K/32]    y : bf16 [M,N] or [M,N/2] under PQ_EPI_SILU_MUL
+ * Constraints: 1 <= M <= 8, K % 256 == 0, 256 <= K <= 20480, N >= 1,
+ * N even under PQ_EPI_SILU_MUL. */
+int pq_gemv_q4(const uint16_t* x, int M, int K,
+               const uint8_t* w, const uint16_t* w_scale, int N,
+               int epi, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Routed MoE decode layer in ONE kernel launch ([Sionic] intro, §4, §5;      */
+/* [M1] dispatch-bound MoE; [M3] merging small kernels).                      */
+/* ------------------------------------------------------------------------- */
+
+size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k);
+
+/* For each token m (1 <= M <= 8):
+ *   route  : if router_logits != NULL, take the top_k experts of the fp32
+ *            logits [M,E] in descending order (ties to the lower id) and
+ *            softmax weights over the selected logits; they are WRITTEN to
+ *            topk_ids / topk_w.  If router_logits == NULL, topk_ids int32
+ *            [M,top_k] and topk_w fp32 [M,top_k] are READ as inputs.
+ *   per slot j with expert e:
+ *            h  = silu(gate_e(q(x_m))) * up_e(q(x_m))      -> bf16 [I]
+ *            y  = down_e(q(h))                             fp32 [H]
+ *   out[m] = bf16( sum_j w[m,j] * y_j ), j in slot order.
+ *   q(.) is the live FP8 quantisation of pq_quantize_fp8.  Every distinct
+ *   expert of the call is streamed from HBM once for all tokens routed to it.
+ *   x   : bf16 [M,H]
+ *   w13 : E4M3 [E,2I,H] (gate rows then up rows)   s13 : fp32 [E,2I,H/128]
+ *   w2  : E4M3 [E,H,I]                              s2  : fp32 [E,H,I/128]
+ *   out : bf16 [M,H]
+ *   h_dbg, hq_dbg, hs_dbg : nullable bf16 [M,top_k,I], E4M3 [M,top_k,I],
+ *            fp32 [M,top_k,I/128] — the intermediate h and its quantisation.
+ *   ws  : workspace of ws_bytes >= moe_decode_layer_workspace(...)
+ * Constraints: 1 <= M <= 8, 1 <= top_k <= 8, top_k <= E <= 1024,
+ * H % 128 == 0, I % 128 == 0, 128 <= H <= 16384, 128 <= I <= 16384.
+ * Router logits must be finite.  The kernel needs the whole GPU while it runs
+ * (its blocks wait on each other; a bounded wait records PQ_ERR_TIMEOUT). */
+int moe_decode_layer(const uint16_t* x, int M, int H,
+                     const float* router_logits,
+                     int32_t* topk_ids, float* topk_w,
+                     int E, int top_k, int I,
+                     const uint8_t* w13, const float* s13,
+                     const uint8_t* w2, const float* s2,
+                     uint16_t* out,
+                     uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Workspace and error helpers.                                               */
+/* ------------------------------------------------------------------------- */
+
+/* Zero a workspace (asynchronously on `stream`); call once per allocation. */
+int pq_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronise `stream` and return the error recorded in the workspace by a
+ * kernel (PQ_OK, PQ_ERR_TIMEOUT or PQ_ERR_BAD_EXPERT); the record is cleared. */
+int pq_workspace_check(void* ws, void* stream);
+
+/* Human-readable name of a pq_status. */
+const char* pq_strerror(int status);
+
+/* HIP error code of the last PQ_ERR_HIP returned on the calling thread. */
+int pq_last_hip_error(void);
+
+/* Kernel launches one call makes for these arguments (1 for every entry
+ * point in this library; reported by the bench as launches per layer). */
+int pq_launches_per_call(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ_H */

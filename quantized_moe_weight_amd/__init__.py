@@ -1,0 +1,197 @@
+"""MI355X (gfx950) quantized-weight decode: Python binding of the C-ABI library.
+
+Every step of the decode path runs in the HIP kernels of ``libpqmoe.so``;
+this module only checks tensor metadata, hands raw device pointers and the
+current HIP stream to the C calls of ``include/pq.h`` and raises on a
+non-zero status.  PyTorch provides device memory and streams.  There is no
+CPU fallback: the library must be built (see ``build.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemv_q4", "moe_decode_layer",
+           "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call",
+           "EPI_NONE", "EPI_SILU_MUL", "lib"]
+
+EPI_NONE = 0
+EPI_SILU_MUL = 1
+
+
+class PqError(RuntimeError):
+    """A pq_* call returned a non-zero pq_status."""
+
+    def __init__(self, what: str, status: int):
+        lib = _lib.load()
+        msg = lib.pq_strerror(status).decode()
+        super().__init__(f"{what}: {msg} (status {status}, hip error {lib.pq_last_hip_error()})")
+        self.status = status
+
+
+def lib():
+    return _lib.load()
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise PqError(what, status)
+
+
+def _need(t, dtype, ndim, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# one zero-initialised workspace per (device, stream); kernels leave it zeroed
+_WS: dict = {}
+
+
+def _workspace(nbytes: int):
+    if nbytes == 0:
+        return None, 0
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(int(nbytes), 4096), dtype=torch.uint8, device="cuda")
+        _check(lib().pq_workspace_init(_p(ws), ws.numel(), _stream()), "pq_workspace_init")
+        _WS[key] = ws
+    return ws, ws.numel()
+
+
+def workspace_check() -> int:
+    """Synchronise and return (and clear) the error recorded by kernels in the
+    current stream's workspace (0 = none)."""
+    key = (torch.cuda.current_device(), torch.cuda.current_stream().cuda_stream)
+    ws = _WS.get(key)
+    if ws is None:
+        return 0
+    return lib().pq_workspace_check(_p(ws), _stream())
+
+
+def launches_per_call() -> int:
+    return lib().pq_launches_per_call()
+
+
+def quantize_fp8(t: torch.Tensor):
+    """Block-128 FP8 quantisation of bf16 or fp32 rows [R, K] -> (codes uint8, scales fp32)."""
+    if t.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("quantize_fp8 takes bf16 or fp32 input")
+    _need(t, t.dtype, 2, "t")
+    R, K = t.shape
+    codes = torch.empty((R, K), dtype=torch.uint8, device=t.device)
+    scales = torch.empty((R, max(K // 128, 1)), dtype=torch.float32, device=t.device)
+    _check(lib().pq_quantize_fp8(_p(t), int(t.dtype == torch.float32), R, K, _p(codes), _p(scales), _stream()),
+           "pq_quantize_fp8")
+    return codes, scales
+
+
+def quantize_q4(w: torch.Tensor):
+    """int4 g32 quantisation of fp32 [N, K] -> (packed uint8 [N, K/2], scales fp16 [N, K/32])."""
+    _need(w, torch.float32, 2, "w")
+    N, K = w.shape
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, max(K // 32, 1)), dtype=torch.float16, device=w.device)
+    _check(lib().pq_quantize_q4(_p(w), N, K, _p(packed), _p(scales), _stream()), "pq_quantize_q4")
+    return packed, scales
+
+
+def gemv_fp8_workspace_bytes(M: int, K: int, N: int, epi: int = EPI_NONE) -> int:
+    return int(lib().pq_gemv_fp8_workspace(M, K, N, epi))
+
+
+def gemv_fp8(x, w, w_scale, epi: int = EPI_NONE, debug: bool = False, out=None):
+    """y = epi(x_q @ w_q^T) with live FP8 quantisation of x.  x bf16 [M,K], w uint8 [N,K],
+    w_scale fp32 [N,K/128].  Returns y (bf16 [M,N] or [M,N/2]), or (y, xq, xs) with debug."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(w, torch.uint8, 2, "w")
+    _need(w_scale, torch.float32, 2, "w_scale")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or w_scale.shape != (N, K // 128):
+        raise ValueError("weight / scale shapes do not match x")
+    n_out = N // 2 if epi == EPI_SILU_MUL else N
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device) if debug else None
+    xs = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if debug else None
+    ws, wsn = _workspace(gemv_fp8_workspace_bytes(M, K, N, epi))
+    _check(lib().pq_gemv_fp8(_p(x), M, K, _p(w), _p(w_scale), N, epi, _p(y), _p(xq), _p(xs), _p(ws), wsn,
+                             _stream()), "pq_gemv_fp8")
+    return (y, xq, xs) if debug else y
+
+
+def gemv_q4(x, w, w_scale, epi: int = EPI_NONE, out=None):
+    """W4A16 GEMV: x bf16 [M,K], w uint8 nibbles [N,K/2], w_scale fp16 [N,K/32]."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(w, torch.uint8, 2, "w")
+    _need(w_scale, torch.float16, 2, "w_scale")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K // 2 or w_scale.shape != (N, K // 32):
+        raise ValueError("weight / scale shapes do not match x")
+    n_out = N // 2 if epi == EPI_SILU_MUL else N
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+    ws, wsn = _workspace(int(lib().pq_gemv_q4_workspace(M, K, N, epi)))
+    _check(lib().pq_gemv_q4(_p(x), M, K, _p(w), _p(w_scale), N, epi, _p(y), _p(ws), wsn, _stream()),
+           "pq_gemv_q4")
+    return y
+
+
+def moe_workspace_bytes(M: int, H: int, I: int, E: int, top_k: int) -> int:
+    return int(lib().moe_decode_layer_workspace(M, H, I, E, top_k))
+
+
+def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=None, top_k: int = 8,
+                     debug: bool = False, out=None):
+    """One routed MoE decode layer in one launch.
+
+    x bf16 [M,H]; w13 uint8 [E,2I,H], s13 fp32 [E,2I,H/128]; w2 uint8 [E,H,I], s2 fp32 [E,H,I/128].
+    Either ``logits`` fp32 [M,E] (routing computed on the GPU) or ``topk_ids`` int32 / ``topk_w`` fp32
+    [M,top_k].  Returns a dict with ``out`` (bf16 [M,H]), ``topk_ids``, ``topk_w`` and, with debug,
+    ``h`` (bf16 [M,k,I]), ``hq`` (uint8 [M,k,I]), ``hs`` (fp32 [M,k,I/128])."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(w13, torch.uint8, 3, "w13")
+    _need(s13, torch.float32, 3, "s13")
+    _need(w2, torch.uint8, 3, "w2")
+    _need(s2, torch.float32, 3, "s2")
+    M, H = x.shape
+    E, two_i, _ = w13.shape
+    I = two_i // 2
+    dev = x.device
+    if logits is not None:
+        _need(logits, torch.float32, 2, "logits")
+        topk_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+        topk_w = torch.empty((M, top_k), dtype=torch.float32, device=dev)
+    else:
+        _need(topk_ids, torch.int32, 2, "topk_ids")
+        _need(topk_w, torch.float32, 2, "topk_w")
+        top_k = topk_ids.shape[1]
+    y = out if out is not None else torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((M, top_k, I), dtype=torch.bfloat16, device=dev) if debug else None
+    hq = torch.empty((M, top_k, I), dtype=torch.uint8, device=dev) if debug else None
+    hs = torch.empty((M, top_k, I // 128), dtype=torch.float32, device=dev) if debug else None
+    ws, wsn = _workspace(moe_workspace_bytes(M, H, I, E, top_k))
+    _check(lib().moe_decode_layer(_p(x), M, H, _p(logits), _p(topk_ids), _p(topk_w), E, top_k, I,
+                                  _p(w13), _p(s13), _p(w2), _p(s2), _p(y), _p(h), _p(hq), _p(hs),
+                                  _p(ws), wsn, _stream()), "moe_decode_layer")
+    res = {"out": y, "topk_ids": topk_ids, "topk_w": topk_w}
+    if debug:
+        res.update(h=h, hq=hq, hs=hs)
+    return res

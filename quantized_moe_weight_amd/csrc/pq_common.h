@@ -1,0 +1,238 @@
+// Shared device and host helpers of the gfx950 decode library.
+//
+// Device side: the FP8 E4M3FN encoder used by every live quantisation, the
+// bf16 rounding of outputs, the FP8 x FP8 16-element block dot product on
+// v_dot2 bf16 pairs, 64-lane wavefront reductions and the agent-scope
+// release/acquire helpers used by the single-launch kernels.
+// Host side: status codes, per-thread HIP error, device-property cache.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pq.h"
+
+namespace pq {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 128;        // FP8 scale block along K
+constexpr int kChunk = 1024;       // bytes of one weight row covered by one wave load (64 lanes x 16 B)
+constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------------------
+// Live FP8 quantisation.
+//
+// The rule (scale s = fp32(amax/448), code = E4M3(fp32(v/s)), ties to even,
+// saturating) is the reading taken of [Sionic] §1's live FP8 activation
+// quantisation with one scale per 128-wide K block ([Sionic] §2).
+// ---------------------------------------------------------------------------
+
+// fp32 -> E4M3FN byte, round to nearest even, |v| >= 448 (and inf) saturate,
+// NaN -> 0x7F.  Integer/rounding ops only; no fast-math.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7Fu;                  // NaN
+  if (a >= 0x43e00000u) return sign | 0x7Eu;          // >= 448: satfinite
+  uint32_t code;
+  if (a < 0x3c800000u) {                              // < 2^-6: subnormal grid of 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scale, RNE
+  } else {                                            // 3-bit mantissa, RNE
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);                   // exponent bias 127 -> 7
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return sign | code;
+}
+
+// Correctly rounded fp32 quotient v / s for a shared divisor: with
+// r = fp64(1/s), fp32(fp64(v * r)) equals the IEEE fp32 quotient for every
+// fp32 v and positive fp32 s (the quotient of two 24-bit values is never an
+// fp32 rounding midpoint and lies at least 2^-49 (relative) away from one,
+// while the fp64 product is within 2^-52).  One fp64 divide per block
+// instead of one fp32 divide per element.
+__device__ __forceinline__ float quotient_f32(float v, double r) {
+  return (float)((double)v * r);
+}
+
+__device__ __forceinline__ float block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4M3Max;       // IEEE fp32 division
+}
+
+// ---------------------------------------------------------------------------
+// Output rounding
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 x FP8 dot products.  Both operands are E4M3 codes; every E4M3 value is
+// exact in bf16, so each pair of bytes is widened to a bf16 pair by the
+// hardware converter and multiplied-accumulated by v_dot2 (exact products,
+// fp32 accumulation).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x2 fp8x2_lo(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+}
+__device__ __forceinline__ bf16x2 fp8x2_hi(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+
+struct Bf16x16 { bf16x2 v[8]; };
+
+__device__ __forceinline__ Bf16x16 widen16(uint4 c) {
+  Bf16x16 r;
+  r.v[0] = fp8x2_lo(c.x); r.v[1] = fp8x2_hi(c.x);
+  r.v[2] = fp8x2_lo(c.y); r.v[3] = fp8x2_hi(c.y);
+  r.v[4] = fp8x2_lo(c.z); r.v[5] = fp8x2_hi(c.z);
+  r.v[6] = fp8x2_lo(c.w); r.v[7] = fp8x2_hi(c.w);
+  return r;
+}
+
+// sum of the 16 products of one lane's 16-byte slice
+__device__ __forceinline__ float dot16(const Bf16x16& a, const Bf16x16& b) {
+  float p = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p = __builtin_amdgcn_fdot2_f32_bf16(a.v[j], b.v[j], p, false);
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Raw buffer loads.  The descriptor lives in SGPRs (one per tensor), the
+// per-lane offset is 32-bit, and an offset at or beyond the descriptor's size
+// returns zeros without touching memory: masked lanes and drained pipeline
+// slots issue loads unconditionally, which keeps the load stream free of
+// branches so the compiler can count outstanding loads statically.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;            // any offset >= this is out of range
+constexpr uint32_t kMaxBufferBytes = 0x7FFFFFF0u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (xor butterfly: every lane ends with the same bits)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float group_max(float v, int width) {  // within aligned groups of `width` lanes
+  for (int o = width >> 1; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------------------
+// Cross-block synchronisation at agent (device) scope.  Blocks of one launch
+// run on all 8 XCDs, whose L2 caches are separate: a producer publishes with
+// a release fence before its counter update, a consumer acquires after
+// observing the counter.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workspace layout shared by every kernel that synchronises across blocks:
+//   [0, 256)            WsHeader
+//   [256, kWsDataOff)   arrival counters (uint32), zero between calls
+//   [kWsDataOff, ...)   per-call scratch data (always written before read)
+// The counter region never moves, whatever the shape of the call, so a
+// counter address is only ever used as a counter and the zero-between-calls
+// invariant holds across calls of different shapes on one workspace.
+constexpr size_t kWsCounterOff = 256;
+constexpr size_t kWsDataOff = 65536;
+constexpr size_t kWsMaxCounters = (kWsDataOff - kWsCounterOff) / 4;
+
+// Workspace header shared by the kernels that synchronise across blocks.
+struct WsHeader {
+  uint32_t error;       // first pq_status recorded by a kernel (0 = none)
+  uint32_t done;        // phase counter of the running call
+  uint32_t exit_count;  // blocks that finished the running call
+  uint32_t pad[61];     // keep the header one 256-byte line
+};
+static_assert(sizeof(WsHeader) == 256, "workspace header is one 256-byte line");
+
+__device__ __forceinline__ void record_error(WsHeader* h, int status) {
+  uint32_t expected = 0u;
+  __hip_atomic_compare_exchange_strong(&h->error, &expected, (uint32_t)status,
+                                       __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until *ctr >= target; gives up after `limit` polls, recording
+// PQ_ERR_TIMEOUT, so that every wave always reaches the end of the kernel.
+__device__ __forceinline__ bool spin_wait_geq(const uint32_t* ctr, uint32_t target, WsHeader* h,
+                                              uint32_t limit) {
+  for (uint32_t it = 0; it < limit; ++it) {
+    if (atomic_load_relaxed(ctr) >= target) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  record_error(h, PQ_ERR_TIMEOUT);
+  return false;
+}
+
+}  // namespace pq
+
+// ---------------------------------------------------------------------------
+// Host helpers
+// ---------------------------------------------------------------------------
+namespace pqhost {
+
+struct DeviceInfo {
+  int device = -1;
+  int num_cus = 0;
+  bool gfx950 = false;
+};
+
+// Properties of the current device (cached per device id).
+int current_device_info(DeviceInfo* out);
+
+void set_last_hip_error(int e);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+__host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace pqhost
+
+#define PQ_HIP_CHECK(expr)                                  \
+  do {                                                      \
+    hipError_t _e = (expr);                                 \
+    if (_e != hipSuccess) {                                 \
+      pqhost::set_last_hip_error((int)_e);                  \
+      return PQ_ERR_HIP;                                    \
+    }                                                       \
+  } while (0)

@@ -1,0 +1,71 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/pq.h declares, and validates arguments on the host before touching
+the GPU."""
+import ctypes
+import os
+
+import pytest
+
+from quantized_moe_weight_amd import _lib
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libpqmoe.so not built", allow_module_level=True)
+
+PQ_OK, PQ_ERR_NULL, PQ_ERR_SHAPE, PQ_ERR_ALIGN, PQ_ERR_WORKSPACE, PQ_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+FAKE = ctypes.c_void_p(1 << 20)          # non-null, 16-byte aligned; never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 8)     # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_header_function_is_exported(lib):
+    names = _lib.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_strerror_covers_every_status(lib):
+    for st in range(-8, 1):
+        assert b"unknown" not in lib.pq_strerror(st)
+    assert lib.pq_launches_per_call() == 1
+
+
+def test_gemv_fp8_host_validation(lib):
+    g = lib.pq_gemv_fp8
+    args = lambda x=FAKE, M=1, K=512, w=FAKE, s=FAKE, N=256, epi=0, y=FAKE: (  # noqa: E731
+        x, M, K, w, s, N, epi, y, NUL, NUL, NUL, 0, NUL)
+    assert g(*args(x=NUL)) == PQ_ERR_NULL
+    assert g(*args(y=NUL)) == PQ_ERR_NULL
+    assert g(*args(M=0)) == PQ_ERR_SHAPE
+    assert g(*args(M=9)) == PQ_ERR_SHAPE
+    assert g(*args(K=500)) == PQ_ERR_SHAPE
+    assert g(*args(K=32768)) == PQ_ERR_SHAPE
+    assert g(*args(N=0)) == PQ_ERR_SHAPE
+    assert g(*args(epi=1, N=255)) == PQ_ERR_SHAPE
+    assert g(*args(epi=7)) == PQ_ERR_SHAPE
+    assert g(*args(w=MIS)) == PQ_ERR_ALIGN
+    # valid arguments on a machine without a gfx950 device stop before any launch
+    assert g(*args()) in (PQ_ERR_UNSUPPORTED, PQ_OK) or g(*args()) < 0
+
+
+def test_quantizers_host_validation(lib):
+    assert lib.pq_quantize_fp8(NUL, 0, 1, 128, FAKE, FAKE, NUL) == PQ_ERR_NULL
+    assert lib.pq_quantize_fp8(FAKE, 0, 1, 100, FAKE, FAKE, NUL) == PQ_ERR_SHAPE
+    assert lib.pq_quantize_fp8(FAKE, 0, 0, 128, FAKE, FAKE, NUL) == PQ_ERR_SHAPE
+    assert lib.pq_quantize_fp8(MIS, 0, 1, 128, FAKE, FAKE, NUL) == PQ_ERR_ALIGN
+    assert lib.pq_quantize_q4(FAKE, 1, 48, FAKE, FAKE, NUL) == PQ_ERR_SHAPE
+    assert lib.pq_quantize_q4(NUL, 1, 64, FAKE, FAKE, NUL) == PQ_ERR_NULL
+
+
+def test_workspace_helpers_host_validation(lib):
+    assert lib.pq_workspace_init(NUL, 0, NUL) == PQ_OK
+    assert lib.pq_workspace_init(NUL, 64, NUL) == PQ_ERR_NULL
+    assert lib.pq_workspace_init(MIS, 64, NUL) == PQ_ERR_ALIGN
+    assert lib.pq_workspace_check(NUL, NUL) == PQ_ERR_NULL

@@ -1,0 +1,153 @@
+"""GPU parity of pq_gemv_fp8 (live FP8 activation quant + block-scaled FP8 GEMV,
+split-K, SiLU*up epilogue) against the oracle."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _helpers import (assert_gemv_close, assert_silu_close, bf16_to_np, need_gpu,
+                      np_bf16_bits_to_torch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    need_gpu()
+    import quantized_moe_weight_amd as pq
+    return pq
+
+
+class splitk:
+    """Force the split-K factor of the library for the duration of a block."""
+
+    def __init__(self, s):
+        self.s = s
+
+    def __enter__(self):
+        self.old = os.environ.get("PQ_SPLITK")
+        if self.s is not None:
+            os.environ["PQ_SPLITK"] = str(self.s)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("PQ_SPLITK", None)
+        else:
+            os.environ["PQ_SPLITK"] = self.old
+
+
+def _case(M, K, N, seed, workload=workloads.FP8_GEMV_SMALL):
+    import torch
+    x = workloads.activation_bf16(M, K, workload=workload, seed=seed)
+    w = workloads.master_weights(N, K, workload=workload, seed=seed)
+    return x, w, np_bf16_bits_to_torch(x), torch.from_numpy(w).cuda()
+
+
+def _run(pq, xt, wt, epi, s=None):
+    q, sc = pq.quantize_fp8(wt)
+    with splitk(s):
+        y, xq, xs = pq.gemv_fp8(xt, q, sc, epi=epi, debug=True)
+    return y, xq, xs, q, sc
+
+
+@pytest.mark.parametrize("M,K,N,S", [
+    (1, 512, 256, None),        # the small dense GEMV workload
+    (1, 512, 256, 1),
+    (2, 640, 37, None),         # 5 blocks: a partial 1 KB chunk, ragged N
+    (3, 1152, 100, 3),
+    (8, 2048, 96, 4),
+    (4, 6144, 300, 2),
+])
+def test_gemv_fp8_plain(pq, M, K, N, S):
+    x, w, xt, wt = _case(M, K, N, seed=M * 100 + K + N)
+    y, xq, xs, q, sc = _run(pq, xt, wt, pq.EPI_NONE, S)
+    qx, sx = oracle.act_quant_fp8(x)
+    assert np.array_equal(xq.cpu().numpy(), qx)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), sx.view(np.uint32))
+    yo, So = oracle.gemv_fp8(qx, sx, q.cpu().numpy(), sc.cpu().numpy())
+    assert_gemv_close(bf16_to_np(y), yo, So, f"M={M} K={K} N={N} S={S}")
+
+
+@pytest.mark.parametrize("M,K,N,S", [
+    (1, 6144, 4096, None),      # one expert gate_up at batch 1 (gate||up, SiLU*up)
+    (1, 6144, 4096, 3),
+    (2, 1024, 70, None),
+    (5, 768, 64, 2),
+])
+def test_gemv_fp8_silu(pq, M, K, N, S):
+    x, w, xt, wt = _case(M, K, N, seed=M + K + N, workload=workloads.FP8_GATE_UP)
+    y, xq, xs, q, sc = _run(pq, xt, wt, pq.EPI_SILU_MUL, S)
+    qx, sx = oracle.act_quant_fp8(x)
+    assert np.array_equal(xq.cpu().numpy(), qx)
+    yo, So = oracle.gemv_fp8(qx, sx, q.cpu().numpy(), sc.cpu().numpy())
+    I = N // 2
+    h = oracle.silu_mul(yo, I)
+    assert_silu_close(bf16_to_np(y), h, yo[:, :I], yo[:, I:], So[:, :I], So[:, I:], f"M={M} S={S}")
+
+
+def test_gemv_fp8_decodes_every_code(pq):
+    """Weight rows hold each of the 256 codes at one position and x is 448 there:
+    y[n] = 448 * dq(code_n) exactly (NaN for the two NaN codes)."""
+    import torch
+    K, k0 = 256, 77
+    w = np.zeros((256, K), np.uint8)
+    w[:, k0] = np.arange(256, dtype=np.uint8)
+    sw = np.ones((256, 2), np.float32)
+    x = np.zeros((1, K), np.uint16)
+    x[0, k0] = workloads.f32_to_bf16_bits(np.array([448.0], np.float32))[0]
+    y = pq.gemv_fp8(np_bf16_bits_to_torch(x), torch.from_numpy(w).cuda(), torch.from_numpy(sw).cuda())
+    got = bf16_to_np(y)[0]
+    want = 448.0 * oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+def test_gemv_fp8_rows_bitwise_independent_of_M(pq):
+    import torch
+    M, K, N = 6, 2048, 512
+    x, w, xt, wt = _case(M, K, N, seed=17)
+    q, sc = pq.quantize_fp8(wt)
+    with splitk(1):
+        y = pq.gemv_fp8(xt, q, sc, epi=pq.EPI_SILU_MUL)
+        for m in range(M):
+            ym = pq.gemv_fp8(xt[m:m + 1].contiguous(), q, sc, epi=pq.EPI_SILU_MUL)
+            assert torch.equal(ym[0].view(torch.int16), y[m].view(torch.int16))
+
+
+def test_gemv_fp8_deterministic_repeats(pq):
+    import torch
+    x, w, xt, wt = _case(1, 6144, 4096, seed=3, workload=workloads.FP8_GATE_UP)
+    q, sc = pq.quantize_fp8(wt)
+    for s in (None, 4):
+        with splitk(s):
+            y0 = pq.gemv_fp8(xt, q, sc, epi=pq.EPI_SILU_MUL)
+            for _ in range(20):
+                assert torch.equal(pq.gemv_fp8(xt, q, sc, epi=pq.EPI_SILU_MUL).view(torch.int16),
+                                   y0.view(torch.int16))
+
+
+def test_gemv_fp8_zero_inputs_give_zero(pq):
+    import torch
+    K, N = 512, 64
+    x = np.zeros((2, K), np.uint16)
+    w = workloads.master_weights(N, K, workload=workloads.FP8_GEMV_SMALL, seed=1)
+    q, sc = pq.quantize_fp8(torch.from_numpy(w).cuda())
+    y = pq.gemv_fp8(np_bf16_bits_to_torch(x), q, sc)
+    assert torch.all(y == 0)
+
+
+def test_gemv_fp8_rejects_bad_shapes(pq):
+    import torch
+    x = torch.zeros((1, 100), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((4, 100), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 0), dtype=torch.float32, device="cuda")
+    with pytest.raises((pq.PqError, ValueError)):
+        pq.gemv_fp8(x, w, s)
+    x = torch.zeros((9, 128), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((4, 128), dtype=torch.uint8, device="cuda")
+    s = torch.ones((4, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(pq.PqError):
+        pq.gemv_fp8(x, w, s)

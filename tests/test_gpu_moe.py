@@ -1,0 +1,212 @@
+"""GPU parity of moe_decode_layer (one launch: route, live act-quant, gate_up +
+SiLU*up, h re-quant, down, weighted combine) against the oracle.
+
+Expected values come only from the oracle run on the same seeded inputs: the
+master weights are drawn once and quantised independently by the library
+(on the GPU) and by the oracle (on the CPU); the test first checks that both
+codings agree bit for bit.
+
+Checks per call: routing ids exact, routing weights within 1e-6, h within the
+SiLU bound, output within 2e-3 * S per element (S = sum_j |w_j| sum_k |h~_k w2~_nk|
+from the oracle), and the share of h codes that differ from the oracle's is
+reported (h crosses a bf16 rounding computed from fp32 on the GPU and fp64 in
+the oracle, so a few codes may sit on the other side of a rounding boundary).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _helpers import assert_gemv_close, assert_silu_close, bf16_to_np, need_gpu, np_bf16_bits_to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    need_gpu()
+    import quantized_moe_weight_amd as pq
+    return pq
+
+
+class Bank:
+    """Expert bank with only the experts a test routes to filled in.
+
+    Master weights are drawn per expert from ``workloads``; the GPU copy is
+    quantised by the library, the oracle copy by the oracle."""
+
+    def __init__(self, pq, E, H, I, workload=workloads.MOE_LAYER, seed=0):
+        import torch
+        self.pq, self.E, self.H, self.I, self.wl, self.seed = pq, E, H, I, workload, seed
+        self.w13 = torch.zeros((E, 2 * I, H), dtype=torch.uint8, device="cuda")
+        self.s13 = torch.ones((E, 2 * I, H // 128), dtype=torch.float32, device="cuda")
+        self.w2 = torch.zeros((E, H, I), dtype=torch.uint8, device="cuda")
+        self.s2 = torch.ones((E, H, I // 128), dtype=torch.float32, device="cuda")
+        self.cpu = {}
+
+    def fill(self, experts):
+        import torch
+        for e in sorted(set(int(v) for v in np.asarray(experts).ravel())):
+            if e in self.cpu:
+                continue
+            m13 = workloads.master_weights(2 * self.I, self.H, workload=self.wl, tensor=workloads.T_W13,
+                                           expert=e, seed=self.seed)
+            m2 = workloads.master_weights(self.H, self.I, workload=self.wl, tensor=workloads.T_W2,
+                                          expert=e, seed=self.seed)
+            q13, s13 = self.pq.quantize_fp8(torch.from_numpy(m13).cuda())
+            q2, s2 = self.pq.quantize_fp8(torch.from_numpy(m2).cuda())
+            self.w13[e].copy_(q13); self.s13[e].copy_(s13); self.w2[e].copy_(q2); self.s2[e].copy_(s2)
+            o13, os13 = oracle.block_quant_fp8(m13)
+            o2, os2 = oracle.block_quant_fp8(m2)
+            assert np.array_equal(q13.cpu().numpy(), o13) and np.array_equal(q2.cpu().numpy(), o2)
+            assert np.array_equal(s13.cpu().numpy(), os13) and np.array_equal(s2.cpu().numpy(), os2)
+            self.cpu[e] = (o13, os13, o2, os2)
+
+    def expert(self, e):
+        return self.cpu[e]
+
+
+def _check(pq, bank, x_bits, res, ref, M, k):
+    ids = res["topk_ids"].cpu().numpy()
+    assert np.array_equal(ids, ref["ids"]), "routing ids differ"
+    assert np.max(np.abs(res["topk_w"].cpu().numpy() - ref["weights"])) <= 1e-6
+    I = bank.I
+    if "h" in res:
+        h = bf16_to_np(res["h"])
+        assert_silu_close(h, ref["h"], ref["gate"], ref["up"], ref["S_gate"], ref["S_up"], "h")
+        hq = res["hq"].cpu().numpy()
+        diff = np.mean(hq != ref["hq"])
+        assert diff <= 2e-3, f"{diff:.2e} of h codes differ from the oracle"
+    y = bf16_to_np(res["out"])
+    return assert_gemv_close(y, ref["out"], ref["S"], f"out M={M}")
+
+
+@pytest.mark.parametrize("M,E,H,I,k", [(1, 16, 512, 256, 4), (2, 16, 640, 384, 4), (3, 24, 1024, 512, 8),
+                                       (8, 32, 1024, 256, 8)])
+def test_moe_small_routed(pq, M, E, H, I, k):
+    import torch
+    bank = Bank(pq, E, H, I, seed=M)
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=M)
+    lg = workloads.router_logits(M, E, workload=workloads.MOE_LAYER, seed=M)
+    ids, _ = oracle.route_topk(lg, k)
+    bank.fill(ids)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              logits=torch.from_numpy(lg).cuda(), top_k=k, debug=True)
+    assert pq.workspace_check() == 0
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k)
+    _check(pq, bank, x, res, ref, M, k)
+
+
+def test_moe_given_routing_with_shared_experts(pq):
+    import torch
+    M, E, H, I, k = 4, 12, 512, 256, 3
+    bank = Bank(pq, E, H, I, seed=9)
+    ids = np.array([[5, 2, 9], [2, 5, 11], [0, 9, 2], [7, 5, 1]], np.int32)
+    w = np.array([[0.5, 0.3, 0.2], [0.6, 0.3, 0.1], [0.4, 0.35, 0.25], [0.9, 0.05, 0.05]], np.float32)
+    bank.fill(ids)
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=9)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              topk_ids=torch.from_numpy(ids).cuda(), topk_w=torch.from_numpy(w).cuda(), debug=True)
+    assert pq.workspace_check() == 0
+    ref = oracle.moe_layer(x, bank.expert, ids=ids, weights=w.astype(np.float64))
+    assert_gemv_close(bf16_to_np(res["out"]), ref["out"], ref["S"], "given routing")
+    assert_silu_close(bf16_to_np(res["h"]), ref["h"], ref["gate"], ref["up"], ref["S_gate"], ref["S_up"], "h")
+
+
+def test_moe_rows_bitwise_independent_of_M(pq):
+    """A token's output in an M-token verify call equals the token decoded alone."""
+    import torch
+    M, E, H, I, k = 6, 20, 1024, 512, 8
+    bank = Bank(pq, E, H, I, seed=4)
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=4)
+    lg = workloads.verify_logits(M, E, workload=workloads.MOE_LAYER, seed=4)
+    bank.fill(oracle.route_topk(lg, k)[0])
+    xt, lt = np_bf16_bits_to_torch(x), torch.from_numpy(lg).cuda()
+    full = pq.moe_decode_layer(xt, bank.w13, bank.s13, bank.w2, bank.s2, logits=lt, top_k=k, debug=True)
+    for m in range(M):
+        one = pq.moe_decode_layer(xt[m:m + 1].contiguous(), bank.w13, bank.s13, bank.w2, bank.s2,
+                                  logits=lt[m:m + 1].contiguous(), top_k=k, debug=True)
+        assert torch.equal(one["out"][0].view(torch.int16), full["out"][m].view(torch.int16))
+        assert torch.equal(one["hq"][0], full["hq"][m])
+        assert torch.equal(one["topk_w"][0], full["topk_w"][m])
+
+
+def test_moe_deterministic_and_workspace_reuse(pq):
+    """Repeated calls are bitwise identical, also interleaved with calls of other
+    shapes on the same workspace (counters must be left at zero)."""
+    import torch
+    E, H, I, k = 16, 512, 256, 4
+    bank = Bank(pq, E, H, I, seed=5)
+    bank.fill(range(E))
+    outs = {}
+    for rep in range(6):
+        for M in (1, 5, 2):
+            x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=50 + M)
+            lg = workloads.router_logits(M, E, workload=workloads.MOE_LAYER, seed=50 + M)
+            r = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                                    logits=torch.from_numpy(lg).cuda(), top_k=k)
+            if rep == 0:
+                outs[M] = r["out"].clone()
+                ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k)
+                assert_gemv_close(bf16_to_np(r["out"]), ref["out"], ref["S"], f"M={M}")
+            else:
+                assert torch.equal(r["out"].view(torch.int16), outs[M].view(torch.int16))
+    assert pq.workspace_check() == 0
+
+
+def test_moe_bad_expert_id_is_reported(pq):
+    import torch
+    E, H, I = 8, 256, 128
+    bank = Bank(pq, E, H, I, seed=6)
+    bank.fill([0, 1])
+    x = torch.zeros((1, H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.tensor([[1, 99]], dtype=torch.int32, device="cuda")
+    w = torch.tensor([[0.5, 0.5]], dtype=torch.float32, device="cuda")
+    pq.moe_decode_layer(x, bank.w13, bank.s13, bank.w2, bank.s2, topk_ids=ids, topk_w=w)
+    assert pq.workspace_check() == -8
+    assert pq.workspace_check() == 0          # the record is cleared
+
+
+def test_moe_watchdog_reports_timeout_and_next_call_is_clean(pq):
+    """A zero spin budget (set from the host) makes waiting blocks give up
+    instead of waiting: the call still ends, the timeout is reported, and the
+    next call with the normal budget is correct."""
+    import torch
+    M, E, H, I, k = 1, 16, 2048, 1024, 4
+    bank = Bank(pq, E, H, I, seed=7)
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=7)
+    lg = workloads.router_logits(M, E, workload=workloads.MOE_LAYER, seed=7)
+    bank.fill(oracle.route_topk(lg, k)[0])
+    args = (np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2)
+    os.environ["PQ_SPIN_LIMIT"] = "0"
+    try:
+        pq.moe_decode_layer(*args, logits=torch.from_numpy(lg).cuda(), top_k=k)
+    finally:
+        del os.environ["PQ_SPIN_LIMIT"]
+    assert pq.workspace_check() in (0, -7)
+    r = pq.moe_decode_layer(*args, logits=torch.from_numpy(lg).cuda(), top_k=k)
+    assert pq.workspace_check() == 0
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k)
+    assert_gemv_close(bf16_to_np(r["out"]), ref["out"], ref["S"], "after timeout")
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_moe_full_size_layer(pq, M):
+    """256 experts, hidden 6144, intermediate 2048, top-8: the routed MoE layer at
+    its real shape (M=1) and a 4-token verify call, every output checked."""
+    import torch
+    shp = workloads.MOE_SHAPE
+    bank = Bank(pq, shp.E, shp.H, shp.I, workload=workloads.MOE_LAYER, seed=0)
+    x = workloads.activation_bf16(M, shp.H, workload=workloads.MOE_LAYER if M == 1 else workloads.MOE_VERIFY)
+    lg = (workloads.router_logits(1, shp.E, workload=workloads.MOE_LAYER) if M == 1
+          else workloads.verify_logits(M, shp.E))
+    ids, _ = oracle.route_topk(lg, shp.top_k)
+    bank.fill(ids)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              logits=torch.from_numpy(lg).cuda(), top_k=shp.top_k, debug=True)
+    assert pq.workspace_check() == 0
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=shp.top_k)
+    worst = _check(pq, bank, x, res, ref, M, shp.top_k)
+    print(f"full-size M={M}: union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")

@@ -1,0 +1,340 @@
+"""Decode benchmark: the routed FP8 MoE layer at batch 1 on one MI355X.
+
+One step = one ``moe_decode_layer`` launch over the full layer: 256 resident
+experts (hidden 6144, intermediate 2048, E4M3 weights with fp32 block-128
+scales, ~10 GB in HBM), fresh N(0,1) router logits per step (64 pre-drawn
+sets, so consecutive steps touch mostly different experts and the 256 MB
+Infinity Cache cannot serve them), top-8 routing, live FP8 activation
+quantisation, gate_up + SiLU*up, h re-quantisation, down and the weighted
+combine.  Inputs are resident in HBM before timing starts.
+
+Reported (one JSON line):
+  value        algorithmic bytes moved per second over the timed steps (GB/s)
+  ms_per_step  wall time per layer call
+  roofline     the layer kernel against HBM peak: algorithmic bytes per launch
+               divided by its mean launch duration (HIP events around each
+               launch on the launch stream); traffic = FETCH_SIZE + WRITE_SIZE
+               of the kernel from the committed rocprofv3 counter summary,
+               scaled by a plain copy kernel of known size (null when the
+               kernel source changed since the counters were taken)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m M]
+       python bench.py --ingest-pmc FETCH.csv WRITE.csv   (writes the counter summary)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KERNEL_NAME = "moe_layer_kernel"
+MOE_SRC = os.path.join(ROOT, "quantized_moe_weight_amd", "csrc", "pq_moe.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "moe_layer_kernel_e256_h6144_i2048_m1.pmc.txt")
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written per dispatch
+METRIC = "achieved HBM GB/s (% of 8 TB/s) + µs/layer, batch-1 top-8 FP8 MoE GEMV"
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha1()
+    for f in ("pq_moe.hip", "pq_common.h", "pq_quant_dev.h"):
+        h.update(open(os.path.join(ROOT, "quantized_moe_weight_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def build_bank(pq, shp, seed=0):
+    """Resident expert bank: master weights drawn per expert on the device,
+    quantised by the library (E4M3 + fp32 block-128 scales)."""
+    import torch
+    import workloads
+    E, H, I = shp.E, shp.H, shp.I
+    w13 = torch.empty((E, 2 * I, H), dtype=torch.uint8, device="cuda")
+    s13 = torch.empty((E, 2 * I, H // 128), dtype=torch.float32, device="cuda")
+    w2 = torch.empty((E, H, I), dtype=torch.uint8, device="cuda")
+    s2 = torch.empty((E, H, I // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):
+        m13 = workloads.master_weights_torch(2 * I, H, workload=workloads.MOE_LAYER, tensor=workloads.T_W13,
+                                             expert=e, seed=seed)
+        q, s = pq.quantize_fp8(m13)
+        w13[e].copy_(q); s13[e].copy_(s)
+        m2 = workloads.master_weights_torch(H, I, workload=workloads.MOE_LAYER, tensor=workloads.T_W2,
+                                            expert=e, seed=seed)
+        q, s = pq.quantize_fp8(m2)
+        w2[e].copy_(q); s2[e].copy_(s)
+    torch.cuda.synchronize()
+    return w13, s13, w2, s2
+
+
+def read_traffic(bytes_alg):
+    """HBM bytes per launch from the committed counter summary, or None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    try:
+        d = json.loads(open(PMC_SUMMARY, encoding="utf-8").read().split("\n---\n")[0])
+    except Exception:
+        return None
+    if d.get("source_sha") != kernel_source_sha():
+        return None
+    return d["fetch_kib"] * 1024 * d["fetch_scale"] + d["write_kib"] * 1024 * d["write_scale"]
+
+
+def cpu_baseline(shp, x_bits, lg, budget_s=12.0):
+    """Time the CPU oracle on one routed layer call (repeated until ~budget_s)."""
+    import numpy as np
+    import oracle
+    import workloads
+    ids, _ = oracle.route_topk(lg, shp.top_k)
+    experts = {}
+    for e in oracle.union_of_experts(ids):
+        m13 = workloads.master_weights_torch(2 * shp.I, shp.H, workload=workloads.MOE_LAYER,
+                                             tensor=workloads.T_W13, expert=int(e)).cpu().numpy()
+        m2 = workloads.master_weights_torch(shp.H, shp.I, workload=workloads.MOE_LAYER,
+                                            tensor=workloads.T_W2, expert=int(e)).cpu().numpy()
+        experts[int(e)] = oracle.block_quant_fp8(m13) + oracle.block_quant_fp8(m2)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    reps, t0 = 0, time.perf_counter()
+    res = None
+    while True:
+        res = oracle.moe_layer(x_bits, lambda e: experts[e], logits=lg, top_k=shp.top_k)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    return dt, reps, cores, res, len(experts)
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import quantized_moe_weight_amd as pq
+    import workloads
+
+    torch.cuda.set_device(0)
+    shp = workloads.MOE_SHAPE
+    M = args.m
+    t_setup = time.perf_counter()
+    w13, s13, w2, s2 = build_bank(pq, shp)
+    wl = workloads.MOE_LAYER if M == 1 else workloads.MOE_VERIFY
+    x_bits = workloads.activation_bf16(M, shp.H, workload=wl)
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    n_draws = 64
+    if M == 1:
+        pool_np = [workloads.router_logits(1, shp.E, workload=wl, draw=d) for d in range(n_draws)]
+    else:
+        pool_np = [workloads.verify_logits(M, shp.E, draw=d) for d in range(n_draws)]
+    pool = [torch.from_numpy(p).cuda() for p in pool_np]
+    call = pq.MoeLayerCall(w13, s13, w2, s2, M=M, top_k=shp.top_k)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    # distinct experts per draw -> algorithmic bytes of each step
+    expert_bytes = 2 * shp.I * shp.H + 4 * 2 * shp.I * (shp.H // 128) + shp.H * shp.I + 4 * shp.H * (shp.I // 128)
+    io_bytes = M * (2 * shp.H + 2 * shp.H + 4 * shp.E)
+    uni = []
+    for d in range(n_draws):
+        call(x, pool[d])
+        uni.append(len(np.unique(call.topk_ids.cpu().numpy())))
+    step_bytes = [u * expert_bytes + io_bytes for u in uni]
+    assert call.check() == 0
+
+    for i in range(args.warmup):
+        call(x, pool[i % n_draws])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record()
+    for i in range(K):
+        starts[i].record()
+        call(x, pool[i % n_draws])
+        ends[i].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    status = call.check()
+    if status != 0:
+        raise RuntimeError(f"kernel reported status {status}")
+
+    bytes_timed = sum(step_bytes[i % n_draws] for i in range(K))
+    value = bytes_timed / (total_ms * 1e-3) / 1e9
+    mean_launch_s = float(np.mean(per_launch_ms)) * 1e-3
+    bytes_per_launch = bytes_timed / K
+    achieved = bytes_per_launch / mean_launch_s / 1e9
+    traffic = read_traffic(bytes_per_launch) if M == 1 else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"routed FP8 MoE decode layer, M={M}: 256 experts resident in HBM, hidden 6144, "
+                         "expert intermediate 2048 (gate||up 6144->2x2048, SiLU*up, down 2048->6144), "
+                         "E4M3 weights with fp32 scale per 128-wide K block, top-8 of N(0,1) logits, "
+                         "live FP8 activation quantisation, bf16 in/out"),
+            "M": M, "experts": shp.E, "hidden": shp.H, "intermediate": shp.I, "top_k": shp.top_k,
+            "mean_experts_streamed": float(np.mean(uni)),
+            "bytes_per_step": int(round(bytes_per_launch)),
+            "launches_per_layer": pq.launches_per_call(),
+            "parallelism": "single GPU",
+        },
+        "us_per_layer": round(total_ms / K * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "kernel": KERNEL_NAME,
+            "mean_launch_us": round(mean_launch_s * 1e6, 2),
+        },
+        "setup_s": round(setup_s, 1),
+    }
+    if M > 1:
+        out["config"]["bytes_per_token"] = int(bytes_per_launch / M)
+        out["config"]["bytes_per_accepted_token_L3.5"] = int(bytes_per_launch / 3.5)
+
+    if args.cpu_baseline:
+        dt, reps, cores, ref, nexp = cpu_baseline(shp, x_bits, pool_np[0])
+        b0 = step_bytes[0]
+        call(x, pool[0])
+        torch.cuda.synchronize()
+        y = call.out.float().cpu().numpy().astype(np.float64)
+        rel = float(np.max(np.abs(y - ref["out"]) / ref["S"]))
+        out["cpu_baseline"] = {
+            "value": round(b0 / dt / 1e9, 3),
+            "unit": "GB/s",
+            "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"one layer call (routing draw 0, {nexp} experts, {b0} bytes) of the same workload, "
+                       f"float64 dequantise-then-matmul oracle repeated {reps}x, {dt:.2f} s per call; "
+                       "weights pre-quantised by the oracle, untimed"),
+            "seconds_per_call": round(dt, 3),
+        }
+        out["parity_check"] = {"max_err_over_S": rel, "bound": 2e-3, "ok": rel <= 2e-3}
+    print(json.dumps(out), flush=True)
+
+
+def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES):
+    """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) into
+    the committed summary: mean KiB per dispatch of the layer kernel and of the
+    calibration copy kernel, and the copy-derived scale factors."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = list(csv.DictReader(open(path, encoding="utf-8")))
+        acc = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        return acc
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        for name, vals in d.items():
+            if key in name:
+                return sum(vals) / len(vals), len(vals), name
+        raise KeyError(key)
+
+    mf, nf, _ = pick(f, KERNEL_NAME)
+    mw, nw, _ = pick(w, KERNEL_NAME)
+    cf, _, cname = pick(f, "copy")
+    cw, _, _ = pick(w, "copy")
+    d = {
+        "kernel": KERNEL_NAME, "source_sha": kernel_source_sha(),
+        "fetch_kib": mf, "write_kib": mw, "dispatches": [nf, nw],
+        "copy_kernel": cname, "copy_bytes": copy_bytes,
+        "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": copy_bytes / (cf * 1024), "write_scale": copy_bytes / (cw * 1024),
+    }
+    txt = json.dumps(d, indent=1)
+    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
+    with open(PMC_SUMMARY, "w", encoding="utf-8") as fh:
+        fh.write(txt + "\n---\n" + f"source: {fetch_csv}, {write_csv}\n")
+    print(txt)
+
+
+def profile_pass(args):
+    """Short run for rocprofv3 counter collection: a few layer launches plus a
+    1 GiB device copy (the calibration kernel of known size)."""
+    import numpy as np
+    import torch
+
+    import quantized_moe_weight_amd as pq
+    import workloads
+    torch.cuda.set_device(0)
+    shp = workloads.MOE_SHAPE
+    w13, s13, w2, s2 = build_bank(pq, shp)
+    x_bits = workloads.activation_bf16(1, shp.H, workload=workloads.MOE_LAYER)
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    call = pq.MoeLayerCall(w13, s13, w2, s2, M=1, top_k=shp.top_k)
+    pool = [torch.from_numpy(workloads.router_logits(1, shp.E, workload=workloads.MOE_LAYER, draw=d)).cuda()
+            for d in range(64)]
+    for i in range(args.steps):
+        call(x, pool[i % 64])
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profile pass: {args.steps} layer launches, 3 copies of {COPY_BYTES} bytes", flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--m", type=int, default=1, choices=[1, 2, 4, 8])
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("RANK", "0")) != 0:
+        return
+    if args.profile_pass:
+        profile_pass(args)
+        return
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

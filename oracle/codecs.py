@@ -13,57 +13,51 @@ from __future__ import annotations
 import numpy as np
 
 E4M3_MAX = 448.0
-_E4M3_MIN_NORMAL = 2.0 ** -6
-_E4M3_SUBNORMAL_QUANTUM = 2.0 ** -9
 
 
-def e4m3_decode(codes) -> np.ndarray:
-    """Value of each E4M3FN byte, as float64 (NaN for 0x7F and 0xFF).
+def _e4m3_value(c: int) -> float:
+    """Value of one E4M3FN byte from the format definition (NaN for 0x7F/0xFF).
 
     Byte layout s|eeee|mmm.  Exponent field 0 is subnormal: (-1)^s * 2^-6 * m/8.
     Exponent fields 1..15 are normal: (-1)^s * 2^(e-7) * (1 + m/8), except that
     e=15, m=7 is NaN.  There is no infinity.  (OCP OFP8 definition of E4M3.)
     """
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
-    s = (c >> 7) & 1
-    e = (c >> 3) & 0xF
-    m = c & 0x7
-    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
-    val = np.where(s == 1, -mag, mag)
-    return np.where((e == 15) & (m == 7), np.nan, val)
+    s, e, m = (c >> 7) & 1, (c >> 3) & 0xF, c & 0x7
+    if e == 15 and m == 7:
+        return float("nan")
+    mag = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -mag if s else mag
+
+
+# the 256 decoded values, and the 126 midpoints between consecutive non-negative finite values
+_E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+_E4M3_MIDPOINTS = (_E4M3_TABLE[1:0x7F] + _E4M3_TABLE[0:0x7E]) / 2.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3FN byte, as float64 (NaN for 0x7F and 0xFF)."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e4m3_encode(values) -> np.ndarray:
     """Encode float32 values to E4M3FN bytes.
 
-    Rounding is to nearest with ties to even on the 3-bit mantissa (the
-    subnormal grid is 2^-9); magnitudes at or above 448 saturate to 448
-    ("satfinite"); NaN encodes to 0x7F.  The pages give no rounding or overflow
-    rule; this is the reading taken (round-to-nearest-even is the IEEE default,
-    saturation keeps a scaled block finite).
+    Rounding is to the nearest representable magnitude with ties to the even
+    code (the even mantissa), found by bisection over the midpoints between
+    consecutive codes; magnitudes beyond the largest midpoint (including all
+    values at or above 448, and infinities) take the largest finite code 0x7E
+    ("satfinite"); NaN encodes to 0x7F; the sign bit is copied.  The pages give
+    no rounding or overflow rule; this is the reading taken (round to nearest
+    even is the IEEE default, saturation keeps a scaled block finite).
     """
     v = np.asarray(values, dtype=np.float32)
     a = np.abs(v).astype(np.float64)
-    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
-
-    # subnormal range: count multiples of 2^-9, round half to even
-    n_sub = np.rint(a / _E4M3_SUBNORMAL_QUANTUM)            # 0..8; 8 is the first normal
-    # normal range: a = 2^e * (1 + f), round f to 3 bits
-    safe = np.where((a > 0) & np.isfinite(a), a, 1.0)
-    frac, ex = np.frexp(safe)                  # safe = frac * 2^ex, 0.5 <= frac < 1 (exact)
-    e = ex.astype(np.int64) - 1                # safe = (2*frac) * 2^e, 1 <= 2*frac < 2
-    mant = np.rint((2.0 * frac - 1.0) * 8.0).astype(np.int64)   # 0..8, exact scaling
-    e = np.where(mant == 8, e + 1, e)
-    mant = np.where(mant == 8, 0, mant)
-    code_norm = ((e + 7) << 3) | mant
-
-    n_sub = np.where(a < _E4M3_MIN_NORMAL, n_sub, 0.0).astype(np.int64)
-    code = np.where(a < _E4M3_MIN_NORMAL, n_sub, code_norm)
-    code = np.where(a >= E4M3_MAX, 0x7E, code)
-    code = np.minimum(code, 0x7E)
-    code = code | sign
-    code = np.where(np.isnan(v), 0x7F, code)
-    return code.astype(np.uint8)
+    c = np.searchsorted(_E4M3_MIDPOINTS, a, side="left")       # mids[c-1] < a <= mids[c]
+    mid = _E4M3_MIDPOINTS[np.minimum(c, len(_E4M3_MIDPOINTS) - 1)]
+    tie = (c < len(_E4M3_MIDPOINTS)) & (a == mid)
+    c = np.where(tie & (c % 2 == 1), c + 1, c)                  # a tie goes to the even code
+    code = c.astype(np.uint8) | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(v), np.uint8(0x7F), code).astype(np.uint8)
 
 
 def bf16_round(values) -> np.ndarray:

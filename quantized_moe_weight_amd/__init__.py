@@ -195,3 +195,47 @@ def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=
     if debug:
         res.update(h=h, hq=hq, hs=hs)
     return res
+
+
+class MoeLayerCall:
+    """A prepared moe_decode_layer call for repeated decode steps: output, routing
+    and workspace buffers are allocated once and the raw pointers resolved up
+    front, so each step is one C call (argument marshalling only)."""
+
+    def __init__(self, w13, s13, w2, s2, M: int, top_k: int = 8, debug: bool = False):
+        _need(w13, torch.uint8, 3, "w13")
+        _need(s13, torch.float32, 3, "s13")
+        _need(w2, torch.uint8, 3, "w2")
+        _need(s2, torch.float32, 3, "s2")
+        self.E, two_i, self.H = w13.shape
+        self.I = two_i // 2
+        self.M, self.top_k = M, top_k
+        dev = w13.device
+        self.w = (w13, s13, w2, s2)
+        self.out = torch.empty((M, self.H), dtype=torch.bfloat16, device=dev)
+        self.topk_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((M, top_k), dtype=torch.float32, device=dev)
+        nb = moe_workspace_bytes(M, self.H, self.I, self.E, top_k)
+        if nb == 0:
+            raise PqError("moe_decode_layer_workspace", -2)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        self.h = torch.empty((M, top_k, self.I), dtype=torch.bfloat16, device=dev) if debug else None
+        self.hq = torch.empty((M, top_k, self.I), dtype=torch.uint8, device=dev) if debug else None
+        self.hs = torch.empty((M, top_k, self.I // 128), dtype=torch.float32, device=dev) if debug else None
+        self._fn = lib().moe_decode_layer
+        _check(lib().pq_workspace_init(_p(self.ws), nb, _stream()), "pq_workspace_init")
+        self._fixed = [_p(t) for t in (w13, s13, w2, s2, self.out, self.h, self.hq, self.hs, self.ws)]
+        self._ids, self._w = _p(self.topk_ids), _p(self.topk_w)
+
+    def __call__(self, x, logits, stream=None):
+        """x bf16 [M,H], logits fp32 [M,E] (device tensors, contiguous).  Returns ``out``."""
+        w13, s13, w2, s2, out, h, hq, hs, ws = self._fixed
+        st = self._fn(_p(x), self.M, self.H, _p(logits), self._ids, self._w, self.E, self.top_k, self.I,
+                      w13, s13, w2, s2, out, h, hq, hs, ws, self.ws.numel(),
+                      ctypes.c_void_p(stream) if stream is not None else _stream())
+        if st != 0:
+            raise PqError("moe_decode_layer", st)
+        return self.out
+
+    def check(self) -> int:
+        return lib().pq_workspace_check(_p(self.ws), _stream())

@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kThreads) void gemv_fp8_kernel(GemvArgs a) {
       const uint32_t row = (uint32_t)(ir + j * a.R);
       const uint32_t wbase = row * (uint32_t)a.K + kc;                       // uniform
       const uint32_t sbase = (row * (uint32_t)nb + kc / pq::kBlock) * 4u;   // uniform
-      wb[j] = pq::buf_load16(wr, ok ? wbase + lane16 : pq::kOOB);
-      sb[j] = pq::buf_load_f32(sr, ok ? sbase + lane_blk4 : pq::kOOB);
+      wb[j] = pq::buf_load16_nt(wr, ok ? wbase + lane16 : pq::kOOB);
+      sb[j] = pq::buf_load_f32_nt(sr, ok ? sbase + lane_blk4 : pq::kOOB);
     }
     if (++ic == a.nch) {
       ic = 0;

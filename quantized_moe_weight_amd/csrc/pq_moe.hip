@@ -11,31 +11,34 @@
 // merging small kernels into few dispatches raised decode from 59% to 81% of
 // measured bandwidth.  Here the whole layer is one launch.
 //
-// Structure (one persistent block per CU, 8 waves, static work split)
-//   A. every block routes the M tokens redundantly (a few hundred ALU ops) and
-//      builds the union of routed experts in first-appearance order; block 0
-//      writes the routing outputs.
-//   B. every block live-quantises x into LDS while its first gate_up weight
+// Structure (persistent blocks, all resident, 8 waves each, static work split)
+//   A. routing: wave m ranks token m's logits (top-k, ties to the lower id,
+//      softmax over the selected logits); wave 0 then builds the union of
+//      routed experts in first-appearance order.  Every block does this
+//      redundantly (a few hundred ALU ops); block 0 writes the routing outputs.
+//   B. the block live-quantises x into LDS while its first gate_up weight
 //      loads are in flight.
 //   C. gate_up units (union entry u, h-row i): each wave streams a contiguous
-//      range of units (gate row + up row, 1 KB chunks per lane-step, a ring of
-//      D steps in flight) and writes h = silu(g)*u as bf16 for every token
-//      routed to u.  Each wave then counts its rows into per-(u, 128-row group)
-//      counters; the wave completing a group re-quantises that group of h for
-//      every token (deterministic: the quantisation depends on values only)
-//      and bumps the phase counter.
-//   D. down units (output row n, all union entries): a wave issues its first
+//      range of units (gate row + up row, one 1 KB chunk per lane-step, a ring
+//      of DG steps in flight) and stores h = silu(g)*u (bf16) for every token
+//      routed to u.  The block then counts its rows into per-(u, 128-row
+//      group) counters; the block completing a group re-quantises that group
+//      of h for every token (the result depends on values only) and bumps the
+//      phase counter.
+//   D. down units (output row n, all union entries): waves issue their first
 //      down weight loads, the block waits for the phase counter, stages the
-//      quantised h of all (token, slot) pairs in LDS and streams the rows; per
-//      row every (token, slot) partial is reduced across the wave and the
-//      tokens' outputs are combined in slot order.
-//   E. the last block to finish resets every counter it used, so the
-//      workspace is ready for the next call without a clearing launch.
+//      quantised h of every (token, slot) pair in LDS and streams its rows; per
+//      row each (token, slot) partial is reduced across the wave and each
+//      token's slots are combined in slot order.
+//   E. the last block to finish resets the counters it used, so the workspace
+//      is ready for the next call without a clearing launch.
 //
+// Cross-block data (h, its quantisation, counters) travels through the
+// agent-coherent (sc1) path: no L2 writeback or invalidate is needed.
 // Every weight byte of the union is read once per call.  The arithmetic done
 // for one token does not depend on the other tokens of the call (same lane
-// split, same reduction order), so a row of an M-token verify call is bitwise
-// equal to the same token decoded alone.
+// split, same reduction order), so a token's output in an M-token verify call
+// is bitwise equal to the same token decoded alone.
 #include <stdlib.h>
 
 #include "pq_quant_dev.h"
@@ -50,8 +53,8 @@ constexpr int kMaxPairs = kMaxM * kMaxTopK;   // 64 = one lane per (token, slot)
 constexpr int kMaxUnion = kMaxPairs;
 constexpr int kMaxE = 1024;
 constexpr int kXPre = 2;
-constexpr int DG = 8;     // gate_up ring depth (chunk-steps; 2 rows per step)
-constexpr int DD = 16;    // down ring depth (chunk-steps; 1 row per step)
+constexpr int DG = 4;     // gate_up ring depth (chunk-steps; 2 rows per step)
+constexpr int DD = 8;     // down ring depth (chunk-steps; 1 row per step)
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 struct MoeArgs {
@@ -74,6 +77,7 @@ struct MoeArgs {
   int M, H, I, E, top_k;
   int routed;
   uint32_t spin_limit;
+  int ybuf_off;     // offset (in floats) of the per-block y buffer after the LDS scales
 };
 
 struct Route {
@@ -87,108 +91,128 @@ struct Route {
 
 __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// start of part i when n items are split over p parts as evenly as possible
+__device__ __forceinline__ int split_start(int n, int p, int i) {
+  const int q = n / p, r = n - (n / p) * p;
+  return i * q + (i < r ? i : r);
+}
+
+// total order on finite floats as unsigned keys (-0 and +0 are one key)
 __device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);   // -0 and +0 compare equal
+  const uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o, pq::kWave);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, pq::kWave);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Phase A, executed by one wave.  Top-k of each token's logits (descending,
-// ties to the lower id), softmax over the selected logits, then the union.
-__device__ void route_wave(const MoeArgs& a, Route& r, pq::WsHeader* hdr) {
+// Top-k of token m's logits by one wave.  Lane l owns experts l, l+64, ...;
+// it first sorts its own candidates (key descending, id ascending), then each
+// of the k rounds takes the wave-wide maximum of the lanes' current heads;
+// among lanes holding the maximum key the lowest expert id wins, so equal
+// logits go to the lower id.  KPER = candidates per lane (E <= 64 * KPER).
+template <int KPER>
+__device__ void route_token(const MoeArgs& a, Route& r, int m) {
+  const int lane = pq::lane_id();
+  // all logit loads issued before the first wait (past E: zero-filled, key 0)
+  const pq::rsrc_t lr = pq::make_rsrc(a.logits + (size_t)m * a.E, (uint32_t)a.E * 4u);
+  float lv[KPER];
+#pragma unroll
+  for (int q = 0; q < KPER; ++q) lv[q] = pq::buf_load_f32(lr, (uint32_t)(q * pq::kWave + lane) * 4u);
+  uint32_t key[KPER];
+  int eid[KPER];
+#pragma unroll
+  for (int q = 0; q < KPER; ++q) {
+    eid[q] = q * pq::kWave + lane;
+    key[q] = eid[q] < a.E ? order_key(lv[q]) : 0u;
+  }
+  // insertion sort of the lane's candidates: larger key first; ids start
+  // ascending and only strictly larger keys move up, so ties stay id-ascending
+#pragma unroll
+  for (int i = 1; i < KPER; ++i) {
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool sw = key[j] > key[j - 1];
+      const uint32_t k0 = key[j - 1], k1 = key[j];
+      const int e0 = eid[j - 1], e1 = eid[j];
+      key[j - 1] = sw ? k1 : k0; key[j] = sw ? k0 : k1;
+      eid[j - 1] = sw ? e1 : e0; eid[j] = sw ? e0 : e1;
+    }
+  }
+  uint32_t my_key = 0;
+  int my_id = 0;
+  for (int j = 0; j < a.top_k; ++j) {
+    const uint32_t mk = pq::wave_max_u32(key[0]);
+    uint64_t tied = __ballot(key[0] == mk);
+    int win = (int)__builtin_ctzll(tied);
+    int id = __builtin_amdgcn_readlane(eid[0], win);
+    tied &= tied - 1;
+    while (tied) {                                   // rare: equal keys on several lanes
+      const int l2 = (int)__builtin_ctzll(tied);
+      const int other = __builtin_amdgcn_readlane(eid[0], l2);
+      if (other < id) { id = other; win = l2; }
+      tied &= tied - 1;
+    }
+    if (lane == win) {                               // the winning lane pops its head
+#pragma unroll
+      for (int q = 0; q + 1 < KPER; ++q) { key[q] = key[q + 1]; eid[q] = eid[q + 1]; }
+      key[KPER - 1] = 0u;
+    }
+    if (lane == j) {
+      my_id = id;
+      my_key = mk;
+    }
+  }
+  const float sel = key_value(my_key);
+  const float l0 = __shfl(sel, 0, pq::kWave);
+  const float ex = lane < a.top_k ? expf(sel - l0) : 0.0f;
+  const float den = pq::wave_sum(ex);
+  if (lane < a.top_k) {
+    const float wgt = ex / den;
+    r.ids[m * a.top_k + lane] = my_id;
+    r.w[m * a.top_k + lane] = wgt;
+    if (blockIdx.x == 0) {
+      a.topk_ids[m * a.top_k + lane] = my_id;
+      a.topk_w[m * a.top_k + lane] = wgt;
+    }
+  }
+}
+
+// Union of routed experts in first-appearance order over pairs p = m*top_k+j
+// (one wave; lane p owns pair p): repeatedly take the lowest unassigned pair,
+// and assign every pair with the same expert to a new union entry.
+__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, int tp) {
   const int lane = pq::lane_id();
   const int P = a.M * a.top_k;
-  if (a.routed) {
-    constexpr int kPer = kMaxE / pq::kWave;   // 16 logits per lane
-    for (int m = 0; m < a.M; ++m) {
-      uint32_t keys[kPer];
-#pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int e = q * pq::kWave + lane;
-        keys[q] = e < a.E ? order_key(a.logits[(size_t)m * a.E + e]) : 0u;
-      }
-      uint32_t taken = 0;
-      float sel = 0.0f;
-      int sel_id = 0;
-      for (int j = 0; j < a.top_k; ++j) {
-        // lane-local best: highest key, then lowest id
-        uint64_t best = 0;
-#pragma unroll
-        for (int q = 0; q < kPer; ++q) {
-          const int e = q * pq::kWave + lane;
-          const bool live = e < a.E && !((taken >> q) & 1u);
-          const uint64_t k = live ? (((uint64_t)keys[q] << 32) | (uint32_t)(~e)) : 0ull;
-          best = k > best ? k : best;
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          const uint64_t other = shfl_xor_u64(best, o);
-          best = other > best ? other : best;
-        }
-        const int id = (int)(~(uint32_t)best);
-        if ((id & (pq::kWave - 1)) == lane) taken |= 1u << (id / pq::kWave);
-        if (lane == j) {
-          sel_id = id;
-          sel = a.logits[(size_t)m * a.E + id];
-        }
-      }
-      // softmax over the k selected logits (lanes 0..k-1), relative to the top one
-      const float l0 = __shfl(sel, 0, pq::kWave);
-      const float ex = lane < a.top_k ? expf(sel - l0) : 0.0f;
-      const float den = pq::wave_sum(ex);
-      if (lane < a.top_k) {
-        r.ids[m * a.top_k + lane] = sel_id;
-        r.w[m * a.top_k + lane] = ex / den;
-        if (blockIdx.x == 0) {
-          a.topk_ids[m * a.top_k + lane] = sel_id;
-          a.topk_w[m * a.top_k + lane] = ex / den;
-        }
-      }
+  const int id = lane < P ? r.ids[lane] : -1;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint64_t remaining = __ballot(lane < P);
+  int u = 0;
+  while (remaining) {
+    const int p0 = (int)__builtin_ctzll(remaining);
+    const int e = __builtin_amdgcn_readlane(id, p0);
+    const uint64_t mine = __ballot(lane < P && id == e);
+    const int n = __popcll(mine);
+    if (lane == p0) {
+      r.uexp[u] = e;
+      r.unp[u] = n < tp ? n : tp;
     }
-  } else if (lane < P) {
-    int id = a.topk_ids[lane];
-    if (id < 0 || id >= a.E) {
-      if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
-      id = 0;
+    if ((mine >> lane) & 1ull) {
+      const int before = __popcll(mine & below);
+      if (before < tp) r.upairs[u][before] = lane;
+      else if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);   // an expert twice in one token
     }
-    r.ids[lane] = id;
-    r.w[lane] = a.topk_w[lane];
+    remaining &= ~mine;
+    ++u;
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-
-  // union in first-appearance order over pairs p = m * top_k + j
-  const int id = lane < P ? r.ids[lane] : -1 - lane;
-  int first = lane, before = 0, total = 0;
-  for (int q = 0; q < P; ++q) {
-    const int v = __shfl(id, q, pq::kWave);
-    if (v == id) {
-      first = q < first ? q : first;
-      before += q < lane ? 1 : 0;
-      ++total;
-    }
-  }
-  const bool is_first = lane < P && first == lane;
-  const uint64_t firsts = __ballot(is_first);
-  const int u = __popcll(firsts & ((1ull << first) - 1ull));
-  if (lane < P) {
-    if (is_first) {
-      r.uexp[u] = id;
-      r.unp[u] = total < kMaxM ? total : kMaxM;
-    }
-    if (before < kMaxM) r.upairs[u][before] = lane;
-    else if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);   // duplicate ids in one token
-  }
-  if (lane == 0) r.nU = __popcll(firsts);
+  if (lane == 0) r.nU = u;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// TP: compile-time bound on the (token, slot) pairs routed to one expert in a
+// call (the smallest power of two >= M), so the per-pair loops unroll tightly.
+template <int TP>
 __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Route route;
@@ -209,8 +233,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   const uint32_t lane16 = 16u * (uint32_t)lane;
   const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
 
-  size_t act_bytes = (size_t)a.M * H > (size_t)P * I ? (size_t)a.M * H : (size_t)P * I;
-  uint8_t* act = smem;                                                  // codes
+  const size_t act_bytes = (size_t)a.M * H > (size_t)P * I ? (size_t)a.M * H : (size_t)P * I;
+  uint8_t* act = smem;                                                              // codes
   float* acts = reinterpret_cast<float*>(smem + pqhost::align_up(act_bytes, 16));   // scales
 
   // ---- x loads first (independent of routing) ------------------------------
@@ -220,48 +244,23 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 #pragma unroll
   for (int it = 0; it < kXPre; ++it) xraw[it] = pq::buf_load16(xr, (uint32_t)(it * kThreads + threadIdx.x) * 16u);
 
-  // ---- A. routing -----------------------------------------------------------
-  if (wv == 0) route_wave(a, route, hdr);
-  __syncthreads();
-  const int nU = ufl(route.nU);
-
-  // ---- C(prefetch). gate_up ring ------------------------------------------
-  const int gu_units = nU * I;
-  const int g0 = (int)((long)gw * gu_units / T);
-  const int g1 = (int)((long)(gw + 1) * gu_units / T);
-  const int gsteps = (g1 - g0) * nchH;
-
-  uint4 wb[DG][2];
-  float sb[DG][2];
-  int iu = g0 / I, ii = g0 - (g0 / I) * I, ic = 0;
-  int ie = ufl(route.uexp[iu < nU ? iu : 0]);
-  auto issue_gu = [&](uint4 (&w)[2], float (&s)[2]) {
-    const bool in_range = iu * I + ii < g1;
-    const uint32_t kc = (uint32_t)(ic * pq::kChunk);
-    const bool ok = in_range && kc + lane16 < (uint32_t)H;
-    const uint8_t* wbase = a.w13 + (size_t)ie * 2 * I * H;
-    const float* sbase = a.s13 + (size_t)ie * 2 * I * nbH;
-    const pq::rsrc_t wr = pq::make_rsrc(wbase, (uint32_t)(2 * I * H));
-    const pq::rsrc_t sr = pq::make_rsrc(sbase, (uint32_t)(2 * I * nbH * 4));
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t row = (uint32_t)(ii + j * I);
-      w[j] = pq::buf_load16(wr, ok ? row * (uint32_t)H + kc + lane16 : pq::kOOB);
-      s[j] = pq::buf_load_f32(sr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+  // ---- A. routing (waves 0..M-1, one token each) -----------------------------
+  if (a.routed) {
+    if (wv < a.M) {
+      if (a.E <= 256) route_token<4>(a, route, wv);
+      else route_token<16>(a, route, wv);
     }
-    if (++ic == nchH) {
-      ic = 0;
-      if (++ii == I) {
-        ii = 0;
-        ++iu;
-        ie = ufl(route.uexp[iu < nU ? iu : 0]);
-      }
+  } else if (wv == 0 && lane < P) {
+    int id = a.topk_ids[lane];
+    if (id < 0 || id >= a.E) {
+      if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
+      id = 0;
     }
-  };
-#pragma unroll
-  for (int q = 0; q < DG; ++q) issue_gu(wb[q], sb[q]);
+    route.ids[lane] = id;
+    route.w[lane] = a.topk_w[lane];
+  }
 
-  // ---- B. live activation quantisation into LDS ----------------------------
+  // ---- B. live activation quantisation into LDS (x loads issued at entry) --
   {
     const int iters = (int)((totx8 + kThreads - 1) / kThreads);
     for (int it = 0; it < iters; ++it) {
@@ -278,14 +277,67 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     }
   }
   __syncthreads();
+  if (wv == 0) build_union(a, route, hdr, TP);
+  __syncthreads();
+  const int nU = ufl(route.nU);
+
+  // ---- C(prefetch). gate_up ring ------------------------------------------
+  const int gu_units = nU * I;
+  const int g0 = ufl(split_start(gu_units, (int)T, gw));
+  const int g1 = ufl(split_start(gu_units, (int)T, gw + 1));
+  const int gsteps = (g1 - g0) * nchH;
+
+  uint4 wb[DG][2];
+  float sb[DG][2];
+  int iu = g0 / I, ii = g0 - (g0 / I) * I, ic = 0;
+  pq::rsrc_t gwr, gsr;
+  auto set_gu_expert = [&]() {
+    const int e = ufl(route.uexp[iu < nU ? iu : 0]);
+    gwr = pq::make_rsrc(a.w13 + (size_t)e * 2 * I * H, (uint32_t)(2 * I * H));
+    gsr = pq::make_rsrc(a.s13 + (size_t)e * 2 * I * nbH, (uint32_t)(2 * I * nbH * 4));
+  };
+  set_gu_expert();
+  auto issue_gu = [&](uint4 (&w)[2], float (&s)[2]) {
+    const bool in_range = iu * I + ii < g1;
+    const uint32_t kc = (uint32_t)(ic * pq::kChunk);
+    const bool ok = in_range && kc + lane16 < (uint32_t)H;
+    const pq::rsrc_t wr = gwr, sr = gsr;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = (uint32_t)(ii + j * I);
+      w[j] = pq::buf_load16_nt(wr, ok ? row * (uint32_t)H + kc + lane16 : pq::kOOB);
+      s[j] = pq::buf_load_f32_nt(sr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+    }
+    if (++ic == nchH) {
+      ic = 0;
+      if (++ii == I) {
+        ii = 0;
+        ++iu;
+        set_gu_expert();
+      }
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < DG; ++q) issue_gu(wb[q], sb[q]);
 
   // ---- C. gate_up + SiLU*up -------------------------------------------------
   {
-    float accg[kMaxM], accu[kMaxM];
+    float accg[TP], accu[TP];
+    int pr[TP], pm[TP];
 #pragma unroll
-    for (int t = 0; t < kMaxM; ++t) accg[t] = accu[t] = 0.0f;
+    for (int t = 0; t < TP; ++t) accg[t] = accu[t] = 0.0f;
     int cu = g0 / I, ci = g0 - (g0 / I) * I, cc = 0;
-    int cnp = ufl(route.unp[cu < nU ? cu : 0]);
+    int cnp = 0;
+    auto load_pairs = [&]() {
+      const int uu = cu < nU ? cu : 0;
+      cnp = ufl(route.unp[uu]);
+#pragma unroll
+      for (int t = 0; t < TP; ++t) {
+        pr[t] = ufl(route.upairs[uu][t]);
+        pm[t] = pr[t] / K;
+      }
+    };
+    load_pairs();
     for (int base = 0; base < gsteps; base += DG) {
 #pragma unroll
       for (int q = 0; q < DG; ++q) {
@@ -295,12 +347,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
             const pq::Bf16x16 wg = pq::widen16(wb[q][0]);
             const pq::Bf16x16 wu = pq::widen16(wb[q][1]);
 #pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
+            for (int t = 0; t < TP; ++t) {
               if (t < cnp) {
-                const int p = ufl(route.upairs[cu][t]);
-                const int m = p / K;
-                const pq::Bf16x16 xv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)m * H + off));
-                const float xs = acts[m * nbH + off / pq::kBlock];
+                const pq::Bf16x16 xv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pm[t] * H + off));
+                const float xs = acts[pm[t] * nbH + off / pq::kBlock];
                 accg[t] = fmaf(pq::dot16(wg, xv), sb[q][0] * xs, accg[t]);
                 accu[t] = fmaf(pq::dot16(wu, xv), sb[q][1] * xs, accu[t]);
               }
@@ -308,15 +358,14 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
           }
           if (cc == nchH - 1) {            // unit (cu, ci) done: h for every routed token
 #pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
+            for (int t = 0; t < TP; ++t) {
               if (t < cnp) {
                 const float g = pq::wave_sum(accg[t]);
                 const float u = pq::wave_sum(accu[t]);
                 if (lane == 0) {
-                  const int p = route.upairs[cu][t];
                   const uint16_t hb = pq::bf16_rne(silu_mul(g, u));
-                  a.hbuf[(size_t)p * I + ci] = hb;
-                  if (a.h_dbg) a.h_dbg[(size_t)p * I + ci] = hb;
+                  pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + ci, hb);
+                  if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + ci] = hb;
                 }
               }
               accg[t] = accu[t] = 0.0f;
@@ -327,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
             if (++ci == I) {
               ci = 0;
               ++cu;
-              cnp = ufl(route.unp[cu < nU ? cu : 0]);
+              load_pairs();
             }
           }
         }
@@ -335,156 +384,174 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
       }
     }
   }
+  pq::wait_vm();            // this wave's h stores are complete
+  __syncthreads();
 
-  // ---- count finished h rows per (u, 128-row group); the completing wave
-  //      re-quantises that group for every token routed to u ---------------
-  if (g1 > g0) {
-    pq::fence_release();
-    for (int G = g0 >> 7; G <= (g1 - 1) >> 7; ++G) {
-      const int lo = g0 > (G << 7) ? g0 : (G << 7);
-      const int hi = g1 < ((G + 1) << 7) ? g1 : ((G + 1) << 7);
+  // ---- count the block's finished h rows per (u, 128-row group); the block
+  //      completing a group re-quantises it for every token routed to u -----
+  if (wv == 0) {
+    const int b0 = split_start(gu_units, (int)T, (int)blockIdx.x * kWaves);
+    const int b1 = split_start(gu_units, (int)T, (int)(blockIdx.x + 1) * kWaves);
+    uint32_t completed = 0;
+    for (int G = b0 >> 7; b1 > b0 && G <= (b1 - 1) >> 7; ++G) {
+      const int lo = b0 > (G << 7) ? b0 : (G << 7);
+      const int hi = b1 < ((G + 1) << 7) ? b1 : ((G + 1) << 7);
       uint32_t old = 0;
       if (lane == 0) old = pq::atomic_add_relaxed(&gcnt[G], (uint32_t)(hi - lo));
       old = (uint32_t)ufl((int)__shfl(old, 0, pq::kWave));
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (old + (uint32_t)(hi - lo) == 128u) {
-        pq::fence_acquire();
         const int u = G / nbI, g = G - (G / nbI) * nbI;
         const int np = ufl(route.unp[u]);
         for (int t = 0; t < np; ++t) {
           const int p = ufl(route.upairs[u][t]);
           const size_t e0 = (size_t)p * I + (size_t)g * pq::kBlock + 2 * lane;
-          const uint32_t two = *reinterpret_cast<const uint32_t*>(a.hbuf + e0);
-          float v[2] = {pq::bf16_to_f32(two & 0xffffu), pq::bf16_to_f32(two >> 16)};
-          float m = fmaxf(fabsf(v[0]), fabsf(v[1]));
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, pq::kWave));
+          const uint32_t two = pq::ld_agent_u32(reinterpret_cast<const uint32_t*>(a.hbuf + e0));
+          const float v0 = pq::bf16_to_f32(two & 0xffffu), v1 = pq::bf16_to_f32(two >> 16);
+          const float m = __uint_as_float(pq::wave_max_u32(__float_as_uint(fmaxf(fabsf(v0), fabsf(v1)))));
           const float s = pq::block_scale(m);
           const double rcp = 1.0 / (double)s;
-          const uint32_t c0 = pq::e4m3_encode(pq::quotient_f32(v[0], rcp));
-          const uint32_t c1 = pq::e4m3_encode(pq::quotient_f32(v[1], rcp));
-          const uint16_t cc2 = (uint16_t)(c0 | (c1 << 8));
-          *reinterpret_cast<uint16_t*>(a.hq + e0) = cc2;
-          if (a.hq_dbg) *reinterpret_cast<uint16_t*>(a.hq_dbg + e0) = cc2;
+          const uint16_t c2 =
+              (uint16_t)pq::e4m3_pack2<false>(pq::quotient_f32(v0, rcp), pq::quotient_f32(v1, rcp), 0u);
+          pq::st_agent_u16(reinterpret_cast<uint16_t*>(a.hq + e0), c2);
+          if (a.hq_dbg) *reinterpret_cast<uint16_t*>(a.hq_dbg + e0) = c2;
           if (lane == 0) {
-            a.hs[(size_t)p * nbI + g] = s;
+            pq::st_agent_u32(reinterpret_cast<uint32_t*>(a.hs) + (size_t)p * nbI + g, __float_as_uint(s));
             if (a.hs_dbg) a.hs_dbg[(size_t)p * nbI + g] = s;
           }
         }
-        pq::fence_release();
-        if (lane == 0) pq::atomic_add_relaxed(&hdr->done, 1u);
+        ++completed;
       }
+    }
+    if (completed) {
+      pq::wait_vm();       // the quantised groups are complete before they are announced
+      if (lane == 0) pq::atomic_add_relaxed(&hdr->done, completed);
     }
   }
 
   // ---- D. down projection + weighted combine --------------------------------
-  const int d0 = (int)((long)gw * H / T);
-  const int d1 = (int)((long)(gw + 1) * H / T);
-  const int dsteps = (d1 - d0) * nU * nchI;
+  // Output rows are dealt to blocks as evenly as possible; inside a block the
+  // (row, union entry) units are split evenly over the waves.  Each unit's y
+  // for every routed token goes to LDS; the block then combines each token's
+  // slots in slot order.
+  const int r0 = split_start(H, (int)gridDim.x, (int)blockIdx.x);
+  const int r1 = split_start(H, (int)gridDim.x, (int)blockIdx.x + 1);
+  const int bunits = (r1 - r0) * nU;
+  const int v0 = ufl(split_start(bunits, kWaves, wv));
+  const int v1 = ufl(split_start(bunits, kWaves, wv + 1));
+  const int dsteps = (v1 - v0) * nchI;
+  float* ybuf = acts + a.ybuf_off;                 // [row_local][P] fp32
   uint4 wd[DD];
   float sd[DD];
-  int jn = d0, ju = 0, jc = 0;
-  int je = ufl(route.uexp[0]);
+  int jr = v0 / nU, ju = v0 - (v0 / nU) * nU, jc = 0;
+  pq::rsrc_t dwr, dsr;
+  auto set_dn_expert = [&]() {
+    const int e = ufl(route.uexp[ju]);
+    dwr = pq::make_rsrc(a.w2 + (size_t)e * H * I, (uint32_t)(H * I));
+    dsr = pq::make_rsrc(a.s2 + (size_t)e * H * nbI, (uint32_t)(H * nbI * 4));
+  };
+  set_dn_expert();
   auto issue_dn = [&](uint4& w, float& s) {
-    const bool in_range = jn < d1;
+    const bool in_range = jr * nU + ju < v1;
     const uint32_t kc = (uint32_t)(jc * pq::kChunk);
     const bool ok = in_range && kc + lane16 < (uint32_t)I;
-    const pq::rsrc_t wr = pq::make_rsrc(a.w2 + (size_t)je * H * I, (uint32_t)(H * I));
-    const pq::rsrc_t sr = pq::make_rsrc(a.s2 + (size_t)je * H * nbI, (uint32_t)(H * nbI * 4));
-    w = pq::buf_load16(wr, ok ? (uint32_t)jn * (uint32_t)I + kc + lane16 : pq::kOOB);
-    s = pq::buf_load_f32(sr, ok ? ((uint32_t)jn * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+    const uint32_t row = (uint32_t)(r0 + jr);
+    w = pq::buf_load16_nt(dwr, ok ? row * (uint32_t)I + kc + lane16 : pq::kOOB);
+    s = pq::buf_load_f32_nt(dsr, ok ? (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
     if (++jc == nchI) {
       jc = 0;
       if (++ju == nU) {
         ju = 0;
-        ++jn;
+        ++jr;
       }
-      je = ufl(route.uexp[ju]);
+      set_dn_expert();
     }
   };
 #pragma unroll
   for (int q = 0; q < DD; ++q) issue_dn(wd[q], sd[q]);
 
   // wait for every h group of the call, then stage the quantised h in LDS
-  __syncthreads();
   if (threadIdx.x == 0) pq::spin_wait_geq(&hdr->done, (uint32_t)(nU * nbI), hdr, a.spin_limit);
   __syncthreads();
-  pq::fence_acquire();
   {
-    const long n16 = (long)P * I / 16;
-    for (long t = threadIdx.x; t < n16; t += kThreads)
-      reinterpret_cast<uint4*>(act)[t] = reinterpret_cast<const uint4*>(a.hq)[t];
-    for (long t = threadIdx.x; t < (long)P * nbI; t += kThreads) acts[t] = a.hs[t];
+    const uint32_t* hq32 = reinterpret_cast<const uint32_t*>(a.hq);
+    const uint32_t* hs32 = reinterpret_cast<const uint32_t*>(a.hs);
+    uint32_t* act32 = reinterpret_cast<uint32_t*>(act);
+    uint32_t* acts32 = reinterpret_cast<uint32_t*>(acts);
+    const int n4 = P * I / 4;
+    for (int t = threadIdx.x; t < n4; t += kThreads) act32[t] = pq::ld_agent_u32(hq32 + t);
+    for (int t = threadIdx.x; t < P * nbI; t += kThreads) acts32[t] = pq::ld_agent_u32(hs32 + t);
   }
   __syncthreads();
 
   {
-    float acc[kMaxM];
+    float acc[TP];
+    int pr[TP];
 #pragma unroll
-    for (int t = 0; t < kMaxM; ++t) acc[t] = 0.0f;
-    float ycap = 0.0f;                 // lane p holds y of pair p for the current row
-    int cn = d0, cu = 0, cc = 0;
-    int cnp = ufl(route.unp[0]);
+    for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
+    int cr = v0 / nU, cu = v0 - (v0 / nU) * nU, cc = 0;
+    int cnp = 0;
+    auto load_pairs = [&]() {
+      cnp = ufl(route.unp[cu]);
+#pragma unroll
+      for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[cu][t]);
+    };
+    load_pairs();
     for (int base = 0; base < dsteps; base += DD) {
 #pragma unroll
       for (int q = 0; q < DD; ++q) {
         if (base + q < dsteps) {
           const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
           if (off < (uint32_t)I) {
-            const pq::Bf16x16 wv = pq::widen16(wd[q]);
+            const pq::Bf16x16 wv2 = pq::widen16(wd[q]);
 #pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
+            for (int t = 0; t < TP; ++t) {
               if (t < cnp) {
-                const int p = ufl(route.upairs[cu][t]);
-                const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)p * I + off));
-                const float hsc = acts[p * nbI + off / pq::kBlock];
-                acc[t] = fmaf(pq::dot16(wv, hv), sd[q] * hsc, acc[t]);
+                const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
+                const float hsc = acts[pr[t] * nbI + off / pq::kBlock];
+                acc[t] = fmaf(pq::dot16(wv2, hv), sd[q] * hsc, acc[t]);
               }
             }
           }
-          if (cc == nchI - 1) {           // (row cn, union entry cu) done
+          if (cc == nchI - 1) {           // unit (row cr, union entry cu) done
 #pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
+            for (int t = 0; t < TP; ++t) {
               if (t < cnp) {
                 const float y = pq::wave_sum(acc[t]);
-                const int p = ufl(route.upairs[cu][t]);
-                ycap = lane == p ? y : ycap;
+                if (lane == 0) ybuf[cr * P + pr[t]] = y;
               }
               acc[t] = 0.0f;
-            }
-            if (cu == nU - 1) {           // row cn done: combine each token's slots in order
-              float o = 0.0f;
-              const int mine = lane < a.M ? lane : 0;
-              for (int j = 0; j < K; ++j) {
-                const float y = __shfl(ycap, mine * K + j, pq::kWave);
-                o = fmaf(route.w[mine * K + j], y, o);
-              }
-              if (lane < a.M) a.out[(size_t)lane * H + cn] = pq::bf16_rne(o);
             }
           }
           if (++cc == nchI) {
             cc = 0;
             if (++cu == nU) {
               cu = 0;
-              ++cn;
+              ++cr;
             }
-            cnp = ufl(route.unp[cu]);
+            load_pairs();
           }
         }
         issue_dn(wd[q], sd[q]);
       }
     }
   }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < (r1 - r0) * a.M; idx += kThreads) {
+    const int rl = idx / a.M, m = idx - (idx / a.M) * a.M;
+    float o = 0.0f;
+    for (int j = 0; j < K; ++j) o = fmaf(route.w[m * K + j], ybuf[rl * P + m * K + j], o);
+    a.out[(size_t)m * H + r0 + rl] = pq::bf16_rne(o);
+  }
 
   // ---- E. the last block resets the counters of this call -------------------
   __syncthreads();
   if (threadIdx.x == 0) {
-    pq::fence_release();
     const uint32_t old = pq::atomic_add_relaxed(&hdr->exit_count, 1u);
     s_last = old == gridDim.x - 1;
   }
   __syncthreads();
   if (s_last) {
-    pq::fence_acquire();
     for (int t = threadIdx.x; t < nU * nbI; t += kThreads) pq::atomic_store_relaxed(&gcnt[t], 0u);
     if (threadIdx.x == 0) {
       pq::atomic_store_relaxed(&hdr->done, 0u);
@@ -498,10 +565,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 // ---------------------------------------------------------------------------
 struct MoePlan {
   size_t lds;
+  int ybuf_off;
   size_t off_h, off_hq, off_hs, ws_total;
 };
 
-int moe_plan(int M, int H, int I, int E, int top_k, MoePlan* p) {
+// num_cus bounds the rows a block can own (the grid has at least one block per
+// CU); num_cus <= 0 checks the shape and sizes the workspace only.
+int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, MoePlan* p) {
   if (M < 1 || M > kMaxM || top_k < 1 || top_k > kMaxTopK || E < top_k || E > kMaxE) return PQ_ERR_SHAPE;
   if (H < pq::kBlock || H % pq::kBlock || H > 16384 || I < pq::kBlock || I % pq::kBlock || I > 16384)
     return PQ_ERR_SHAPE;
@@ -510,9 +580,14 @@ int moe_plan(int M, int H, int I, int E, int top_k, MoePlan* p) {
   if (P * nbI > pq::kWsMaxCounters) return PQ_ERR_SHAPE;
   if ((size_t)2 * I * H > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
   const size_t act = (size_t)M * H > P * I ? (size_t)M * H : P * I;
-  const size_t actsc = ((size_t)M * H / pq::kBlock > P * nbI ? (size_t)M * H / pq::kBlock : P * nbI) * 4;
-  p->lds = pqhost::align_up(act, 16) + actsc;
-  if (p->lds + sizeof(Route) + 64 > 160 * 1024) return PQ_ERR_SHAPE;
+  const size_t nsc = (size_t)M * H / pq::kBlock > P * nbI ? (size_t)M * H / pq::kBlock : P * nbI;
+  p->ybuf_off = (int)nsc;
+  p->lds = 0;
+  if (num_cus > 0) {
+    const size_t rows_max = ((size_t)H + num_cus - 1) / num_cus;
+    p->lds = pqhost::align_up(act, 16) + (nsc + rows_max * P) * 4;
+    if (p->lds + sizeof(Route) + 64 > 160 * 1024) return PQ_ERR_SHAPE;
+  }
   p->off_h = pq::kWsDataOff;
   p->off_hq = pqhost::align_up(p->off_h + P * I * 2, 256);
   p->off_hs = pqhost::align_up(p->off_hq + P * I, 256);
@@ -520,33 +595,9 @@ int moe_plan(int M, int H, int I, int E, int top_k, MoePlan* p) {
   return PQ_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k) {
-  MoePlan pl;
-  if (moe_plan(M, H, I, E, top_k, &pl) != PQ_OK) return 0;
-  return pl.ws_total;
-}
-
-int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits, int32_t* topk_ids,
-                     float* topk_w, int E, int top_k, int I, const uint8_t* w13, const float* s13,
-                     const uint8_t* w2, const float* s2, uint16_t* out, uint16_t* h_dbg, uint8_t* hq_dbg,
-                     float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !topk_ids || !topk_w || !w13 || !s13 || !w2 || !s2 || !out || !ws) return PQ_ERR_NULL;
-  MoePlan pl;
-  int st = moe_plan(M, H, I, E, top_k, &pl);
-  if (st != PQ_OK) return st;
-  const void* ptrs[] = {x, router_logits, topk_ids, topk_w, w13, s13, w2, s2, out, h_dbg, hq_dbg, hs_dbg, ws};
-  for (const void* q : ptrs)
-    if (q && !pqhost::aligned16(q)) return PQ_ERR_ALIGN;
-  if (ws_bytes < pl.ws_total) return PQ_ERR_WORKSPACE;
-  pqhost::DeviceInfo dev;
-  st = pqhost::current_device_info(&dev);
-  if (st != PQ_OK) return st;
-
-  auto kern = moe_layer_kernel;
+template <int TP>
+int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& dev, hipStream_t stream) {
+  auto kern = moe_layer_kernel<TP>;
   static bool attr_set = false;
   if (!attr_set) {
     PQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -556,7 +607,39 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
   int per_cu = 0;
   PQ_HIP_CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads, pl.lds));
   if (per_cu < 1) return PQ_ERR_SHAPE;
-  int grid = dev.num_cus * per_cu;                  // every block resident: blocks wait on each other
+  const int grid = dev.num_cus * per_cu;   // every block resident: blocks wait on each other
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), pl.lds, stream, a);
+  PQ_HIP_CHECK(hipGetLastError());
+  return PQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k) {
+  MoePlan pl;
+  if (moe_plan(M, H, I, E, top_k, 0, &pl) != PQ_OK) return 0;
+  return pl.ws_total;
+}
+
+int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits, int32_t* topk_ids,
+                     float* topk_w, int E, int top_k, int I, const uint8_t* w13, const float* s13,
+                     const uint8_t* w2, const float* s2, uint16_t* out, uint16_t* h_dbg, uint8_t* hq_dbg,
+                     float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !topk_ids || !topk_w || !w13 || !s13 || !w2 || !s2 || !out || !ws) return PQ_ERR_NULL;
+  MoePlan pl;
+  int st = moe_plan(M, H, I, E, top_k, 0, &pl);       // shape checks (device independent)
+  if (st != PQ_OK) return st;
+  const void* ptrs[] = {x, router_logits, topk_ids, topk_w, w13, s13, w2, s2, out, h_dbg, hq_dbg, hs_dbg, ws};
+  for (const void* q : ptrs)
+    if (q && !pqhost::aligned16(q)) return PQ_ERR_ALIGN;
+  if (ws_bytes < pl.ws_total) return PQ_ERR_WORKSPACE;
+  pqhost::DeviceInfo dev;
+  st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+  st = moe_plan(M, H, I, E, top_k, dev.num_cus, &pl);
+  if (st != PQ_OK) return st;
 
   MoeArgs a;
   a.x = x; a.logits = router_logits; a.topk_ids = topk_ids; a.topk_w = topk_w;
@@ -569,12 +652,15 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
   a.M = M; a.H = H; a.I = I; a.E = E; a.top_k = top_k;
   a.routed = router_logits != nullptr;
   a.spin_limit = kSpinLimit;
+  a.ybuf_off = pl.ybuf_off;
   const char* lim = getenv("PQ_SPIN_LIMIT");
   if (lim && *lim) a.spin_limit = (uint32_t)strtoul(lim, nullptr, 10);
 
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), pl.lds, (hipStream_t)stream, a);
-  PQ_HIP_CHECK(hipGetLastError());
-  return PQ_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 1) return launch_moe<1>(a, pl, dev, s);
+  if (M == 2) return launch_moe<2>(a, pl, dev, s);
+  if (M <= 4) return launch_moe<4>(a, pl, dev, s);
+  return launch_moe<8>(a, pl, dev, s);
 }
 
 }  // extern "C"

@@ -22,12 +22,12 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 raw, float v[8]) {
 // Returns the 8 codes packed little-endian.
 __device__ __forceinline__ uint2 fp8_codes8(const float v[8], float s) {
   const double r = 1.0 / (double)s;
-  uint32_t c[8];
+  float q[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = e4m3_encode(quotient_f32(v[i], r));
+  for (int i = 0; i < 8; ++i) q[i] = quotient_f32(v[i], r);
   uint2 out;
-  out.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  out.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  out.x = e4m3_pack2<true>(q[2], q[3], e4m3_pack2<false>(q[0], q[1], 0u));
+  out.y = e4m3_pack2<true>(q[6], q[7], e4m3_pack2<false>(q[4], q[5], 0u));
   return out;
 }
 

@@ -210,3 +210,27 @@ def test_moe_full_size_layer(pq, M):
     ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=shp.top_k)
     worst = _check(pq, bank, x, res, ref, M, shp.top_k)
     print(f"full-size M={M}: union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
+
+
+@pytest.mark.parametrize("E", [16, 200, 256, 1000])
+def test_moe_routing_ties_and_signed_zero(pq, E):
+    """Equal logits go to the lower expert id; -0 and +0 are equal."""
+    import torch
+    M, H, I, k = 4, 256, 128, 8
+    bank = Bank(pq, E, H, I, seed=11)
+    rng = np.random.default_rng(E)
+    lg = np.round(rng.standard_normal((M, E)), 1).astype(np.float32)   # many exact ties
+    lg[1, :] = 0.0
+    lg[1, ::3] = -0.0
+    lg[2, :] = 1.5                                                     # everything tied
+    lg[3, E - 1] = 9.0
+    lg[3, E // 2] = 9.0
+    ids_ref, w_ref = oracle.route_topk(lg, k)
+    bank.fill(ids_ref)
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=11)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              logits=torch.from_numpy(lg).cuda(), top_k=k)
+    assert np.array_equal(res["topk_ids"].cpu().numpy(), ids_ref)
+    assert np.max(np.abs(res["topk_w"].cpu().numpy() - w_ref)) <= 1e-6
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k)
+    assert_gemv_close(bf16_to_np(res["out"]), ref["out"], ref["S"], f"ties E={E}")

@@ -24,7 +24,7 @@ __all__ = [
     "T_X", "T_W", "T_W13", "T_W2", "T_LOGITS", "T_OUTLIER",
     "generator", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "activation_bf16", "master_weights", "router_logits", "verify_logits",
-    "MoEShape", "MOE_SHAPE", "Q4_SHAPES",
+    "MoEShape", "MOE_SHAPE", "Q4_SHAPES", "torch_seed", "master_weights_torch",
 ]
 
 # workload keys (first spawn-key component)
@@ -116,3 +116,22 @@ def verify_logits(M: int, E: int, *, rho: float = 0.5, workload: int = MOE_VERIF
     s = g.standard_normal(E)
     e = g.standard_normal((M, E))
     return (np.sqrt(rho) * s[None, :] + np.sqrt(1.0 - rho) * e).astype(np.float32)
+
+
+def torch_seed(workload: int, tensor: int, expert: int = 0, seed: int = 0) -> int:
+    """64-bit seed for torch's device generator, derived from the same spawn key."""
+    ss = np.random.SeedSequence(seed, spawn_key=(int(workload), int(tensor), int(expert)))
+    return int(ss.generate_state(1, dtype=np.uint64)[0] >> np.uint64(1))
+
+
+def master_weights_torch(N: int, K: int, *, workload: int, tensor: int = T_W, expert: int = 0,
+                         seed: int = 0, sigma: float = 0.02, device: str = "cuda"):
+    """fp32 master weights [N,K] = fp32(sigma * N(0,1)) drawn on the device by torch's
+    seeded generator (used for the 10 GB expert bank, where host generation is slow).
+    The same (workload, tensor, expert, seed) always gives the same tensor on a given
+    device type; copying it to the host gives the CPU side the identical values."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(workload, tensor, expert, seed))
+    w = torch.randn((N, K), generator=g, device=device, dtype=torch.float32)
+    return w.mul_(sigma)

@@ -197,6 +197,13 @@ __device__ __forceinline__ float group_max(float v, int width) {  // within alig
   return v;
 }
 
+// First index of part i when n items are dealt to p parts as evenly as
+// possible (the first n % p parts get one more), without 64-bit division.
+__device__ __forceinline__ int split_start(int n, int p, int i) {
+  const int q = n / p, r = n - (n / p) * p;
+  return i * q + (i < r ? i : r);
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 

@@ -1,0 +1,365 @@
+// int4 g32 weight-streaming GEMV (W4A16, M <= 8) with an optional fused
+// SiLU(gate)*up epilogue.
+//
+// [M3]: Q4 weight-streaming decode kernels; [CMP]: routed experts held at 4
+// bits.  Weights are symmetric int4 with one fp16 scale per 32 consecutive K
+// values, stored as offset-binary nibbles (low nibble = even k).
+//
+// gfx950 design
+//   * each block owns a contiguous range of output rows and streams them in
+//     1 KB chunks (one 16-byte load per lane = 32 weights = exactly one scale
+//     group); the (row, chunk) units of the block are dealt to its 8 waves in
+//     order, so K is split inside the block wherever a row straddles two
+//     waves, and the split is reduced through LDS after one barrier: no
+//     global partials, atomics or store waits in the stream;
+//   * each wave keeps D chunks in flight in a ring of raw buffer loads issued
+//     without branches (out-of-range slots return zero without memory
+//     traffic), and the last D steps drain the ring without issuing;
+//   * unpacking without a packed bf16 subtract: nibble n becomes the bf16
+//     value 1 + n/16 (n shifted into the top mantissa bits under the exponent
+//     of 1.0) with one shift and one and-or per pair, v_dot2 multiplies it with
+//     bf16 x exactly, and the group's sum is corrected with the group's sum of
+//     x:  sum (n-8) x = 16 * (sum (1 + n/16) x - 1.5 * sum x);
+//   * x is staged once per block in LDS as bf16 with each run of 8 values
+//     stored as the pairs (x0,x4)(x1,x5)(x2,x6)(x3,x7) that the unpack yields,
+//     plus 1.5 times the per-group sums of x; the activation loads are issued
+//     before the weight ring so staging does not wait for weights.
+#include <stdlib.h>
+
+#include "pq_common.h"
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / pq::kWave;
+constexpr int kMaxM = 8;
+constexpr int kGroup = 32;                 // weights per fp16 scale
+constexpr int kRowsCap = 128;              // rows per block at most
+constexpr int kXGroups = 2;                // x groups per thread loaded before the weight ring
+constexpr long kMaxMK = 69632;             // M*K bound: activation + sums + partials fit LDS
+constexpr uint32_t kOne = 0x3F803F80u;     // bf16 pair (1.0, 1.0)
+constexpr uint32_t kNibMask = 0x00780078u; // mantissa bits 3..6 of both halves
+
+struct Q4Args {
+  const uint16_t* x;
+  const uint8_t* w;
+  const uint16_t* wsc;
+  uint16_t* y;
+  int M, K, N;
+  int R;        // output rows (N, or N/2 under SiLU*up)
+  int nch;      // 1 KB chunks per row
+};
+
+// The constant (1.0, 1.0) held in a VGPR the compiler cannot see through:
+// with it in a register each pair below is one shift and one v_and_or_b32
+// (the mask rides in an SGPR) instead of shift, and, or with two literals.
+__device__ __forceinline__ uint32_t one_pair_reg() {
+  uint32_t v = kOne;
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// bf16 pair (1 + n_j/16, 1 + n_{j+4}/16) from the 8 nibbles of one dword
+template <int J>
+__device__ __forceinline__ uint32_t nib_pair(uint32_t d, uint32_t one) {
+  const uint32_t t = J == 0 ? (d << 3) : (d >> (4 * J - 3));
+  return (t & kNibMask) | one;
+}
+
+struct Pairs16 { uint32_t v[16]; };        // 32 weights as 16 bf16 pairs
+
+__device__ __forceinline__ Pairs16 unpack32(uint4 w, uint32_t one) {
+  Pairs16 r;
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    r.v[4 * t + 0] = nib_pair<0>(d[t], one);
+    r.v[4 * t + 1] = nib_pair<1>(d[t], one);
+    r.v[4 * t + 2] = nib_pair<2>(d[t], one);
+    r.v[4 * t + 3] = nib_pair<3>(d[t], one);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float dot32(const Pairs16& w, const uint4 (&x)[4]) {
+  float p = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t xs[4] = {x[t].x, x[t].y, x[t].z, x[t].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pq::bf16x2, w.v[4 * t + j]),
+                                          __builtin_bit_cast(pq::bf16x2, xs[j]), p, false);
+  }
+  return p;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// 8 bf16 values x0..x7 -> the pairs (x0,x4)(x1,x5)(x2,x6)(x3,x7)
+__device__ __forceinline__ uint4 pair_order(uint4 r) {
+  uint4 o;
+  o.x = __builtin_amdgcn_perm(r.z, r.x, 0x05040100u);
+  o.y = __builtin_amdgcn_perm(r.z, r.x, 0x07060302u);
+  o.z = __builtin_amdgcn_perm(r.w, r.y, 0x05040100u);
+  o.w = __builtin_amdgcn_perm(r.w, r.y, 0x07060302u);
+  return o;
+}
+
+// LDS layout of one block: [x pairs: M*K*2 + 64 (a dummy group)]
+// [c: M*K/32 + 1 floats (one dummy)][partials: (rows + kWaves) * M * NROW floats]
+__host__ __device__ inline size_t x_region(int M, int K) { return (size_t)M * K * 2 + 64; }
+__host__ __device__ inline size_t c_region(int M, int K) { return ((size_t)M * (K / kGroup) + 4) * 4; }
+__host__ __device__ inline size_t lds_bytes(int M, int K, int rows, int nrow) {
+  return x_region(M, K) + c_region(M, K) + (size_t)(rows + kWaves) * M * nrow * 4;
+}
+
+// Stage one 32-value group of x: pairs into LDS and c = the v_dot2 chain of
+// dot32 with every weight pair (1.5, 1.5), in the same order, so that a group
+// whose nibbles are all 8 (q = 0) contributes exactly zero.
+__device__ __forceinline__ void stage_group(uint4* xs_l, float* gsum, int slot, const uint4 (&raw)[4]) {
+  uint4 xv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    xv[t] = pair_order(raw[t]);
+    xs_l[4 * slot + t] = xv[t];
+  }
+  Pairs16 th;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) th.v[i] = 0x3FC03FC0u;
+  gsum[slot] = dot32(th, xv);
+}
+
+template <int NROW, int D, int MT>
+__global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4* xs_l = reinterpret_cast<uint4*>(smem);
+  float* gsum = reinterpret_cast<float*>(smem + x_region(MT, a.K));
+  const int ng = a.K / kGroup;                        // groups per row
+  float* part = reinterpret_cast<float*>(smem + x_region(MT, a.K) + c_region(MT, a.K));   // [(row + wave)][MT][NROW]
+
+  const int tid = (int)threadIdx.x;
+  const int lane = pq::lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(pq::wave_id());
+  const int r0 = pq::split_start(a.R, (int)gridDim.x, (int)blockIdx.x);
+  const int nrows = pq::split_start(a.R, (int)gridDim.x, (int)blockIdx.x + 1) - r0;
+  const int nunits = nrows * a.nch;
+  const int u0 = pq::split_start(nunits, kWaves, wv);
+  const int nsteps = pq::split_start(nunits, kWaves, wv + 1) - u0;
+  const uint32_t rowb = (uint32_t)(a.K / 2);
+
+  // Activation loads first, one whole group per thread (kXGroups groups),
+  // and a plain barrier: every wave of the block has issued them before any
+  // weight load, so staging waits for x only, not for the weight ring.
+  const int ngr = MT * a.K / kGroup;                  // groups of x
+  const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(MT * a.K * 2));
+  uint4 xpre[kXGroups][4];
+#pragma unroll
+  for (int i = 0; i < kXGroups; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int g = tid + i * kThreads;
+      xpre[i][t] = pq::buf_load16(xr, g < ngr ? (uint32_t)g * 64u + 16u * t : pq::kOOB);
+    }
+  __builtin_amdgcn_s_barrier();
+
+  const pq::rsrc_t wr = pq::make_rsrc(a.w, (uint32_t)((size_t)a.N * rowb));
+  const pq::rsrc_t sr = pq::make_rsrc(a.wsc, (uint32_t)((size_t)a.N * ng * 2));
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+
+  uint4 wbuf[D][NROW];
+  _Float16 sbuf[D][NROW];
+  int ir = u0 / a.nch, ic = u0 - (u0 / a.nch) * a.nch, left = nsteps;
+  auto issue = [&](uint4 (&wb)[NROW], _Float16 (&sb)[NROW]) {
+    const uint32_t off = (uint32_t)(ic * pq::kChunk) + lane16;     // packed byte in the row
+    const bool ok = left > 0 && off < rowb;
+#pragma unroll
+    for (int j = 0; j < NROW; ++j) {
+      const uint32_t row = (uint32_t)(r0 + ir + j * a.R);
+      wb[j] = pq::buf_load16_nt(wr, ok ? row * rowb + off : pq::kOOB);
+      sb[j] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+          sr, (int)(ok ? (row * (uint32_t)ng + off / 16u) * 2u : pq::kOOB), 0, pq::kAuxNT));
+    }
+    --left;
+    if (++ic == a.nch) { ic = 0; ++ir; }
+  };
+#pragma unroll
+  for (int j = 0; j < D; ++j) issue(wbuf[j], sbuf[j]);
+  __builtin_amdgcn_sched_barrier(0);                  // keep the staging work below the ring issue
+
+  // Stage x.  The preloaded groups are stored unconditionally (threads
+  // without a group write the dummy slot), which keeps their loads ahead of
+  // the ring; groups beyond kXGroups per thread (M*K > 32768) follow.
+#pragma unroll
+  for (int i = 0; i < kXGroups; ++i) {
+    const int g = tid + i * kThreads;
+    stage_group(xs_l, gsum, g < ngr ? g : ngr, xpre[i]);
+  }
+  for (int g = tid + kXGroups * kThreads; g < ngr; g += kThreads) {
+    uint4 raw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) raw[t] = pq::buf_load16(xr, (uint32_t)g * 64u + 16u * t);
+    stage_group(xs_l, gsum, g, raw);
+  }
+  __syncthreads();
+
+  const uint32_t one = one_pair_reg();
+  float acc[NROW][MT];
+#pragma unroll
+  for (int j = 0; j < NROW; ++j)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
+
+  int cr = u0 / a.nch, cc = u0 - (u0 / a.nch) * a.nch;    // consume cursor (local row, chunk)
+  auto consume = [&](const uint4 (&wb)[NROW], const _Float16 (&sb)[NROW], bool last) {
+    const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
+    if (off < rowb) {
+      const int g = (int)(off / 16u);                  // this lane's group in the row
+      Pairs16 w[NROW];
+      float sc[NROW];
+#pragma unroll
+      for (int j = 0; j < NROW; ++j) {
+        w[j] = unpack32(wb[j], one);
+        sc[j] = 16.0f * (float)sb[j];
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        uint4 xv[4];
+        const uint4* xp = xs_l + (size_t)m * (a.K / 8) + 4 * g;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xv[t] = xp[t];
+        const float c = gsum[m * ng + g];
+#pragma unroll
+        for (int j = 0; j < NROW; ++j) acc[j][m] = fmaf(dot32(w[j], xv) - c, sc[j], acc[j][m]);
+      }
+    }
+    if (cc == a.nch - 1 || last) {                     // this wave's part of row cr is done
+      float v = 0.0f;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < NROW; ++j) {
+          const float s = pq::wave_sum(acc[j][m]);
+          acc[j][m] = 0.0f;
+          if (lane == m * NROW + j) v = s;
+        }
+      if (lane < MT * NROW) part[(cr + wv) * MT * NROW + lane] = v;
+    }
+    if (++cc == a.nch) { cc = 0; ++cr; }
+  };
+
+  int base = 0;
+  for (; base + D < nsteps; base += D) {               // steady state: every slot refills
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      consume(wbuf[q], sbuf[q], false);
+      issue(wbuf[q], sbuf[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < D; ++q)                          // drain
+    if (base + q < nsteps) consume(wbuf[q], sbuf[q], base + q == nsteps - 1);
+  __syncthreads();
+
+  // reduce each row over the waves that covered it, in wave order
+  for (int i = tid; i < nrows * MT; i += kThreads) {
+    const int r = i / MT, m = i - (i / MT) * MT;
+    float g = 0.0f, u = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      const int a0 = pq::split_start(nunits, kWaves, w), a1 = pq::split_start(nunits, kWaves, w + 1);
+      if (a0 < a1 && a0 < (r + 1) * a.nch && a1 > r * a.nch) {
+        g += part[((r + w) * MT + m) * NROW];
+        if (NROW == 2) u += part[((r + w) * MT + m) * NROW + 1];
+      }
+    }
+    a.y[(size_t)m * a.R + r0 + r] = pq::bf16_rne(NROW == 2 ? silu_mul(g, u) : g);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+constexpr size_t kMaxLds = 160 * 1024;
+
+int check_shape(int M, int K, int N, int epi) {
+  if (M < 1 || M > kMaxM || K < kGroup || K % kGroup != 0 || N < 1) return PQ_ERR_SHAPE;
+  if (epi != PQ_EPI_NONE && epi != PQ_EPI_SILU_MUL) return PQ_ERR_SHAPE;
+  if (epi == PQ_EPI_SILU_MUL && N % 2 != 0) return PQ_ERR_SHAPE;
+  if ((long)M * K > kMaxMK) return PQ_ERR_SHAPE;
+  if ((size_t)N * (K / 2) > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
+  return PQ_OK;
+}
+
+template <int NROW, int D, int MT>
+hipError_t launch_m(const Q4Args& a, int num_cus, hipStream_t stream) {
+  auto kern = gemv_q4_kernel<NROW, D, MT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // Blocks: PQ_BLOCKS_PER_CU per CU (default 1), at most one per row and at
+  // least enough for kRowsCap rows per block.  The grid depends on R and the
+  // device only, so the K split inside a row, and with it every output bit,
+  // is the same for every M.
+  const char* env = getenv("PQ_BLOCKS_PER_CU");
+  const int per_cu = env && atoi(env) > 0 ? atoi(env) : 1;
+  long grid = (long)num_cus * per_cu;
+  if (grid > a.R) grid = a.R;
+  const long need = ((long)a.R + kRowsCap - 1) / kRowsCap;
+  if (grid < need) grid = need;
+  const int rows = (int)((a.R + grid - 1) / grid);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds_bytes(a.M, a.K, rows, NROW), stream, a);
+  return hipGetLastError();
+}
+
+template <int NROW, int D>
+hipError_t launch(const Q4Args& a, int num_cus, hipStream_t s) {
+  switch (a.M) {
+    case 1: return launch_m<NROW, D, 1>(a, num_cus, s);
+    case 2: return launch_m<NROW, D, 2>(a, num_cus, s);
+    case 3: return launch_m<NROW, D, 3>(a, num_cus, s);
+    case 4: return launch_m<NROW, D, 4>(a, num_cus, s);
+    case 5: return launch_m<NROW, D, 5>(a, num_cus, s);
+    case 6: return launch_m<NROW, D, 6>(a, num_cus, s);
+    case 7: return launch_m<NROW, D, 7>(a, num_cus, s);
+    default: return launch_m<NROW, D, 8>(a, num_cus, s);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pq_gemv_q4_workspace(int, int, int, int) { return 0; }
+
+int pq_gemv_q4(const uint16_t* x, int M, int K, const uint8_t* w, const uint16_t* w_scale, int N, int epi,
+               uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!x || !w || !w_scale || !y) return PQ_ERR_NULL;
+  int st = check_shape(M, K, N, epi);
+  if (st != PQ_OK) return st;
+  if (!pqhost::aligned16(x) || !pqhost::aligned16(w) || !pqhost::aligned16(w_scale) || !pqhost::aligned16(y))
+    return PQ_ERR_ALIGN;
+  pqhost::DeviceInfo dev;
+  st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+
+  Q4Args a;
+  a.x = x; a.w = w; a.wsc = w_scale; a.y = y;
+  a.M = M; a.K = K; a.N = N;
+  a.R = epi == PQ_EPI_SILU_MUL ? N / 2 : N;
+  a.nch = (K / 2 + pq::kChunk - 1) / pq::kChunk;
+
+  hipError_t e = epi == PQ_EPI_SILU_MUL ? launch<2, 8>(a, dev.num_cus, (hipStream_t)stream)
+                                        : launch<1, 16>(a, dev.num_cus, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    pqhost::set_last_hip_error((int)e);
+    return PQ_ERR_HIP;
+  }
+  return PQ_OK;
+}
+
+}  // extern "C"

@@ -91,12 +91,6 @@ struct Route {
 
 __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// start of part i when n items are split over p parts as evenly as possible
-__device__ __forceinline__ int split_start(int n, int p, int i) {
-  const int q = n / p, r = n - (n / p) * p;
-  return i * q + (i < r ? i : r);
-}
-
 // total order on finite floats as unsigned keys (-0 and +0 are one key)
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t b = __float_as_uint(f == 0.0f ? 0.0f : f);
@@ -283,8 +277,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 
   // ---- C(prefetch). gate_up ring ------------------------------------------
   const int gu_units = nU * I;
-  const int g0 = ufl(split_start(gu_units, (int)T, gw));
-  const int g1 = ufl(split_start(gu_units, (int)T, gw + 1));
+  const int g0 = ufl(pq::split_start(gu_units, (int)T, gw));
+  const int g1 = ufl(pq::split_start(gu_units, (int)T, gw + 1));
   const int gsteps = (g1 - g0) * nchH;
 
   uint4 wb[DG][2];
@@ -390,8 +384,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   // ---- count the block's finished h rows per (u, 128-row group); the block
   //      completing a group re-quantises it for every token routed to u -----
   if (wv == 0) {
-    const int b0 = split_start(gu_units, (int)T, (int)blockIdx.x * kWaves);
-    const int b1 = split_start(gu_units, (int)T, (int)(blockIdx.x + 1) * kWaves);
+    const int b0 = pq::split_start(gu_units, (int)T, (int)blockIdx.x * kWaves);
+    const int b1 = pq::split_start(gu_units, (int)T, (int)(blockIdx.x + 1) * kWaves);
     uint32_t completed = 0;
     for (int G = b0 >> 7; b1 > b0 && G <= (b1 - 1) >> 7; ++G) {
       const int lo = b0 > (G << 7) ? b0 : (G << 7);
@@ -434,11 +428,11 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   // (row, union entry) units are split evenly over the waves.  Each unit's y
   // for every routed token goes to LDS; the block then combines each token's
   // slots in slot order.
-  const int r0 = split_start(H, (int)gridDim.x, (int)blockIdx.x);
-  const int r1 = split_start(H, (int)gridDim.x, (int)blockIdx.x + 1);
+  const int r0 = pq::split_start(H, (int)gridDim.x, (int)blockIdx.x);
+  const int r1 = pq::split_start(H, (int)gridDim.x, (int)blockIdx.x + 1);
   const int bunits = (r1 - r0) * nU;
-  const int v0 = ufl(split_start(bunits, kWaves, wv));
-  const int v1 = ufl(split_start(bunits, kWaves, wv + 1));
+  const int v0 = ufl(pq::split_start(bunits, kWaves, wv));
+  const int v1 = ufl(pq::split_start(bunits, kWaves, wv + 1));
   const int dsteps = (v1 - v0) * nchI;
   float* ybuf = acts + a.ybuf_off;                 // [row_local][P] fp32
   uint4 wd[DD];

@@ -1,0 +1,215 @@
+"""GPU parity of pq_gemv_q4 (int4 g32 W4A16 GEMV, K split inside a block,
+SiLU*up epilogue) against the oracle.
+
+Weights are quantised by the oracle and uploaded; the library's own int4
+quantiser is checked bit-equal to it on the same rows.  At the dense-stack
+sizes (K = 5120 / 17408, N up to 2 x 17408) the oracle evaluates a seeded
+sample of rows (always including the first and last) one by one."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from _helpers import (assert_gemv_close, assert_silu_close, bf16_to_np, need_gpu,
+                      np_bf16_bits_to_torch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pq():
+    need_gpu()
+    import quantized_moe_weight_amd as pq
+    return pq
+
+
+def _upload(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _q4_on_gpu(pq, w):
+    """Oracle int4 quantisation of w, uploaded; the GPU quantiser must agree."""
+    p, s = oracle.q4_quant(w)
+    pg, sg = pq.quantize_q4(_upload(w))
+    assert np.array_equal(pg.cpu().numpy(), p)
+    assert np.array_equal(sg.cpu().numpy().view(np.uint16), s.view(np.uint16))
+    return p, s, pg, sg
+
+
+def _x(M, K, seed):
+    x = workloads.activation_bf16(M, K, workload=workloads.Q4_STACK, seed=seed)
+    return x, np_bf16_bits_to_torch(x)
+
+
+class blocks_per_cu:
+    """Set PQ_BLOCKS_PER_CU (how many blocks share the rows) for a block of code."""
+
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        self.old = os.environ.get("PQ_BLOCKS_PER_CU")
+        os.environ["PQ_BLOCKS_PER_CU"] = str(self.n)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("PQ_BLOCKS_PER_CU", None)
+        else:
+            os.environ["PQ_BLOCKS_PER_CU"] = self.old
+
+
+@pytest.mark.parametrize("M,K,N,S", [       # S: blocks per CU (None: default)
+    (1, 32, 1, None),           # one group, one row
+    (2, 96, 37, None),          # 3 groups: a partial 1 KB chunk, ragged N
+    (3, 2080, 100, 5),          # 65 groups split 5 ways
+    (1, 5120, 640, 8),
+    (8, 8704, 64, None),        # largest K allowed at M = 8
+    (4, 4096, 300, 2),
+    (5, 2048, 129, 1),
+    (2, 17408, 40, None),       # 9 chunks per row over 8 waves
+])
+def test_gemv_q4_plain(pq, M, K, N, S):
+    seed = M * 1000 + K + N
+    x, xt = _x(M, K, seed)
+    w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=seed)
+    p, s, pg, sg = _q4_on_gpu(pq, w)
+    with blocks_per_cu(S or 1):
+        y = pq.gemv_q4(xt, pg, sg)
+    yo, So = oracle.gemv_q4(x, p, s)
+    assert_gemv_close(bf16_to_np(y), yo, So, f"M={M} K={K} N={N} blocks/CU={S}")
+
+
+@pytest.mark.parametrize("M,K,N,S", [
+    (2, 1024, 70, None),
+    (5, 768, 64, 2),
+    (1, 4096, 512, 4),
+])
+def test_gemv_q4_silu(pq, M, K, N, S):
+    seed = M + K + N
+    x, xt = _x(M, K, seed)
+    w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=seed)
+    p, s, pg, sg = _q4_on_gpu(pq, w)
+    with blocks_per_cu(S or 1):
+        y = pq.gemv_q4(xt, pg, sg, epi=pq.EPI_SILU_MUL)
+    yo, So = oracle.gemv_q4(x, p, s)
+    I = N // 2
+    h = oracle.silu_mul(yo, I)
+    assert_silu_close(bf16_to_np(y), h, yo[:, :I], yo[:, I:], So[:, :I], So[:, I:], f"M={M} S={S}")
+
+
+def _sample(n_rows, count, seed):
+    rng = np.random.default_rng(seed)
+    r = rng.choice(n_rows, size=min(count, n_rows), replace=False)
+    return np.unique(np.concatenate([r, [0, n_rows - 1]]))
+
+
+@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("layer", [0, 1, 2])
+def test_gemv_q4_dense_stack_layers(pq, M, layer):
+    """The three layer shapes of the 4-bit dense decode stack at full size, in
+    the launch configuration the benchmark times; sampled rows against the oracle."""
+    import torch
+    K, N, silu = workloads.Q4_SHAPES[layer]
+    seed = 7 + layer
+    x, xt = _x(M, K, seed)
+    wt = workloads.master_weights_torch(N, K, workload=workloads.Q4_STACK, tensor=workloads.T_W,
+                                        expert=layer, seed=seed, device="cuda")
+    pg, sg = pq.quantize_q4(wt)
+    y = bf16_to_np(pq.gemv_q4(xt, pg, sg, epi=pq.EPI_SILU_MUL if silu else pq.EPI_NONE))
+    R = N // 2 if silu else N
+    rows = _sample(R, 192, seed)
+    want_rows = np.concatenate([rows, rows + R]) if silu else rows
+    w_rows = wt[torch.from_numpy(want_rows).cuda()].cpu().numpy()
+    p, s = oracle.q4_quant(w_rows)
+    assert np.array_equal(pg[torch.from_numpy(want_rows).cuda()].cpu().numpy(), p)
+    assert np.array_equal(sg[torch.from_numpy(want_rows).cuda()].cpu().numpy().view(np.uint16), s.view(np.uint16))
+    yo, So = oracle.gemv_q4(x, p, s)
+    if silu:
+        n = len(rows)
+        h = oracle.silu_mul(yo, n)
+        assert_silu_close(y[:, rows], h, yo[:, :n], yo[:, n:], So[:, :n], So[:, n:], f"layer {layer} M={M}")
+    else:
+        assert_gemv_close(y[:, rows], yo, So, f"layer {layer} M={M}")
+
+
+def test_gemv_q4_decodes_every_nibble(pq):
+    """Row n holds nibble n & 15 at one position, x is 1 there and the fp16 scale
+    of that group is chosen per row (normal, subnormal, largest finite, zero):
+    y[n] = (nibble - 8) * scale exactly."""
+    import torch
+    K, k0 = 96, 45                     # k0 in group 1, odd position (high nibble)
+    scales = np.array([1.0, 0.5, 2.0 ** -24, 2.0 ** -14, 65504.0, 0.0, 3.0, 1.0 / 7], np.float16)
+    n_rows = 16 * len(scales)
+    q = np.zeros((n_rows, K), np.int64)
+    q[:, k0] = np.tile(np.arange(16) - 8, len(scales))
+    packed = oracle.q4_pack(q)
+    sc = np.ones((n_rows, K // 32), np.float16)
+    sc[:, 1] = np.repeat(scales, 16)
+    x = np.zeros((1, K), np.uint16)
+    x[0, k0] = workloads.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    y = bf16_to_np(pq.gemv_q4(np_bf16_bits_to_torch(x), _upload(packed), _upload(sc)))[0]
+    want = q[:, k0] * sc[:, 1].astype(np.float64)
+    want_bf16 = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(want.astype(np.float32))).astype(np.float64)
+    assert np.array_equal(y, want_bf16)
+
+
+def test_gemv_q4_rows_bitwise_independent_of_M(pq):
+    import torch
+    M, K, N = 6, 2048, 512
+    x, xt = _x(M, K, 17)
+    w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=17)
+    p, s, pg, sg = _q4_on_gpu(pq, w)
+    y = pq.gemv_q4(xt, pg, sg, epi=pq.EPI_SILU_MUL)
+    for m in range(M):
+        ym = pq.gemv_q4(xt[m:m + 1].contiguous(), pg, sg, epi=pq.EPI_SILU_MUL)
+        assert torch.equal(ym[0].view(torch.int16), y[m].view(torch.int16))
+
+
+def test_gemv_q4_split_points_change_only_rounding(pq):
+    """The grid decides where a row's K range is cut between waves; any cut
+    agrees with the oracle within the GEMV tolerance, and a repeated call with
+    the same grid is bitwise identical."""
+    import torch
+    M, K, N = 2, 5120, 700
+    x, xt = _x(M, K, 23)
+    w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=23)
+    p, s, pg, sg = _q4_on_gpu(pq, w)
+    yo, So = oracle.gemv_q4(x, p, s)
+    for n in (1, 2, 3, 8):
+        with blocks_per_cu(n):
+            ys = pq.gemv_q4(xt, pg, sg)
+            ys2 = pq.gemv_q4(xt, pg, sg)
+        assert torch.equal(ys.view(torch.int16), ys2.view(torch.int16))
+        assert_gemv_close(bf16_to_np(ys), yo, So, f"blocks/CU={n}")
+
+
+def test_gemv_q4_zero_inputs(pq):
+    import torch
+    M, K, N = 3, 1024, 80
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=3)
+    p, s = oracle.q4_quant(w)
+    y = pq.gemv_q4(x, _upload(p), _upload(s))
+    assert torch.count_nonzero(y.view(torch.int16)) == 0
+    xt = np_bf16_bits_to_torch(workloads.activation_bf16(M, K, workload=workloads.Q4_STACK, seed=3))
+    y = pq.gemv_q4(xt, _upload(np.full_like(p, 0x88)), _upload(s))     # every code is 0
+    assert torch.count_nonzero(y.view(torch.int16)) == 0
+
+
+@pytest.mark.parametrize("M,K,N,epi", [
+    (9, 64, 4, 0),          # M above 8
+    (1, 48, 4, 0),          # K not a multiple of 32
+    (1, 64, 5, 1),          # odd N under SiLU
+    (8, 8736, 4, 0),        # activation does not fit LDS
+])
+def test_gemv_q4_bad_shapes(pq, M, K, N, epi):
+    import torch
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((N, K // 2), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((N, K // 32), dtype=torch.float16, device="cuda")
+    with pytest.raises(pq.PqError) as e:
+        pq.gemv_q4(x, w, s, epi=epi)
+    assert e.value.status == -2

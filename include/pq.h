@@ -123,21 +123,27 @@ int pq_gemv_fp8(const uint16_t* x, int M, int K,
 /* int4 g32 weight-streaming GEMV (W4A16): [M3] Q4 decode.                    */
 /* ------------------------------------------------------------------------- */
 
-/* Workspace bytes pq_gemv_q4 needs: always 0 (the split of K inside a row is
- * reduced on chip); kept so both GEMV calls have the same shape of API. */
+/* Workspace bytes pq_gemv_q4 needs for this shape on the current device
+ * (arrival counters and the partial sums of row tiles cut between waves);
+ * 0 when none is needed, and 0 for invalid shapes (pq_gemv_q4 then reports
+ * the error). */
 size_t pq_gemv_q4_workspace(int M, int K, int N, int epi);
 
 /* y = epi(bf16( sum_g s[n,g] sum_{k in g} x[m,k] q[n,k] )), fp32 accumulation.
  *   x : bf16 [M,K]    w : nibbles [N,K/2] (layout of pq_quantize_q4)
  *   w_scale : fp16 [N,K/32]    y : bf16 [M,N] or [M,N/2] under PQ_EPI_SILU_MUL
- *   ws, ws_bytes : ignored (may be NULL / 0).
+ *   ws : device workspace of ws_bytes >= pq_gemv_q4_workspace(...) (may be
+ *        NULL when that is 0), zeroed once by pq_workspace_init; calls that
+ *        share a workspace must be ordered (one stream).
  * Constraints: 1 <= M <= 8, K % 32 == 0, K >= 32, N >= 1, N even under
- * PQ_EPI_SILU_MUL, N*K/2 < 2^31, and M*K <= 69632 (the bf16 activation, its
- * group sums and the per-block partial sums live in one CU's LDS; e.g.
- * K = 17408 at M <= 4, K = 8704 at M = 8); PQ_ERR_SHAPE otherwise.
- * Each output row is computed by one block; its bits depend on the shape and
- * the device's CU count only (not on M or on the other rows); the variable
- * PQ_BLOCKS_PER_CU (default 1) sets the number of blocks per CU. */
+ * PQ_EPI_SILU_MUL, N*K/2 < 2^31, and M*K <= 69632 (the bf16 activation and
+ * its staging live in one CU's LDS; e.g. K = 17408 at M <= 4, K = 8704 at
+ * M = 8); PQ_ERR_SHAPE otherwise.
+ * M >= 5 with K % 256 == 0 runs on the matrix cores (bf16 MFMA on unpacked
+ * nibbles), everything else on the vector units; PQ_Q4_PATH=valu or =mfma
+ * forces one kernel (mfma only where K % 256 == 0).  For a given kernel the
+ * output bits depend on the shape and the device's CU count only (not on M
+ * or on other rows); PQ_BLOCKS_PER_CU (default 1) sets the blocks per CU. */
 int pq_gemv_q4(const uint16_t* x, int M, int K,
                const uint8_t* w, const uint16_t* w_scale, int N,
                int epi, uint16_t* y, void* ws, size_t ws_bytes, void* stream);

@@ -25,6 +25,7 @@
 //     plus 1.5 times the per-group sums of x; the activation loads are issued
 //     before the weight ring so staging does not wait for weights.
 #include <stdlib.h>
+#include <string.h>
 
 #include "pq_common.h"
 
@@ -62,8 +63,8 @@ __device__ __forceinline__ uint32_t one_pair_reg() {
 // bf16 pair (1 + n_j/16, 1 + n_{j+4}/16) from the 8 nibbles of one dword
 template <int J>
 __device__ __forceinline__ uint32_t nib_pair(uint32_t d, uint32_t one) {
-  const uint32_t t = J == 0 ? (d << 3) : (d >> (4 * J - 3));
-  return (t & kNibMask) | one;
+  if constexpr (J == 0) return ((d << 3) & kNibMask) | one;
+  else return ((d >> (4 * J - 3)) & kNibMask) | one;
 }
 
 struct Pairs16 { uint32_t v[16]; };        // 32 weights as 16 bf16 pairs
@@ -277,6 +278,284 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// MFMA path (K % 256 == 0).
+//
+// The dot products run on the matrix cores as D = A * B with
+// v_mfma_f32_16x16x32_bf16, arranged "transposed":
+//   * B (32 k x 16 columns) holds the weights of 16 rows: lane l feeds row
+//     l % 16 with the 8 k of one nibble dword of the group picked by its lane
+//     group q = l / 16, unpacked to (1 + n/16) pairs;
+//   * A (16 rows x 32 k) holds x: A row i = 4 m' + q' is token m' and group
+//     slot q'; its k entries are x where q' equals the lane group q that
+//     carries them and zero elsewhere.
+// Each output lane l then holds, for token l / 16 and weight row l % 16, the
+// four per-group partial sums sum_k (1 + n/16) x of one 4-group window, so
+// the fp16 group scales (the lane's own row) apply per lane with no cross-lane
+// reduction.  The offset 1.5 * sum x is a second MFMA chain on the same A with
+// every weight equal to 1.5: identical operand positions, so a group whose
+// codes are all 8 gives exactly zero.
+//
+// Work is split stream-K style: the (16-row block, 256-k chunk) units of the
+// whole matrix are dealt to all waves of the grid in order.  A row block
+// covered by one wave is finished by it; one cut between waves is combined at
+// the end of their streams (partials through the workspace, an arrival counter
+// per block, the last arriver adds the parts in wave order), so the load ring
+// never waits for a store.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRB = 16;          // weight rows per tile
+constexpr int kGroupsPerStep = 8;  // 256 k = 128 bytes of each row per step
+constexpr int kKStep = kGroupsPerStep * kGroup;
+constexpr int kMXPre = 4;        // 16-byte x pieces per thread loaded before the ring
+
+struct Q4MArgs {
+  const uint16_t* x;
+  const uint8_t* w;
+  const uint16_t* wsc;
+  uint16_t* y;
+  float* part;       // [waves][2][SETS * NROW][64]
+  uint32_t* cnt;     // [nrb]
+  int M, K, N, R;
+  int nrb, nkc, U;   // row blocks, k steps per row block, units = nrb * nkc
+};
+
+__device__ __forceinline__ floatx4 mfma16(uint4 a, uint4 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// the 4 bf16 pairs of one nibble dword, in the order of the x pieces
+__device__ __forceinline__ uint4 unpack8(uint32_t d, uint32_t one) {
+  uint4 r;
+  r.x = nib_pair<0>(d, one);
+  r.y = nib_pair<1>(d, one);
+  r.z = nib_pair<2>(d, one);
+  r.w = nib_pair<3>(d, one);
+  return r;
+}
+
+// wave whose unit range [split_start(U, T, w), split_start(U, T, w + 1)) holds u
+__device__ __forceinline__ int wave_of(int u, int U, int T) {
+  const int q = U / T, r = U - (U / T) * T;
+  return u < r * (q + 1) ? u / (q + 1) : r + (u - r * (q + 1)) / q;
+}
+
+template <int NROW, int D, int MT>
+__global__ __launch_bounds__(kThreads) void gemv_q4_mfma_kernel(Q4MArgs a) {
+  constexpr int SETS = (MT + 3) / 4;          // A tiles of 4 tokens
+  constexpr int NS = SETS * NROW;             // partial values per lane per segment
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4* xs_l = reinterpret_cast<uint4*>(smem);   // [MT*K/8] pieces, a dummy piece, a zero piece
+  const int nx = MT * a.K / 8;
+  const int zero_piece = nx + 1;
+
+  const int tid = (int)threadIdx.x;
+  const int lane = pq::lane_id();
+  const int T = (int)gridDim.x * kWaves;
+  const int gw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + pq::wave_id());
+  const int u0 = pq::split_start(a.U, T, gw);
+  const int nsteps = pq::split_start(a.U, T, gw + 1) - u0;
+
+  // activation loads first, then a plain barrier, then the weight ring
+  const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(MT * a.K * 2));
+  uint4 xpre[kMXPre];
+#pragma unroll
+  for (int i = 0; i < kMXPre; ++i) {
+    const int p = tid + i * kThreads;
+    xpre[i] = pq::buf_load16(xr, p < nx ? (uint32_t)p * 16u : pq::kOOB);
+  }
+  __builtin_amdgcn_s_barrier();
+
+  const uint32_t rowb = (uint32_t)(a.K / 2);
+  const int ng = a.K / kGroup;
+  const pq::rsrc_t wr = pq::make_rsrc(a.w, (uint32_t)((size_t)a.N * rowb));
+  const pq::rsrc_t sr = pq::make_rsrc(a.wsc, (uint32_t)((size_t)a.N * ng * 2));
+  const int rl = lane & 15, lq = lane >> 4;
+
+  uint4 wbuf[D][NROW][2];
+  uint4 sbuf[D][NROW];
+  int irb = u0 / a.nkc, ikc = u0 - (u0 / a.nkc) * a.nkc, left = nsteps;
+  auto issue = [&](uint4 (&wb)[NROW][2], uint4 (&sb)[NROW]) {
+    const int row = irb * kRB + rl;
+    const bool ok = left > 0 && row < a.R;
+#pragma unroll
+    for (int j = 0; j < NROW; ++j) {
+      const uint32_t grow = (uint32_t)(row + j * a.R);
+      const uint32_t off = grow * rowb + (uint32_t)ikc * 128u + 16u * (uint32_t)lq;
+      wb[j][0] = pq::buf_load16_nt(wr, ok ? off : pq::kOOB);
+      wb[j][1] = pq::buf_load16_nt(wr, ok ? off + 64u : pq::kOOB);
+      sb[j] = pq::buf_load16_nt(sr, ok ? (grow * (uint32_t)ng + (uint32_t)ikc * kGroupsPerStep) * 2u : pq::kOOB);
+    }
+    --left;
+    if (++ikc == a.nkc) { ikc = 0; ++irb; }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(wbuf[d], sbuf[d]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // stage x in the paired order (threads without a piece write the dummy)
+#pragma unroll
+  for (int i = 0; i < kMXPre; ++i) {
+    const int p = tid + i * kThreads;
+    xs_l[p < nx ? p : nx] = pair_order(xpre[i]);
+  }
+  for (int p = tid + kMXPre * kThreads; p < nx; p += kThreads) xs_l[p] = pair_order(pq::buf_load16(xr, (uint32_t)p * 16u));
+  if (tid == 0) xs_l[zero_piece] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  // this lane's A row: token 4 s + (lane % 16) / 4, group slot lane % 4; it
+  // carries x only where the slot equals its lane group
+  int abase[SETS];
+#pragma unroll
+  for (int s = 0; s < SETS; ++s) {
+    const int m = 4 * s + (rl >> 2);
+    abase[s] = ((rl & 3) == lq && m < MT) ? m * (a.K / 8) + 4 * lq : -1;
+  }
+  const uint32_t one = one_pair_reg();
+  const uint32_t th = one_pair_reg() + 0x00400040u;   // (1.5, 1.5)
+  const uint4 b15 = make_uint4(th, th, th, th);
+
+  float acc[SETS][NROW], st0[SETS][NROW], st1[SETS][NROW];
+#pragma unroll
+  for (int s = 0; s < SETS; ++s)
+#pragma unroll
+    for (int j = 0; j < NROW; ++j) acc[s][j] = st0[s][j] = st1[s][j] = 0.0f;
+  bool has0 = false, has1 = false;
+  const int rb_first = u0 / a.nkc;
+  const int rb_last = nsteps > 0 ? (u0 + nsteps - 1) / a.nkc : rb_first;
+
+  auto output = [&](int rb, const float (&v)[SETS][NROW]) {
+    const int row = rb * kRB + rl;
+#pragma unroll
+    for (int s = 0; s < SETS; ++s) {
+      const int m = 4 * s + lq;
+      if (m < MT && row < a.R) {
+        const float g = 16.0f * v[s][0];
+        a.y[(size_t)m * a.R + row] = pq::bf16_rne(NROW == 2 ? silu_mul(g, 16.0f * v[s][NROW - 1]) : g);
+      }
+    }
+  };
+  auto ncover = [&](int rb) {
+    return wave_of((rb + 1) * a.nkc - 1, a.U, T) - wave_of(rb * a.nkc, a.U, T) + 1;
+  };
+
+  int crb = rb_first, ckc = u0 - rb_first * a.nkc;
+  auto consume = [&](const uint4 (&wb)[NROW][2], const uint4 (&sb)[NROW], bool last) {
+    const int g0 = ckc * kGroupsPerStep;
+    float sc[NROW][8];
+#pragma unroll
+    for (int j = 0; j < NROW; ++j) {
+      const uint32_t h[4] = {sb[j].x, sb[j].y, sb[j].z, sb[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[j][2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(h[e] & 0xffffu));
+        sc[j][2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(h[e] >> 16));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < SETS; ++s) {
+#pragma unroll
+      for (int win = 0; win < 2; ++win) {
+        uint4 af[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) af[t] = xs_l[abase[s] >= 0 ? abase[s] + 4 * (g0 + 4 * win) + t : zero_piece];
+        floatx4 dc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dc = mfma16(af[t], b15, dc);
+#pragma unroll
+        for (int j = 0; j < NROW; ++j) {
+          const uint32_t dw[4] = {wb[j][win].x, wb[j][win].y, wb[j][win].z, wb[j][win].w};
+          floatx4 dd = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) dd = mfma16(af[t], unpack8(dw[t], one), dd);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[s][j] = fmaf(dd[e] - dc[e], sc[j][4 * win + e], acc[s][j]);
+        }
+      }
+    }
+    if (ckc == a.nkc - 1 || last) {            // end of this wave's part of row block crb
+      if (ncover(crb) == 1) {
+        output(crb, acc);
+      } else if (crb == rb_first) {
+#pragma unroll
+        for (int s = 0; s < SETS; ++s)
+#pragma unroll
+          for (int j = 0; j < NROW; ++j) st0[s][j] = acc[s][j];
+        has0 = true;
+      } else {
+#pragma unroll
+        for (int s = 0; s < SETS; ++s)
+#pragma unroll
+          for (int j = 0; j < NROW; ++j) st1[s][j] = acc[s][j];
+        has1 = true;
+      }
+#pragma unroll
+      for (int s = 0; s < SETS; ++s)
+#pragma unroll
+        for (int j = 0; j < NROW; ++j) acc[s][j] = 0.0f;
+    }
+    if (++ckc == a.nkc) { ckc = 0; ++crb; }
+  };
+
+  int base = 0;
+  for (; base + D < nsteps; base += D) {
+#pragma unroll
+    for (int q = 0; q < D; ++q) {
+      consume(wbuf[q], sbuf[q], false);
+      issue(wbuf[q], sbuf[q]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < D; ++q)
+    if (base + q < nsteps) consume(wbuf[q], sbuf[q], base + q == nsteps - 1);
+
+  // row blocks cut between waves: publish this wave's parts, then the last
+  // covering wave to arrive adds all parts in wave order
+  if (has0 || has1) {
+    uint32_t* p32 = reinterpret_cast<uint32_t*>(a.part);
+#pragma unroll
+    for (int s = 0; s < SETS; ++s)
+#pragma unroll
+      for (int j = 0; j < NROW; ++j) {
+        const int k = s * NROW + j;
+        if (has0) pq::st_agent_u32(p32 + ((size_t)(gw * 2 + 0) * NS + k) * 64 + lane, __float_as_uint(st0[s][j]));
+        if (has1) pq::st_agent_u32(p32 + ((size_t)(gw * 2 + 1) * NS + k) * 64 + lane, __float_as_uint(st1[s][j]));
+      }
+    pq::wait_vm();
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      if (which == 0 ? !has0 : !has1) continue;
+      const int rb = which == 0 ? rb_first : rb_last;
+      uint32_t old = 0;
+      if (lane == 0) old = pq::atomic_add_relaxed(&a.cnt[rb], 1u);
+      old = __shfl(old, 0, pq::kWave);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      const int w0 = wave_of(rb * a.nkc, a.U, T);
+      const int nc = ncover(rb);
+      if (old == (uint32_t)(nc - 1)) {
+        float v[SETS][NROW];
+#pragma unroll
+        for (int s = 0; s < SETS; ++s)
+#pragma unroll
+          for (int j = 0; j < NROW; ++j) v[s][j] = 0.0f;
+        for (int wc = w0; wc < w0 + nc; ++wc) {
+          const int slot = pq::split_start(a.U, T, wc) / a.nkc == rb ? 0 : 1;
+#pragma unroll
+          for (int s = 0; s < SETS; ++s)
+#pragma unroll
+            for (int j = 0; j < NROW; ++j)
+              v[s][j] += __uint_as_float(pq::ld_agent_u32(p32 + ((size_t)(wc * 2 + slot) * NS + s * NROW + j) * 64 + lane));
+        }
+        output(rb, v);
+        if (lane == 0) pq::atomic_store_relaxed(&a.cnt[rb], 0u);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 constexpr size_t kMaxLds = 160 * 1024;
@@ -328,33 +607,113 @@ hipError_t launch(const Q4Args& a, int num_cus, hipStream_t s) {
   }
 }
 
+// ---- MFMA path -----------------------------------------------------------
+int blocks_per_cu() {
+  const char* env = getenv("PQ_BLOCKS_PER_CU");
+  return env && atoi(env) > 0 ? atoi(env) : 1;
+}
+
+// The matrix-core kernel needs K % 256 == 0 and one counter per 16-row tile.
+// By default it serves M >= 5, where the vector kernel's dot products
+// dominate; below that the vector kernel is faster on MI355X (measured on the
+// 5120 / 2 x 17408 / 17408 dense-stack shapes).  PQ_Q4_PATH=valu or =mfma
+// forces one of them (mfma only where its conditions hold).
+bool use_mfma(int M, int K, int R) {
+  if (K % kKStep != 0 || (size_t)((R + kRB - 1) / kRB) > pq::kWsMaxCounters) return false;
+  const char* env = getenv("PQ_Q4_PATH");
+  if (env && strcmp(env, "valu") == 0) return false;
+  if (env && strcmp(env, "mfma") == 0) return true;
+  return M >= 5;
+}
+
+// grid (blocks) and workspace bytes of the MFMA path
+void mfma_plan(int M, int R, int nrow, int num_cus, int* grid, size_t* ws) {
+  *grid = num_cus * blocks_per_cu();
+  const int sets = (M + 3) / 4;
+  *ws = pq::kWsDataOff + (size_t)(*grid) * kWaves * 2 * sets * nrow * 64 * sizeof(float);
+}
+
+template <int NROW, int D, int MT>
+hipError_t launch_mfma_m(const Q4MArgs& a, int grid, hipStream_t stream) {
+  auto kern = gemv_q4_mfma_kernel<NROW, D, MT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t lds = ((size_t)a.M * a.K / 8 + 2) * 16;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int NROW, int D>
+hipError_t launch_mfma(const Q4MArgs& a, int grid, hipStream_t s) {
+  switch (a.M) {
+    case 1: return launch_mfma_m<NROW, D, 1>(a, grid, s);
+    case 2: return launch_mfma_m<NROW, D, 2>(a, grid, s);
+    case 3: return launch_mfma_m<NROW, D, 3>(a, grid, s);
+    case 4: return launch_mfma_m<NROW, D, 4>(a, grid, s);
+    case 5: return launch_mfma_m<NROW, D, 5>(a, grid, s);
+    case 6: return launch_mfma_m<NROW, D, 6>(a, grid, s);
+    case 7: return launch_mfma_m<NROW, D, 7>(a, grid, s);
+    default: return launch_mfma_m<NROW, D, 8>(a, grid, s);
+  }
+}
+
 }  // namespace
 
 extern "C" {
 
-size_t pq_gemv_q4_workspace(int, int, int, int) { return 0; }
+size_t pq_gemv_q4_workspace(int M, int K, int N, int epi) {
+  if (check_shape(M, K, N, epi) != PQ_OK) return 0;
+  const int R = epi == PQ_EPI_SILU_MUL ? N / 2 : N;
+  if (!use_mfma(M, K, R)) return 0;
+  pqhost::DeviceInfo dev;
+  if (pqhost::current_device_info(&dev) != PQ_OK) return 0;
+  int grid;
+  size_t ws;
+  mfma_plan(M, R, epi == PQ_EPI_SILU_MUL ? 2 : 1, dev.num_cus, &grid, &ws);
+  return ws;
+}
 
 int pq_gemv_q4(const uint16_t* x, int M, int K, const uint8_t* w, const uint16_t* w_scale, int N, int epi,
                uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!x || !w || !w_scale || !y) return PQ_ERR_NULL;
   int st = check_shape(M, K, N, epi);
   if (st != PQ_OK) return st;
-  if (!pqhost::aligned16(x) || !pqhost::aligned16(w) || !pqhost::aligned16(w_scale) || !pqhost::aligned16(y))
+  if (!pqhost::aligned16(x) || !pqhost::aligned16(w) || !pqhost::aligned16(w_scale) || !pqhost::aligned16(y) ||
+      (ws && !pqhost::aligned16(ws)))
     return PQ_ERR_ALIGN;
   pqhost::DeviceInfo dev;
   st = pqhost::current_device_info(&dev);
   if (st != PQ_OK) return st;
-
-  Q4Args a;
-  a.x = x; a.w = w; a.wsc = w_scale; a.y = y;
-  a.M = M; a.K = K; a.N = N;
-  a.R = epi == PQ_EPI_SILU_MUL ? N / 2 : N;
-  a.nch = (K / 2 + pq::kChunk - 1) / pq::kChunk;
-
-  hipError_t e = epi == PQ_EPI_SILU_MUL ? launch<2, 8>(a, dev.num_cus, (hipStream_t)stream)
-                                        : launch<1, 16>(a, dev.num_cus, (hipStream_t)stream);
+  const int R = epi == PQ_EPI_SILU_MUL ? N / 2 : N;
+  hipError_t e;
+  if (use_mfma(M, K, R)) {
+    int grid;
+    size_t need;
+    mfma_plan(M, R, epi == PQ_EPI_SILU_MUL ? 2 : 1, dev.num_cus, &grid, &need);
+    if (ws == nullptr || ws_bytes < need) return PQ_ERR_WORKSPACE;
+    Q4MArgs a;
+    a.x = x; a.w = w; a.wsc = w_scale; a.y = y;
+    a.cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + pq::kWsCounterOff);
+    a.part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + pq::kWsDataOff);
+    a.M = M; a.K = K; a.N = N; a.R = R;
+    a.nrb = (R + kRB - 1) / kRB;
+    a.nkc = K / kKStep;
+    a.U = a.nrb * a.nkc;
+    e = epi == PQ_EPI_SILU_MUL ? launch_mfma<2, 4>(a, grid, (hipStream_t)stream)
+                               : launch_mfma<1, 8>(a, grid, (hipStream_t)stream);
+  } else {
+    Q4Args a;
+    a.x = x; a.w = w; a.wsc = w_scale; a.y = y;
+    a.M = M; a.K = K; a.N = N;
+    a.R = R;
+    a.nch = (K / 2 + pq::kChunk - 1) / pq::kChunk;
+    e = epi == PQ_EPI_SILU_MUL ? launch<2, 8>(a, dev.num_cus, (hipStream_t)stream)
+                               : launch<1, 16>(a, dev.num_cus, (hipStream_t)stream);
+  }
   if (e != hipSuccess) {
     pqhost::set_last_hip_error((int)e);
     return PQ_ERR_HIP;

@@ -1,5 +1,8 @@
-"""GPU parity of pq_gemv_q4 (int4 g32 W4A16 GEMV, K split inside a block,
-SiLU*up epilogue) against the oracle.
+"""GPU parity of pq_gemv_q4 (int4 g32 W4A16 GEMV with SiLU*up epilogue) against
+the oracle.  Two kernels: the MFMA one (K % 256 == 0, stream-K split with a
+cross-wave combine; the default for M >= 5) and the VALU one (K split inside a
+block).  PQ_Q4_PATH=valu / =mfma forces either, so both are checked on the
+same shapes.
 
 Weights are quantised by the oracle and uploaded; the library's own int4
 quantiser is checked bit-equal to it on the same rows.  At the dense-stack
@@ -23,6 +26,26 @@ def pq():
     need_gpu()
     import quantized_moe_weight_amd as pq
     return pq
+
+
+class env:
+    """Set one environment variable of the library for a block of code."""
+
+    def __init__(self, name, value):
+        self.name, self.value = name, value
+
+    def __enter__(self):
+        self.old = os.environ.get(self.name)
+        if self.value is None:
+            os.environ.pop(self.name, None)
+        else:
+            os.environ[self.name] = str(self.value)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop(self.name, None)
+        else:
+            os.environ[self.name] = self.old
 
 
 def _upload(a):
@@ -70,29 +93,35 @@ class blocks_per_cu:
     (4, 4096, 300, 2),
     (5, 2048, 129, 1),
     (2, 17408, 40, None),       # 9 chunks per row over 8 waves
+    (7, 512, 3000, 2),          # many row tiles, 2 k steps each
+    (1, 256, 17, None),         # one k step, ragged tile
 ])
-def test_gemv_q4_plain(pq, M, K, N, S):
+@pytest.mark.parametrize("path", [None, "valu", "mfma"])
+def test_gemv_q4_plain(pq, M, K, N, S, path):
     seed = M * 1000 + K + N
     x, xt = _x(M, K, seed)
     w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=seed)
     p, s, pg, sg = _q4_on_gpu(pq, w)
-    with blocks_per_cu(S or 1):
+    with blocks_per_cu(S or 1), env("PQ_Q4_PATH", path):
         y = pq.gemv_q4(xt, pg, sg)
     yo, So = oracle.gemv_q4(x, p, s)
-    assert_gemv_close(bf16_to_np(y), yo, So, f"M={M} K={K} N={N} blocks/CU={S}")
+    assert_gemv_close(bf16_to_np(y), yo, So, f"M={M} K={K} N={N} blocks/CU={S} path={path}")
 
 
 @pytest.mark.parametrize("M,K,N,S", [
     (2, 1024, 70, None),
     (5, 768, 64, 2),
     (1, 4096, 512, 4),
+    (8, 2048, 2 * 37, None),    # 37 rows: a ragged 16-row tile, two token sets
+    (3, 8192, 2 * 300, 3),
 ])
-def test_gemv_q4_silu(pq, M, K, N, S):
+@pytest.mark.parametrize("path", [None, "valu", "mfma"])
+def test_gemv_q4_silu(pq, M, K, N, S, path):
     seed = M + K + N
     x, xt = _x(M, K, seed)
     w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=seed)
     p, s, pg, sg = _q4_on_gpu(pq, w)
-    with blocks_per_cu(S or 1):
+    with blocks_per_cu(S or 1), env("PQ_Q4_PATH", path):
         y = pq.gemv_q4(xt, pg, sg, epi=pq.EPI_SILU_MUL)
     yo, So = oracle.gemv_q4(x, p, s)
     I = N // 2
@@ -135,12 +164,13 @@ def test_gemv_q4_dense_stack_layers(pq, M, layer):
         assert_gemv_close(y[:, rows], yo, So, f"layer {layer} M={M}")
 
 
-def test_gemv_q4_decodes_every_nibble(pq):
+@pytest.mark.parametrize("K,path", [(96, None), (512, "valu"), (512, "mfma")])
+def test_gemv_q4_decodes_every_nibble(pq, K, path):
     """Row n holds nibble n & 15 at one position, x is 1 there and the fp16 scale
     of that group is chosen per row (normal, subnormal, largest finite, zero):
     y[n] = (nibble - 8) * scale exactly."""
     import torch
-    K, k0 = 96, 45                     # k0 in group 1, odd position (high nibble)
+    k0 = 45                            # k0 in group 1, odd position (high nibble)
     scales = np.array([1.0, 0.5, 2.0 ** -24, 2.0 ** -14, 65504.0, 0.0, 3.0, 1.0 / 7], np.float16)
     n_rows = 16 * len(scales)
     q = np.zeros((n_rows, K), np.int64)
@@ -150,25 +180,29 @@ def test_gemv_q4_decodes_every_nibble(pq):
     sc[:, 1] = np.repeat(scales, 16)
     x = np.zeros((1, K), np.uint16)
     x[0, k0] = workloads.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
-    y = bf16_to_np(pq.gemv_q4(np_bf16_bits_to_torch(x), _upload(packed), _upload(sc)))[0]
+    with env("PQ_Q4_PATH", path):
+        y = bf16_to_np(pq.gemv_q4(np_bf16_bits_to_torch(x), _upload(packed), _upload(sc)))[0]
     want = q[:, k0] * sc[:, 1].astype(np.float64)
     want_bf16 = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(want.astype(np.float32))).astype(np.float64)
     assert np.array_equal(y, want_bf16)
 
 
-def test_gemv_q4_rows_bitwise_independent_of_M(pq):
+@pytest.mark.parametrize("K,path", [(2080, None), (2048, "valu"), (2048, "mfma")])
+def test_gemv_q4_rows_bitwise_independent_of_M(pq, K, path):
     import torch
-    M, K, N = 6, 2048, 512
+    M, N = 6, 512
     x, xt = _x(M, K, 17)
     w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=17)
     p, s, pg, sg = _q4_on_gpu(pq, w)
-    y = pq.gemv_q4(xt, pg, sg, epi=pq.EPI_SILU_MUL)
-    for m in range(M):
-        ym = pq.gemv_q4(xt[m:m + 1].contiguous(), pg, sg, epi=pq.EPI_SILU_MUL)
-        assert torch.equal(ym[0].view(torch.int16), y[m].view(torch.int16))
+    with env("PQ_Q4_PATH", path):
+        y = pq.gemv_q4(xt, pg, sg, epi=pq.EPI_SILU_MUL)
+        for m in range(M):
+            ym = pq.gemv_q4(xt[m:m + 1].contiguous(), pg, sg, epi=pq.EPI_SILU_MUL)
+            assert torch.equal(ym[0].view(torch.int16), y[m].view(torch.int16))
 
 
-def test_gemv_q4_split_points_change_only_rounding(pq):
+@pytest.mark.parametrize("path", ["valu", "mfma"])
+def test_gemv_q4_split_points_change_only_rounding(pq, path):
     """The grid decides where a row's K range is cut between waves; any cut
     agrees with the oracle within the GEMV tolerance, and a repeated call with
     the same grid is bitwise identical."""
@@ -179,24 +213,26 @@ def test_gemv_q4_split_points_change_only_rounding(pq):
     p, s, pg, sg = _q4_on_gpu(pq, w)
     yo, So = oracle.gemv_q4(x, p, s)
     for n in (1, 2, 3, 8):
-        with blocks_per_cu(n):
+        with blocks_per_cu(n), env("PQ_Q4_PATH", path):
             ys = pq.gemv_q4(xt, pg, sg)
             ys2 = pq.gemv_q4(xt, pg, sg)
         assert torch.equal(ys.view(torch.int16), ys2.view(torch.int16))
         assert_gemv_close(bf16_to_np(ys), yo, So, f"blocks/CU={n}")
 
 
-def test_gemv_q4_zero_inputs(pq):
+@pytest.mark.parametrize("K,path", [(1056, None), (1024, "valu"), (1024, "mfma")])
+def test_gemv_q4_zero_inputs(pq, K, path):
     import torch
-    M, K, N = 3, 1024, 80
+    M, N = 3, 80
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=3)
     p, s = oracle.q4_quant(w)
-    y = pq.gemv_q4(x, _upload(p), _upload(s))
-    assert torch.count_nonzero(y.view(torch.int16)) == 0
     xt = np_bf16_bits_to_torch(workloads.activation_bf16(M, K, workload=workloads.Q4_STACK, seed=3))
-    y = pq.gemv_q4(xt, _upload(np.full_like(p, 0x88)), _upload(s))     # every code is 0
-    assert torch.count_nonzero(y.view(torch.int16)) == 0
+    with env("PQ_Q4_PATH", path):
+        y = pq.gemv_q4(x, _upload(p), _upload(s))
+        assert torch.count_nonzero(y.view(torch.int16)) == 0
+        y = pq.gemv_q4(xt, _upload(np.full_like(p, 0x88)), _upload(s))     # every code is 0
+        assert torch.count_nonzero(y.view(torch.int16)) == 0
 
 
 @pytest.mark.parametrize("M,K,N,epi", [

@@ -265,7 +265,8 @@ struct WsHeader {
   uint32_t error;       // first pq_status recorded by a kernel (0 = none)
   uint32_t done;        // phase counter of the running call
   uint32_t exit_count;  // blocks that finished the running call
-  uint32_t pad[61];     // keep the header one 256-byte line
+  uint32_t epoch;       // calls completed on this workspace (wraps)
+  uint32_t pad[60];     // keep the header one 256-byte line
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is one 256-byte line");
 
@@ -282,6 +283,17 @@ __device__ __forceinline__ bool spin_wait_geq(const uint32_t* ctr, uint32_t targ
   for (uint32_t it = 0; it < limit; ++it) {
     if (atomic_load_relaxed(ctr) >= target) return true;
     __builtin_amdgcn_s_sleep(2);
+  }
+  record_error(h, PQ_ERR_TIMEOUT);
+  return false;
+}
+
+// Wait until *flag == value.  Each waiting block polls its own flag line, so
+// the polls do not contend with the atomics of the phase counter.
+__device__ __forceinline__ bool spin_wait_eq(const uint32_t* flag, uint32_t value, WsHeader* h, uint32_t limit) {
+  for (uint32_t it = 0; it < limit; ++it) {
+    if (atomic_load_relaxed(flag) == value) return true;
+    __builtin_amdgcn_s_sleep(1);
   }
   record_error(h, PQ_ERR_TIMEOUT);
   return false;

@@ -11,7 +11,7 @@
 // merging small kernels into few dispatches raised decode from 59% to 81% of
 // measured bandwidth.  Here the whole layer is one launch.
 //
-// Structure (persistent blocks, all resident, 8 waves each, static work split)
+// Structure (persistent blocks, one per CU, 16 waves each, static work split)
 //   A. routing: wave m ranks token m's logits (top-k, ties to the lower id,
 //      softmax over the selected logits); wave 0 then builds the union of
 //      routed experts in first-appearance order.  Every block does this
@@ -21,19 +21,17 @@
 //   C. gate_up units (union entry u, h-row i): each wave streams a contiguous
 //      range of units (gate row + up row, one 1 KB chunk per lane-step, a ring
 //      of DG steps in flight) and stores h = silu(g)*u (bf16) for every token
-//      routed to u.  The block then counts its rows into per-(u, 128-row
-//      group) counters; the block completing a group re-quantises that group
-//      of h for every token (the result depends on values only) and bumps the
-//      phase counter.
+//      routed to u, then adds its row count to the phase counter.
 //   D. down units (output row n, all union entries): waves issue their first
-//      down weight loads, the block waits for the phase counter, stages the
-//      quantised h of every (token, slot) pair in LDS and streams its rows; per
+//      down weight loads, the block waits for the phase counter to reach every
+//      h row, quantises h of every (token, slot) pair into LDS (each block
+//      derives the same codes from the same values) and streams its rows; per
 //      row each (token, slot) partial is reduced across the wave and each
 //      token's slots are combined in slot order.
 //   E. the last block to finish resets the counters it used, so the workspace
 //      is ready for the next call without a clearing launch.
 //
-// Cross-block data (h, its quantisation, counters) travels through the
+// Cross-block data (h and the counters) travels through the
 // agent-coherent (sc1) path: no L2 writeback or invalidate is needed.
 // Every weight byte of the union is read once per call.  The arithmetic done
 // for one token does not depend on the other tokens of the call (same lane
@@ -45,17 +43,17 @@
 
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / pq::kWave;
 constexpr int kMaxM = 8;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxPairs = kMaxM * kMaxTopK;   // 64 = one lane per (token, slot)
 constexpr int kMaxUnion = kMaxPairs;
 constexpr int kMaxE = 1024;
-constexpr int kXPre = 2;
 constexpr int DG = 4;     // gate_up ring depth (chunk-steps; 2 rows per step)
 constexpr int DD = 8;     // down ring depth (chunk-steps; 1 row per step)
 constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int kFlagStride = 32;          // uint32 per release flag: one 128-byte line each
 
 struct MoeArgs {
   const uint16_t* x;
@@ -72,8 +70,6 @@ struct MoeArgs {
   float* hs_dbg;
   uint8_t* ws;
   uint16_t* hbuf;   // [P][I] bf16
-  uint8_t* hq;      // [P][I] E4M3
-  float* hs;        // [P][I/128]
   int M, H, I, E, top_k;
   int routed;
   uint32_t spin_limit;
@@ -211,9 +207,12 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Route route;
   __shared__ int s_last;
+  __shared__ uint32_t s_next;     // next gate_up unit of this block
+  __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
+  __shared__ uint32_t s_epoch;    // value the release flags take in this call
 
   pq::WsHeader* hdr = reinterpret_cast<pq::WsHeader*>(a.ws);
-  uint32_t* gcnt = reinterpret_cast<uint32_t*>(a.ws + pq::kWsCounterOff);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + pq::kWsCounterOff);   // one line per block
 
   const int lane = pq::lane_id();
   const int wv = pq::wave_id();
@@ -234,9 +233,21 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   // ---- x loads first (independent of routing) ------------------------------
   const long totx8 = (long)a.M * H / 8;
   const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
+  // enough loads in flight for the whole of x at H = 6144 (16 bytes each)
+  constexpr int kXPre = (TP * 3 + 3) / 4;
   uint4 xraw[kXPre];
 #pragma unroll
-  for (int it = 0; it < kXPre; ++it) xraw[it] = pq::buf_load16(xr, (uint32_t)(it * kThreads + threadIdx.x) * 16u);
+  for (int it = 0; it < kXPre; ++it) {
+    const long t = (long)it * kThreads + threadIdx.x;
+    xraw[it] = pq::buf_load16(xr, t < totx8 ? (uint32_t)t * 16u : pq::kOOB);
+  }
+
+
+  if (threadIdx.x == 0) {       // block counters; first used after the barriers below
+    s_next = 0u;
+    s_arrive = 0u;
+    s_epoch = pq::ld_agent_u32(&hdr->epoch) + 1u;   // this call's flag value
+  }
 
   // ---- A. routing (waves 0..M-1, one token each) -----------------------------
   if (a.routed) {
@@ -254,13 +265,68 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     route.w[lane] = a.topk_w[lane];
   }
 
-  // ---- B. live activation quantisation into LDS (x loads issued at entry) --
+  __syncthreads();                            // routes visible
+  if (wv == 0) build_union(a, route, hdr, TP);
+  __syncthreads();
+  const int nU = ufl(route.nU);
+
+  // ---- C. gate_up + SiLU*up -------------------------------------------------
+  // The block owns the units [bu0, bu1) (union entry u, h-row i: one gate row
+  // and one up row); its waves take them one at a time from an LDS counter,
+  // so a wave whose loads issue later (the scheduler favours older waves)
+  // simply takes fewer.  Each wave keeps DG chunk-steps in flight; every ring
+  // slot remembers its unit and chunk.
+  const int gu_units = nU * I;
+  const int bu0 = pq::split_start(gu_units, (int)gridDim.x, (int)blockIdx.x);
+  const int bu1 = pq::split_start(gu_units, (int)gridDim.x, (int)blockIdx.x + 1);
+
+  uint4 wb[DG][2];
+  float sb[DG][2];
+  int su[DG], sch[DG];              // unit (-1: none) and chunk of each slot
+  int iunit = bu0 - 1, ic = nchH;   // issue cursor
+  bool more = true;
+  int cur_e = -1;
+  pq::rsrc_t gwr = pq::make_rsrc(a.w13, 0u), gsr = pq::make_rsrc(a.s13, 0u);
+  auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], int& su_q, int& sch_q) {
+    if (ic == nchH && more) {       // take the block's next unit
+      int u = 0;
+      if (lane == 0) u = bu0 + (int)atomicAdd(&s_next, 1u);
+      iunit = ufl(u);
+      ic = 0;
+      more = iunit < bu1;
+      if (more) {
+        const int e = ufl(route.uexp[iunit / I]);
+        if (e != cur_e) {
+          cur_e = e;
+          gwr = pq::make_rsrc(a.w13 + (size_t)e * 2 * I * H, (uint32_t)(2 * I * H));
+          gsr = pq::make_rsrc(a.s13 + (size_t)e * 2 * I * nbH, (uint32_t)(2 * I * nbH * 4));
+        }
+      }
+    }
+    const uint32_t kc = (uint32_t)(ic * pq::kChunk);
+    const bool ok = more && kc + lane16 < (uint32_t)H;
+    const uint32_t ii = more ? (uint32_t)(iunit - (iunit / I) * I) : 0u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = ii + (uint32_t)(j * I);
+      w[j] = pq::buf_load16_nt(gwr, ok ? row * (uint32_t)H + kc + lane16 : pq::kOOB);
+      s[j] = pq::buf_load_f32_nt(gsr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+    }
+    su_q = more ? iunit : -1;
+    sch_q = ic;
+    if (more) ++ic;
+  };
+#pragma unroll
+  for (int q = 0; q < DG; ++q) issue_gu(wb[q], sb[q], su[q], sch[q]);
+
+  // ---- B. live activation quantisation into LDS (its loads, issued at entry,
+  //      are older than the weight ring, so this waits for x only) -----------
   {
     const int iters = (int)((totx8 + kThreads - 1) / kThreads);
     for (int it = 0; it < iters; ++it) {
       const long t = (long)it * kThreads + threadIdx.x;
       const bool valid = t < totx8;
-      const uint4 raw = it < kXPre ? xraw[it < kXPre ? it : 0] : pq::buf_load16(xr, (uint32_t)t * 16u);
+      const uint4 raw = it < kXPre ? xraw[it < kXPre ? it : 0] : pq::buf_load16(xr, valid ? (uint32_t)t * 16u : pq::kOOB);
       float v[8];
       pq::bf16x8_to_f32(raw, v);
       const float s = pq::fp8_block_scale16(v, valid);
@@ -271,59 +337,15 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     }
   }
   __syncthreads();
-  if (wv == 0) build_union(a, route, hdr, TP);
-  __syncthreads();
-  const int nU = ufl(route.nU);
 
-  // ---- C(prefetch). gate_up ring ------------------------------------------
-  const int gu_units = nU * I;
-  const int g0 = ufl(pq::split_start(gu_units, (int)T, gw));
-  const int g1 = ufl(pq::split_start(gu_units, (int)T, gw + 1));
-  const int gsteps = (g1 - g0) * nchH;
-
-  uint4 wb[DG][2];
-  float sb[DG][2];
-  int iu = g0 / I, ii = g0 - (g0 / I) * I, ic = 0;
-  pq::rsrc_t gwr, gsr;
-  auto set_gu_expert = [&]() {
-    const int e = ufl(route.uexp[iu < nU ? iu : 0]);
-    gwr = pq::make_rsrc(a.w13 + (size_t)e * 2 * I * H, (uint32_t)(2 * I * H));
-    gsr = pq::make_rsrc(a.s13 + (size_t)e * 2 * I * nbH, (uint32_t)(2 * I * nbH * 4));
-  };
-  set_gu_expert();
-  auto issue_gu = [&](uint4 (&w)[2], float (&s)[2]) {
-    const bool in_range = iu * I + ii < g1;
-    const uint32_t kc = (uint32_t)(ic * pq::kChunk);
-    const bool ok = in_range && kc + lane16 < (uint32_t)H;
-    const pq::rsrc_t wr = gwr, sr = gsr;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t row = (uint32_t)(ii + j * I);
-      w[j] = pq::buf_load16_nt(wr, ok ? row * (uint32_t)H + kc + lane16 : pq::kOOB);
-      s[j] = pq::buf_load_f32_nt(sr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
-    }
-    if (++ic == nchH) {
-      ic = 0;
-      if (++ii == I) {
-        ii = 0;
-        ++iu;
-        set_gu_expert();
-      }
-    }
-  };
-#pragma unroll
-  for (int q = 0; q < DG; ++q) issue_gu(wb[q], sb[q]);
-
-  // ---- C. gate_up + SiLU*up -------------------------------------------------
   {
     float accg[TP], accu[TP];
     int pr[TP], pm[TP];
 #pragma unroll
     for (int t = 0; t < TP; ++t) accg[t] = accu[t] = 0.0f;
-    int cu = g0 / I, ci = g0 - (g0 / I) * I, cc = 0;
-    int cnp = 0;
-    auto load_pairs = [&]() {
-      const int uu = cu < nU ? cu : 0;
+    int pairs_u = -1, cnp = 0;
+    auto load_pairs = [&](int uu) {
+      pairs_u = uu;
       cnp = ufl(route.unp[uu]);
 #pragma unroll
       for (int t = 0; t < TP; ++t) {
@@ -331,11 +353,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
         pm[t] = pr[t] / K;
       }
     };
-    load_pairs();
-    for (int base = 0; base < gsteps; base += DG) {
+    for (;;) {
 #pragma unroll
       for (int q = 0; q < DG; ++q) {
-        if (base + q < gsteps) {
+        if (su[q] >= 0) {
+          const int unit = su[q], cc = sch[q];
+          const int uu = unit / I, ci = unit - (unit / I) * I;
+          if (uu != pairs_u) load_pairs(uu);
           const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
           if (off < (uint32_t)H) {
             const pq::Bf16x16 wg = pq::widen16(wb[q][0]);
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
               }
             }
           }
-          if (cc == nchH - 1) {            // unit (cu, ci) done: h for every routed token
+          if (cc == nchH - 1) {            // unit done: h for every routed token
 #pragma unroll
             for (int t = 0; t < TP; ++t) {
               if (t < cnp) {
@@ -365,116 +389,119 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
               accg[t] = accu[t] = 0.0f;
             }
           }
-          if (++cc == nchH) {
-            cc = 0;
-            if (++ci == I) {
-              ci = 0;
-              ++cu;
-              load_pairs();
-            }
-          }
         }
-        issue_gu(wb[q], sb[q]);
+        issue_gu(wb[q], sb[q], su[q], sch[q]);
       }
+      bool busy = false;
+#pragma unroll
+      for (int q = 0; q < DG; ++q) busy |= su[q] >= 0;
+      if (!busy) break;
     }
   }
-  pq::wait_vm();            // this wave's h stores are complete
-  __syncthreads();
 
-  // ---- count the block's finished h rows per (u, 128-row group); the block
-  //      completing a group re-quantises it for every token routed to u -----
-  if (wv == 0) {
-    const int b0 = pq::split_start(gu_units, (int)T, (int)blockIdx.x * kWaves);
-    const int b1 = pq::split_start(gu_units, (int)T, (int)(blockIdx.x + 1) * kWaves);
-    uint32_t completed = 0;
-    for (int G = b0 >> 7; b1 > b0 && G <= (b1 - 1) >> 7; ++G) {
-      const int lo = b0 > (G << 7) ? b0 : (G << 7);
-      const int hi = b1 < ((G + 1) << 7) ? b1 : ((G + 1) << 7);
-      uint32_t old = 0;
-      if (lane == 0) old = pq::atomic_add_relaxed(&gcnt[G], (uint32_t)(hi - lo));
-      old = (uint32_t)ufl((int)__shfl(old, 0, pq::kWave));
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (old + (uint32_t)(hi - lo) == 128u) {
-        const int u = G / nbI, g = G - (G / nbI) * nbI;
-        const int np = ufl(route.unp[u]);
-        for (int t = 0; t < np; ++t) {
-          const int p = ufl(route.upairs[u][t]);
-          const size_t e0 = (size_t)p * I + (size_t)g * pq::kBlock + 2 * lane;
-          const uint32_t two = pq::ld_agent_u32(reinterpret_cast<const uint32_t*>(a.hbuf + e0));
-          const float v0 = pq::bf16_to_f32(two & 0xffffu), v1 = pq::bf16_to_f32(two >> 16);
-          const float m = __uint_as_float(pq::wave_max_u32(__float_as_uint(fmaxf(fabsf(v0), fabsf(v1)))));
-          const float s = pq::block_scale(m);
-          const double rcp = 1.0 / (double)s;
-          const uint16_t c2 =
-              (uint16_t)pq::e4m3_pack2<false>(pq::quotient_f32(v0, rcp), pq::quotient_f32(v1, rcp), 0u);
-          pq::st_agent_u16(reinterpret_cast<uint16_t*>(a.hq + e0), c2);
-          if (a.hq_dbg) *reinterpret_cast<uint16_t*>(a.hq_dbg + e0) = c2;
-          if (lane == 0) {
-            pq::st_agent_u32(reinterpret_cast<uint32_t*>(a.hs) + (size_t)p * nbI + g, __float_as_uint(s));
-            if (a.hs_dbg) a.hs_dbg[(size_t)p * nbI + g] = s;
-          }
-        }
-        ++completed;
-      }
+  // Count the finished h rows: each wave's stores complete (sc1) before it
+  // arrives; the last wave of the block to arrive adds the block's rows to
+  // the phase counter (one device atomic per block: they serialise on one
+  // address).
+  // The block that completes the count releases every block through its own
+  // flag line (value = this call's epoch, so a flag left by an earlier call
+  // never matches).
+  pq::wait_vm();
+  uint32_t last = 0;
+  if (lane == 0) {
+    const uint32_t before = atomicAdd(&s_arrive, 1u);
+    if (before == (uint32_t)(kWaves - 1) && bu1 > bu0) {
+      const uint32_t rows = (uint32_t)(bu1 - bu0);
+      last = pq::atomic_add_relaxed(&hdr->done, rows) + rows == (uint32_t)gu_units;
     }
-    if (completed) {
-      pq::wait_vm();       // the quantised groups are complete before they are announced
-      if (lane == 0) pq::atomic_add_relaxed(&hdr->done, completed);
-    }
+  }
+  if (ufl((int)last)) {
+    const uint32_t ep = s_epoch;
+    for (int b = lane; b < (int)gridDim.x; b += pq::kWave) pq::st_agent_u32(flags + (size_t)b * kFlagStride, ep);
   }
 
   // ---- D. down projection + weighted combine --------------------------------
   // Output rows are dealt to blocks as evenly as possible; inside a block the
-  // (row, union entry) units are split evenly over the waves.  Each unit's y
-  // for every routed token goes to LDS; the block then combines each token's
-  // slots in slot order.
+  // (union entry, row) units are taken expert by expert (consecutive rows of
+  // one expert are contiguous in memory) and split evenly over the waves.
+  // Each unit's y for every routed token goes to LDS; the block then combines
+  // each token's slots in slot order.
   const int r0 = pq::split_start(H, (int)gridDim.x, (int)blockIdx.x);
   const int r1 = pq::split_start(H, (int)gridDim.x, (int)blockIdx.x + 1);
-  const int bunits = (r1 - r0) * nU;
+  const int nrows = r1 - r0;
+  const int bunits = nrows * nU;
   const int v0 = ufl(pq::split_start(bunits, kWaves, wv));
   const int v1 = ufl(pq::split_start(bunits, kWaves, wv + 1));
   const int dsteps = (v1 - v0) * nchI;
   float* ybuf = acts + a.ybuf_off;                 // [row_local][P] fp32
   uint4 wd[DD];
   float sd[DD];
-  int jr = v0 / nU, ju = v0 - (v0 / nU) * nU, jc = 0;
+  int ju = nrows > 0 ? v0 / nrows : 0;
+  int jr = v0 - ju * nrows, jc = 0, dleft = dsteps;
   pq::rsrc_t dwr, dsr;
   auto set_dn_expert = [&]() {
-    const int e = ufl(route.uexp[ju]);
+    const int e = ufl(route.uexp[ju < nU ? ju : 0]);
     dwr = pq::make_rsrc(a.w2 + (size_t)e * H * I, (uint32_t)(H * I));
     dsr = pq::make_rsrc(a.s2 + (size_t)e * H * nbI, (uint32_t)(H * nbI * 4));
   };
   set_dn_expert();
   auto issue_dn = [&](uint4& w, float& s) {
-    const bool in_range = jr * nU + ju < v1;
     const uint32_t kc = (uint32_t)(jc * pq::kChunk);
-    const bool ok = in_range && kc + lane16 < (uint32_t)I;
+    const bool ok = dleft > 0 && kc + lane16 < (uint32_t)I;
     const uint32_t row = (uint32_t)(r0 + jr);
     w = pq::buf_load16_nt(dwr, ok ? row * (uint32_t)I + kc + lane16 : pq::kOOB);
     s = pq::buf_load_f32_nt(dsr, ok ? (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+    --dleft;
     if (++jc == nchI) {
       jc = 0;
-      if (++ju == nU) {
-        ju = 0;
-        ++jr;
+      if (++jr == nrows) {
+        jr = 0;
+        ++ju;
+        set_dn_expert();
       }
-      set_dn_expert();
     }
   };
 #pragma unroll
   for (int q = 0; q < DD; ++q) issue_dn(wd[q], sd[q]);
 
-  // wait for every h group of the call, then stage the quantised h in LDS
-  if (threadIdx.x == 0) pq::spin_wait_geq(&hdr->done, (uint32_t)(nU * nbI), hdr, a.spin_limit);
+  // wait for every h row of the call, then quantise h into LDS: every block
+  // derives the same codes and scales from the same values (block 0 also
+  // writes them out when asked)
+  if (threadIdx.x == 0) pq::spin_wait_eq(flags + (size_t)blockIdx.x * kFlagStride, s_epoch, hdr, a.spin_limit);
   __syncthreads();
   {
-    const uint32_t* hq32 = reinterpret_cast<const uint32_t*>(a.hq);
-    const uint32_t* hs32 = reinterpret_cast<const uint32_t*>(a.hs);
-    uint32_t* act32 = reinterpret_cast<uint32_t*>(act);
-    uint32_t* acts32 = reinterpret_cast<uint32_t*>(acts);
-    const int n4 = P * I / 4;
-    for (int t = threadIdx.x; t < n4; t += kThreads) act32[t] = pq::ld_agent_u32(hq32 + t);
-    for (int t = threadIdx.x; t < P * nbI; t += kThreads) acts32[t] = pq::ld_agent_u32(hs32 + t);
+    const uint32_t* h32 = reinterpret_cast<const uint32_t*>(a.hbuf);
+    const int nblk = P * nbI;
+    constexpr int kBatch = 8;                                // loads in flight per wave
+    for (int b0 = wv; b0 < nblk; b0 += kBatch * kWaves) {   // one 128-value block per wave step
+      uint32_t two[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int b = b0 + i * kWaves;
+        const int p = b / nbI, g = b - (b / nbI) * nbI;
+        two[i] = b < nblk ? pq::ld_agent_u32(h32 + ((size_t)p * I + (size_t)g * pq::kBlock) / 2 + lane) : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int b = b0 + i * kWaves;
+        if (b < nblk) {
+          const int p = b / nbI, g = b - (b / nbI) * nbI;
+          const size_t e0 = (size_t)p * I + (size_t)g * pq::kBlock + 2 * lane;
+          const float v0 = pq::bf16_to_f32(two[i] & 0xffffu), v1 = pq::bf16_to_f32(two[i] >> 16);
+          const float m = __uint_as_float(pq::wave_max_u32(__float_as_uint(fmaxf(fabsf(v0), fabsf(v1)))));
+          const float s = pq::block_scale(m);
+          const double rcp = 1.0 / (double)s;
+          const uint16_t c2 =
+              (uint16_t)pq::e4m3_pack2<false>(pq::quotient_f32(v0, rcp), pq::quotient_f32(v1, rcp), 0u);
+          *reinterpret_cast<uint16_t*>(act + e0) = c2;
+          if (lane == 0) acts[p * nbI + g] = s;
+          if (blockIdx.x == 0) {
+            if (a.hq_dbg) *reinterpret_cast<uint16_t*>(a.hq_dbg + e0) = c2;
+            if (a.hs_dbg && lane == 0) a.hs_dbg[p * nbI + g] = s;
+          }
+        }
+      }
+    }
   }
   __syncthreads();
 
@@ -483,52 +510,59 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     int pr[TP];
 #pragma unroll
     for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
-    int cr = v0 / nU, cu = v0 - (v0 / nU) * nU, cc = 0;
+    int cu = nrows > 0 ? v0 / nrows : 0;
+    int cr = v0 - cu * nrows, cc = 0;
     int cnp = 0;
     auto load_pairs = [&]() {
-      cnp = ufl(route.unp[cu]);
+      const int uu = cu < nU ? cu : 0;
+      cnp = ufl(route.unp[uu]);
 #pragma unroll
-      for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[cu][t]);
+      for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[uu][t]);
     };
     load_pairs();
-    for (int base = 0; base < dsteps; base += DD) {
+    auto consume_dn = [&](const uint4& w, float sw) {
+      const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
+      if (off < (uint32_t)I) {
+        const pq::Bf16x16 wv2 = pq::widen16(w);
 #pragma unroll
-      for (int q = 0; q < DD; ++q) {
-        if (base + q < dsteps) {
-          const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
-          if (off < (uint32_t)I) {
-            const pq::Bf16x16 wv2 = pq::widen16(wd[q]);
-#pragma unroll
-            for (int t = 0; t < TP; ++t) {
-              if (t < cnp) {
-                const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
-                const float hsc = acts[pr[t] * nbI + off / pq::kBlock];
-                acc[t] = fmaf(pq::dot16(wv2, hv), sd[q] * hsc, acc[t]);
-              }
-            }
-          }
-          if (cc == nchI - 1) {           // unit (row cr, union entry cu) done
-#pragma unroll
-            for (int t = 0; t < TP; ++t) {
-              if (t < cnp) {
-                const float y = pq::wave_sum(acc[t]);
-                if (lane == 0) ybuf[cr * P + pr[t]] = y;
-              }
-              acc[t] = 0.0f;
-            }
-          }
-          if (++cc == nchI) {
-            cc = 0;
-            if (++cu == nU) {
-              cu = 0;
-              ++cr;
-            }
-            load_pairs();
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp) {
+            const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
+            const float hsc = acts[pr[t] * nbI + off / pq::kBlock];
+            acc[t] = fmaf(pq::dot16(wv2, hv), sw * hsc, acc[t]);
           }
         }
+      }
+      if (cc == nchI - 1) {               // unit (union entry cu, row cr) done
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp) {
+            const float y = pq::wave_sum(acc[t]);
+            if (lane == 0) ybuf[cr * P + pr[t]] = y;
+          }
+          acc[t] = 0.0f;
+        }
+      }
+      if (++cc == nchI) {
+        cc = 0;
+        if (++cr == nrows) {
+          cr = 0;
+          ++cu;
+          load_pairs();
+        }
+      }
+    };
+    int base = 0;
+    for (; base + DD < dsteps; base += DD) {     // steady state: every slot refills
+#pragma unroll
+      for (int q = 0; q < DD; ++q) {
+        consume_dn(wd[q], sd[q]);
         issue_dn(wd[q], sd[q]);
       }
     }
+#pragma unroll
+    for (int q = 0; q < DD; ++q)                 // drain
+      if (base + q < dsteps) consume_dn(wd[q], sd[q]);
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < (r1 - r0) * a.M; idx += kThreads) {
@@ -546,10 +580,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   }
   __syncthreads();
   if (s_last) {
-    for (int t = threadIdx.x; t < nU * nbI; t += kThreads) pq::atomic_store_relaxed(&gcnt[t], 0u);
     if (threadIdx.x == 0) {
       pq::atomic_store_relaxed(&hdr->done, 0u);
       pq::atomic_store_relaxed(&hdr->exit_count, 0u);
+      pq::atomic_store_relaxed(&hdr->epoch, s_epoch);
     }
   }
 }
@@ -560,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 struct MoePlan {
   size_t lds;
   int ybuf_off;
-  size_t off_h, off_hq, off_hs, ws_total;
+  size_t off_h, ws_total;
 };
 
 // num_cus bounds the rows a block can own (the grid has at least one block per
@@ -571,7 +605,6 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, MoePlan* p) {
     return PQ_ERR_SHAPE;
   const size_t P = (size_t)M * top_k;
   const size_t nbI = I / pq::kBlock;
-  if (P * nbI > pq::kWsMaxCounters) return PQ_ERR_SHAPE;
   if ((size_t)2 * I * H > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
   const size_t act = (size_t)M * H > P * I ? (size_t)M * H : P * I;
   const size_t nsc = (size_t)M * H / pq::kBlock > P * nbI ? (size_t)M * H / pq::kBlock : P * nbI;
@@ -583,9 +616,7 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, MoePlan* p) {
     if (p->lds + sizeof(Route) + 64 > 160 * 1024) return PQ_ERR_SHAPE;
   }
   p->off_h = pq::kWsDataOff;
-  p->off_hq = pqhost::align_up(p->off_h + P * I * 2, 256);
-  p->off_hs = pqhost::align_up(p->off_hq + P * I, 256);
-  p->ws_total = pqhost::align_up(p->off_hs + P * nbI * 4, 256);
+  p->ws_total = pqhost::align_up(p->off_h + P * I * 2, 256);
   return PQ_OK;
 }
 
@@ -601,7 +632,10 @@ int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& de
   int per_cu = 0;
   PQ_HIP_CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads, pl.lds));
   if (per_cu < 1) return PQ_ERR_SHAPE;
-  const int grid = dev.num_cus * per_cu;   // every block resident: blocks wait on each other
+  // one block per CU (blocks wait on each other, so all must be resident; one
+  // per CU also keeps the per-block staging of h to one copy per CU)
+  const int grid = dev.num_cus;
+  if ((size_t)grid * kFlagStride * 4 > pq::kWsDataOff - pq::kWsCounterOff) return PQ_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), pl.lds, stream, a);
   PQ_HIP_CHECK(hipGetLastError());
   return PQ_OK;
@@ -641,8 +675,6 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
   a.h_dbg = h_dbg; a.hq_dbg = hq_dbg; a.hs_dbg = hs_dbg;
   a.ws = reinterpret_cast<uint8_t*>(ws);
   a.hbuf = reinterpret_cast<uint16_t*>(a.ws + pl.off_h);
-  a.hq = a.ws + pl.off_hq;
-  a.hs = reinterpret_cast<float*>(a.ws + pl.off_hs);
   a.M = M; a.H = H; a.I = I; a.E = E; a.top_k = top_k;
   a.routed = router_logits != nullptr;
   a.spin_limit = kSpinLimit;

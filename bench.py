@@ -261,20 +261,27 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES):
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
 
-    def pick(d, key):
-        for name, vals in d.items():
-            if key in name:
-                return sum(vals) / len(vals), len(vals), name
-        raise KeyError(key)
+    def pick(d, key, largest=False):
+        vals, name = [], None
+        for n, v in d.items():
+            if key in n:
+                vals += v
+                name = n
+        if not vals:
+            raise KeyError(key)
+        if largest:              # the calibration copies: the dispatches of the largest size
+            top = max(vals)
+            vals = [v for v in vals if v >= 0.5 * top]
+        return sum(vals) / len(vals), len(vals), name
 
     mf, nf, _ = pick(f, KERNEL_NAME)
     mw, nw, _ = pick(w, KERNEL_NAME)
-    cf, _, cname = pick(f, "copy")
-    cw, _, _ = pick(w, "copy")
+    cf, ncf, cname = pick(f, "copy", largest=True)
+    cw, ncw, _ = pick(w, "copy", largest=True)
     d = {
         "kernel": KERNEL_NAME, "source_sha": kernel_source_sha(),
         "fetch_kib": mf, "write_kib": mw, "dispatches": [nf, nw],
-        "copy_kernel": cname, "copy_bytes": copy_bytes,
+        "copy_kernel": cname, "copy_bytes": copy_bytes, "copy_dispatches": [ncf, ncw],
         "copy_fetch_kib": cf, "copy_write_kib": cw,
         "fetch_scale": copy_bytes / (cf * 1024), "write_scale": copy_bytes / (cw * 1024),
     }

@@ -46,10 +46,14 @@ def _case(M, K, N, seed, workload=workloads.FP8_GEMV_SMALL):
 
 
 def _run(pq, xt, wt, epi, s=None):
+    """GPU GEMV on library-quantised weights; returns the oracle's own codes and
+    scales (checked equal to the library's) for the reference computation."""
     q, sc = pq.quantize_fp8(wt)
+    qo, so = oracle.block_quant_fp8(wt.cpu().numpy())
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(sc.cpu().numpy().view(np.uint32), so.view(np.uint32))
     with splitk(s):
         y, xq, xs = pq.gemv_fp8(xt, q, sc, epi=epi, debug=True)
-    return y, xq, xs, q, sc
+    return y, xq, xs, qo, so
 
 
 @pytest.mark.parametrize("M,K,N,S", [
@@ -66,7 +70,7 @@ def test_gemv_fp8_plain(pq, M, K, N, S):
     qx, sx = oracle.act_quant_fp8(x)
     assert np.array_equal(xq.cpu().numpy(), qx)
     assert np.array_equal(xs.cpu().numpy().view(np.uint32), sx.view(np.uint32))
-    yo, So = oracle.gemv_fp8(qx, sx, q.cpu().numpy(), sc.cpu().numpy())
+    yo, So = oracle.gemv_fp8(qx, sx, q, sc)
     assert_gemv_close(bf16_to_np(y), yo, So, f"M={M} K={K} N={N} S={S}")
 
 
@@ -81,7 +85,7 @@ def test_gemv_fp8_silu(pq, M, K, N, S):
     y, xq, xs, q, sc = _run(pq, xt, wt, pq.EPI_SILU_MUL, S)
     qx, sx = oracle.act_quant_fp8(x)
     assert np.array_equal(xq.cpu().numpy(), qx)
-    yo, So = oracle.gemv_fp8(qx, sx, q.cpu().numpy(), sc.cpu().numpy())
+    yo, So = oracle.gemv_fp8(qx, sx, q, sc)
     I = N // 2
     h = oracle.silu_mul(yo, I)
     assert_silu_close(bf16_to_np(y), h, yo[:, :I], yo[:, I:], So[:, :I], So[:, I:], f"M={M} S={S}")

@@ -53,6 +53,7 @@ constexpr int kMaxE = 1024;
 constexpr int DG = 4;     // gate_up ring depth (chunk-steps; 2 rows per step)
 constexpr int DD = 8;     // down ring depth (chunk-steps; 1 row per step)
 constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int kAuxSC1 = 0x10;            // buffer aux bit: agent-coherent (sc1) access
 constexpr int kFlagStride = 32;          // uint32 per release flag: one 128-byte line each
 
 struct MoeArgs {
@@ -470,34 +471,33 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   if (threadIdx.x == 0) pq::spin_wait_eq(flags + (size_t)blockIdx.x * kFlagStride, s_epoch, hdr, a.spin_limit);
   __syncthreads();
   {
-    const uint32_t* h32 = reinterpret_cast<const uint32_t*>(a.hbuf);
-    const int nblk = P * nbI;
-    constexpr int kBatch = 8;                                // loads in flight per wave
-    for (int b0 = wv; b0 < nblk; b0 += kBatch * kWaves) {   // one 128-value block per wave step
-      uint32_t two[kBatch];
+    // 8 values per lane, 16 lanes per 128-value block (the layout of the
+    // activation quantiser); agent-coherent 16-byte loads, a batch in flight
+    const int nvec = P * I / 8;
+    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P * I * 2));
+    constexpr int kBatch = 2;
+    for (int t0 = 0; t0 < nvec; t0 += kBatch * kThreads) {
+      uint4 raw[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        const int b = b0 + i * kWaves;
-        const int p = b / nbI, g = b - (b / nbI) * nbI;
-        two[i] = b < nblk ? pq::ld_agent_u32(h32 + ((size_t)p * I + (size_t)g * pq::kBlock) / 2 + lane) : 0u;
+        const int t = t0 + i * kThreads + (int)threadIdx.x;
+        raw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            hr, (int)(t < nvec ? (uint32_t)t * 16u : pq::kOOB), 0, kAuxSC1));
       }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        const int b = b0 + i * kWaves;
-        if (b < nblk) {
-          const int p = b / nbI, g = b - (b / nbI) * nbI;
-          const size_t e0 = (size_t)p * I + (size_t)g * pq::kBlock + 2 * lane;
-          const float v0 = pq::bf16_to_f32(two[i] & 0xffffu), v1 = pq::bf16_to_f32(two[i] >> 16);
-          const float m = __uint_as_float(pq::wave_max_u32(__float_as_uint(fmaxf(fabsf(v0), fabsf(v1)))));
-          const float s = pq::block_scale(m);
-          const double rcp = 1.0 / (double)s;
-          const uint16_t c2 =
-              (uint16_t)pq::e4m3_pack2<false>(pq::quotient_f32(v0, rcp), pq::quotient_f32(v1, rcp), 0u);
-          *reinterpret_cast<uint16_t*>(act + e0) = c2;
-          if (lane == 0) acts[p * nbI + g] = s;
+        const int t = t0 + i * kThreads + (int)threadIdx.x;
+        const bool valid = t < nvec;
+        float v[8];
+        pq::bf16x8_to_f32(raw[i], v);
+        const float sc = pq::fp8_block_scale16(v, valid);
+        if (valid) {
+          const uint2 c8 = pq::fp8_codes8(v, sc);
+          reinterpret_cast<uint2*>(act)[t] = c8;
+          if ((threadIdx.x & 15) == 0) acts[t / 16] = sc;
           if (blockIdx.x == 0) {
-            if (a.hq_dbg) *reinterpret_cast<uint16_t*>(a.hq_dbg + e0) = c2;
-            if (a.hs_dbg && lane == 0) a.hs_dbg[p * nbI + g] = s;
+            if (a.hq_dbg) reinterpret_cast<uint2*>(a.hq_dbg)[t] = c8;
+            if (a.hs_dbg && (threadIdx.x & 15) == 0) a.hs_dbg[t / 16] = sc;
           }
         }
       }

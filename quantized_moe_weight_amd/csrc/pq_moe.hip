@@ -231,18 +231,21 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   uint8_t* act = smem;                                                              // codes
   float* acts = reinterpret_cast<float*>(smem + pqhost::align_up(act_bytes, 16));   // scales
 
-  // ---- x loads first (independent of routing) ------------------------------
+  // ---- x loads first (independent of routing), by the waves that do not
+  //      route: they quantise x while waves 0..M-1 rank the logits --------------
+  const int nrt = a.routed ? a.M : 1;               // routing waves
+  const int tq = (int)threadIdx.x - nrt * pq::kWave;  // quantising thread index (< 0: routing wave)
+  const int nq = kThreads - nrt * pq::kWave;
   const long totx8 = (long)a.M * H / 8;
   const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
-  // enough loads in flight for the whole of x at H = 6144 (16 bytes each)
-  constexpr int kXPre = (TP * 3 + 3) / 4;
+  // enough loads in flight for the whole of x at H = 6144 up to M = 4 (16 bytes each)
+  constexpr int kXPre = TP == 1 ? 1 : TP == 2 ? 2 : TP == 4 ? 4 : 8;
   uint4 xraw[kXPre];
 #pragma unroll
   for (int it = 0; it < kXPre; ++it) {
-    const long t = (long)it * kThreads + threadIdx.x;
-    xraw[it] = pq::buf_load16(xr, t < totx8 ? (uint32_t)t * 16u : pq::kOOB);
+    const long t = (long)it * nq + tq;
+    xraw[it] = pq::buf_load16(xr, tq >= 0 && t < totx8 ? (uint32_t)t * 16u : pq::kOOB);
   }
-
 
   if (threadIdx.x == 0) {       // block counters; first used after the barriers below
     s_next = 0u;
@@ -266,7 +269,24 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     route.w[lane] = a.topk_w[lane];
   }
 
-  __syncthreads();                            // routes visible
+  // ---- B. live activation quantisation into LDS (non-routing waves) --------
+  if (tq >= 0) {
+    const int iters = (int)((totx8 + nq - 1) / nq);
+    for (int it = 0; it < iters; ++it) {
+      const long t = (long)it * nq + tq;
+      const bool valid = t < totx8;
+      const uint4 raw = it < kXPre ? xraw[it < kXPre ? it : 0] : pq::buf_load16(xr, valid ? (uint32_t)t * 16u : pq::kOOB);
+      float v[8];
+      pq::bf16x8_to_f32(raw, v);
+      const float s = pq::fp8_block_scale16(v, valid);
+      if (valid) {
+        reinterpret_cast<uint2*>(act)[t] = pq::fp8_codes8(v, s);
+        if ((tq & 15) == 0) acts[(t * 8) / pq::kBlock] = s;
+      }
+    }
+  }
+
+  __syncthreads();                            // routes and the quantised x visible
   if (wv == 0) build_union(a, route, hdr, TP);
   __syncthreads();
   const int nU = ufl(route.nU);
@@ -320,24 +340,6 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 #pragma unroll
   for (int q = 0; q < DG; ++q) issue_gu(wb[q], sb[q], su[q], sch[q]);
 
-  // ---- B. live activation quantisation into LDS (its loads, issued at entry,
-  //      are older than the weight ring, so this waits for x only) -----------
-  {
-    const int iters = (int)((totx8 + kThreads - 1) / kThreads);
-    for (int it = 0; it < iters; ++it) {
-      const long t = (long)it * kThreads + threadIdx.x;
-      const bool valid = t < totx8;
-      const uint4 raw = it < kXPre ? xraw[it < kXPre ? it : 0] : pq::buf_load16(xr, valid ? (uint32_t)t * 16u : pq::kOOB);
-      float v[8];
-      pq::bf16x8_to_f32(raw, v);
-      const float s = pq::fp8_block_scale16(v, valid);
-      if (valid) {
-        reinterpret_cast<uint2*>(act)[t] = pq::fp8_codes8(v, s);
-        if ((threadIdx.x & 15) == 0) acts[(t * 8) / pq::kBlock] = s;
-      }
-    }
-  }
-  __syncthreads();
 
   {
     float accg[TP], accu[TP];

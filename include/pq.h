@@ -97,9 +97,9 @@ int pq_quantize_q4(const float* w, int N, int K, uint8_t* packed, uint16_t* scal
 /* quantisation fused in ([Sionic] §1 and §4; §2 scales per K block).         */
 /* ------------------------------------------------------------------------- */
 
-/* Workspace bytes pq_gemv_fp8 needs for this shape (split-K partials and
- * completion counters); 0 when no split is used.  Returns 0 for invalid
- * shapes as well (pq_gemv_fp8 then reports the error). */
+/* Workspace bytes pq_gemv_fp8 needs: always 0 (where a row's K range is cut
+ * between waves, the parts are reduced on chip); kept so the call has the
+ * same shape of API as the others. */
 size_t pq_gemv_fp8_workspace(int M, int K, int N, int epi);
 
 /* y = epi(bf16( sum_b s_x[m,b] s_w[n,b] sum_{k in b} q_x[m,k] q_w[n,k] ))
@@ -109,10 +109,12 @@ size_t pq_gemv_fp8_workspace(int M, int K, int N, int epi);
  *   y       : bf16 [M,N] (PQ_EPI_NONE) or bf16 [M,N/2] (PQ_EPI_SILU_MUL)
  *   xq_dbg  : nullable, E4M3 [M,K]  — the quantised activation codes
  *   xs_dbg  : nullable, fp32 [M,K/128] — the activation scales
- *   ws      : device workspace of ws_bytes >= pq_gemv_fp8_workspace(...)
- *             (may be NULL when that is 0), zeroed once by pq_workspace_init.
+ *   ws, ws_bytes : ignored (may be NULL / 0).
  * Constraints: 1 <= M <= 8, K % 128 == 0, 128 <= K <= 16384, N >= 1,
- * N even under PQ_EPI_SILU_MUL. */
+ * N*K < 2^31, N even under PQ_EPI_SILU_MUL; PQ_ERR_SHAPE otherwise.
+ * Each output row is computed by one block; its bits depend on the shape and
+ * the device's CU count only (not on M or on the other rows); the variable
+ * PQ_BLOCKS_PER_CU (default 1) sets the number of blocks per CU. */
 int pq_gemv_fp8(const uint16_t* x, int M, int K,
                 const uint8_t* w, const float* w_scale, int N,
                 int epi, uint16_t* y,

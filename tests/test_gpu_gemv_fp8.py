@@ -1,5 +1,6 @@
 """GPU parity of pq_gemv_fp8 (live FP8 activation quant + block-scaled FP8 GEMV,
-split-K, SiLU*up epilogue) against the oracle."""
+K split inside a block, SiLU*up epilogue) against the oracle.  The parameter S
+sets PQ_BLOCKS_PER_CU, which moves where rows are cut between waves."""
 import os
 
 import numpy as np
@@ -21,21 +22,22 @@ def pq():
 
 
 class splitk:
-    """Force the split-K factor of the library for the duration of a block."""
+    """Set PQ_BLOCKS_PER_CU (how many blocks share the rows, hence where a row's
+    K range is cut between waves) for the duration of a block."""
 
     def __init__(self, s):
         self.s = s
 
     def __enter__(self):
-        self.old = os.environ.get("PQ_SPLITK")
+        self.old = os.environ.get("PQ_BLOCKS_PER_CU")
         if self.s is not None:
-            os.environ["PQ_SPLITK"] = str(self.s)
+            os.environ["PQ_BLOCKS_PER_CU"] = str(self.s)
 
     def __exit__(self, *a):
         if self.old is None:
-            os.environ.pop("PQ_SPLITK", None)
+            os.environ.pop("PQ_BLOCKS_PER_CU", None)
         else:
-            os.environ["PQ_SPLITK"] = self.old
+            os.environ["PQ_BLOCKS_PER_CU"] = self.old
 
 
 def _case(M, K, N, seed, workload=workloads.FP8_GEMV_SMALL):

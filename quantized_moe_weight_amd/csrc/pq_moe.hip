@@ -169,34 +169,52 @@ __device__ void route_token(const MoeArgs& a, Route& r, int m) {
   }
 }
 
-// Union of routed experts in first-appearance order over pairs p = m*top_k+j
-// (one wave; lane p owns pair p): repeatedly take the lowest unassigned pair,
-// and assign every pair with the same expert to a new union entry.
-__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, int tp) {
+// Union of the routed experts in ascending expert id (the order does not
+// change any result: every h row and every y row is computed whole by one
+// wave, and each token's slots are combined in slot order), built in parallel
+// by one wave: lane p marks expert ids[p] in an LDS bitmap, the union index of
+// an expert is the number of marked ids below it, and a pair's place among the
+// pairs of its expert is the number of lower pairs with the same id.  An
+// expert given twice to one token is an error.
+__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, int tp, uint32_t* emask) {
   const int lane = pq::lane_id();
   const int P = a.M * a.top_k;
-  const int id = lane < P ? r.ids[lane] : -1;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint64_t remaining = __ballot(lane < P);
-  int u = 0;
-  while (remaining) {
-    const int p0 = (int)__builtin_ctzll(remaining);
-    const int e = __builtin_amdgcn_readlane(id, p0);
-    const uint64_t mine = __ballot(lane < P && id == e);
-    const int n = __popcll(mine);
-    if (lane == p0) {
-      r.uexp[u] = e;
+  const bool act = lane < P;
+  const int id = act ? r.ids[lane] : 0;
+  if (act) atomicOr(&emask[id >> 5], 1u << (id & 31));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);       // LDS ops of one wave complete in order
+  const int nw = (a.E + 31) >> 5;
+  const uint32_t word = lane < nw ? __hip_atomic_load(&emask[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
+  const int cnt = __popc(word);
+  int incl = cnt;                                  // inclusive prefix over the bitmap words
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) {
+    const int v = __shfl_up(incl, d, pq::kWave);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - cnt;
+  const int total = __shfl(incl, 31, pq::kWave);
+  const int w = id >> 5;
+  const int u = __shfl(excl, w, pq::kWave) + __popc((uint32_t)__shfl((int)word, w, pq::kWave) & ((1u << (id & 31)) - 1u));
+  int slot = 0, n = 0;
+  bool dup = false;
+  for (int q = 0; q < P; ++q) {
+    const int idq = __builtin_amdgcn_readlane(id, q);
+    if (idq == id) {
+      ++n;
+      if (q < lane) ++slot;
+      if (q != lane && q / a.top_k == lane / a.top_k) dup = true;
+    }
+  }
+  if (act) {
+    if (slot == 0) {
+      r.uexp[u] = id;
       r.unp[u] = n < tp ? n : tp;
     }
-    if ((mine >> lane) & 1ull) {
-      const int before = __popcll(mine & below);
-      if (before < tp) r.upairs[u][before] = lane;
-      else if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);   // an expert twice in one token
-    }
-    remaining &= ~mine;
-    ++u;
+    if (slot < tp) r.upairs[u][slot] = lane;
+    if ((slot >= tp || dup) && blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
   }
-  if (lane == 0) r.nU = u;
+  if (lane == 0) r.nU = total;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
@@ -208,6 +226,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Route route;
   __shared__ int s_last;
+  __shared__ uint32_t s_emask[kMaxE / 32];   // routed-expert bitmap
   __shared__ uint32_t s_next;     // next gate_up unit of this block
   __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
   __shared__ uint32_t s_epoch;    // value the release flags take in this call
@@ -231,12 +250,15 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   uint8_t* act = smem;                                                              // codes
   float* acts = reinterpret_cast<float*>(smem + pqhost::align_up(act_bytes, 16));   // scales
 
-  // ---- x loads first (independent of routing), by the waves that do not
-  //      route: they quantise x while waves 0..M-1 rank the logits --------------
+  // ---- x loads first (independent of routing); the waves that do not route
+  //      quantise x while waves 0..M-1 rank the logits ------------------------
   const int nrt = a.routed ? a.M : 1;               // routing waves
-  const int tq = (int)threadIdx.x - nrt * pq::kWave;  // quantising thread index (< 0: routing wave)
-  const int nq = kThreads - nrt * pq::kWave;
   const long totx8 = (long)a.M * H / 8;
+  // when the other waves cannot cover x in one pass, every wave takes a share
+  // (the routing waves after routing)
+  const bool xq_all = totx8 > (long)(kThreads - nrt * pq::kWave);
+  const int tq = xq_all ? (int)threadIdx.x : (int)threadIdx.x - nrt * pq::kWave;   // < 0: routing wave only
+  const int nq = xq_all ? kThreads : kThreads - nrt * pq::kWave;
   const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
   // enough loads in flight for the whole of x at H = 6144 up to M = 4 (16 bytes each)
   constexpr int kXPre = TP == 1 ? 1 : TP == 2 ? 2 : TP == 4 ? 4 : 8;
@@ -252,6 +274,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     s_arrive = 0u;
     s_epoch = pq::ld_agent_u32(&hdr->epoch) + 1u;   // this call's flag value
   }
+  if (threadIdx.x < kMaxE / 32) s_emask[threadIdx.x] = 0u;
 
   // ---- A. routing (waves 0..M-1, one token each) -----------------------------
   if (a.routed) {
@@ -269,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     route.w[lane] = a.topk_w[lane];
   }
 
-  // ---- B. live activation quantisation into LDS (non-routing waves) --------
+  // ---- B. live activation quantisation into LDS ------------------------------
   if (tq >= 0) {
     const int iters = (int)((totx8 + nq - 1) / nq);
     for (int it = 0; it < iters; ++it) {
@@ -287,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   }
 
   __syncthreads();                            // routes and the quantised x visible
-  if (wv == 0) build_union(a, route, hdr, TP);
+  if (wv == 0) build_union(a, route, hdr, TP, s_emask);
   __syncthreads();
   const int nU = ufl(route.nU);
 
@@ -593,6 +616,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+// LDS the kernel declares statically (routing tables, expert bitmap, block
+// counters), reserved next to the dynamic area.
+constexpr size_t kStaticLds = sizeof(Route) + kMaxE / 8 + 256;
+
 struct MoePlan {
   size_t lds;
   int ybuf_off;
@@ -615,7 +642,7 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, MoePlan* p) {
   if (num_cus > 0) {
     const size_t rows_max = ((size_t)H + num_cus - 1) / num_cus;
     p->lds = pqhost::align_up(act, 16) + (nsc + rows_max * P) * 4;
-    if (p->lds + sizeof(Route) + 64 > 160 * 1024) return PQ_ERR_SHAPE;
+    if (p->lds + kStaticLds > 160 * 1024) return PQ_ERR_SHAPE;
   }
   p->off_h = pq::kWsDataOff;
   p->ws_total = pqhost::align_up(p->off_h + P * I * 2, 256);
@@ -628,7 +655,7 @@ int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& de
   static bool attr_set = false;
   if (!attr_set) {
     PQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)(160 * 1024 - sizeof(Route) - 64)));
+                                     (int)(160 * 1024 - kStaticLds)));
     attr_set = true;
   }
   int per_cu = 0;

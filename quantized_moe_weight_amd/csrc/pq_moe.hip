@@ -172,19 +172,31 @@ __device__ void route_token(const MoeArgs& a, Route& r, int m) {
 // Union of the routed experts in ascending expert id (the order does not
 // change any result: every h row and every y row is computed whole by one
 // wave, and each token's slots are combined in slot order), built in parallel
-// by one wave: lane p marks expert ids[p] in an LDS bitmap, the union index of
-// an expert is the number of marked ids below it, and a pair's place among the
-// pairs of its expert is the number of lower pairs with the same id.  An
-// expert given twice to one token is an error.
-__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, int tp, uint32_t* emask) {
+// by one wave with one LDS bitmap per token: lane p = (m, j) sets bit ids[p]
+// in token m's map; the union index of an expert is the number of experts
+// below it set in any map, a pair's place among the pairs of its expert is the
+// number of lower tokens whose map holds it.  An expert given twice to one
+// token is an error.
+__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint32_t (*tmask)[kMaxE / 32]) {
   const int lane = pq::lane_id();
   const int P = a.M * a.top_k;
   const bool act = lane < P;
   const int id = act ? r.ids[lane] : 0;
-  if (act) atomicOr(&emask[id >> 5], 1u << (id & 31));
+  const int m = act ? lane / a.top_k : 0;
+  const int w = id >> 5;
+  const uint32_t bit = 1u << (id & 31);
+  bool dup = false;
+  if (act) dup = (atomicOr(&tmask[m][w], bit) & bit) != 0u;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);       // LDS ops of one wave complete in order
   const int nw = (a.E + 31) >> 5;
-  const uint32_t word = lane < nw ? __hip_atomic_load(&emask[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
+  uint32_t word = 0u;                              // lane's word of the union bitmap
+  int n = 0, slot = 0;
+  for (int mm = 0; mm < a.M; ++mm) {
+    if (lane < nw) word |= __hip_atomic_load(&tmask[mm][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const int has = (__hip_atomic_load(&tmask[mm][w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & bit) != 0u;
+    n += has;
+    slot += mm < m ? has : 0;
+  }
   const int cnt = __popc(word);
   int incl = cnt;                                  // inclusive prefix over the bitmap words
 #pragma unroll
@@ -194,25 +206,15 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, int t
   }
   const int excl = incl - cnt;
   const int total = __shfl(incl, 31, pq::kWave);
-  const int w = id >> 5;
-  const int u = __shfl(excl, w, pq::kWave) + __popc((uint32_t)__shfl((int)word, w, pq::kWave) & ((1u << (id & 31)) - 1u));
-  int slot = 0, n = 0;
-  bool dup = false;
-  for (int q = 0; q < P; ++q) {
-    const int idq = __builtin_amdgcn_readlane(id, q);
-    if (idq == id) {
-      ++n;
-      if (q < lane) ++slot;
-      if (q != lane && q / a.top_k == lane / a.top_k) dup = true;
-    }
-  }
+  const int u = __shfl(excl, w, pq::kWave) + __popc((uint32_t)__shfl((int)word, w, pq::kWave) & (bit - 1u));
   if (act) {
-    if (slot == 0) {
+    // n <= M and slot < M; a duplicate shares its slot with the first copy
+    if (slot == 0 && !dup) {
       r.uexp[u] = id;
-      r.unp[u] = n < tp ? n : tp;
+      r.unp[u] = n;
     }
-    if (slot < tp) r.upairs[u][slot] = lane;
-    if ((slot >= tp || dup) && blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
+    if (!dup) r.upairs[u][slot] = lane;
+    if (dup && blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
   }
   if (lane == 0) r.nU = total;
 }
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Route route;
   __shared__ int s_last;
-  __shared__ uint32_t s_emask[kMaxE / 32];   // routed-expert bitmap
+  __shared__ uint32_t s_tmask[kMaxM][kMaxE / 32];   // routed-expert bitmap of each token
   __shared__ uint32_t s_next;     // next gate_up unit of this block
   __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
   __shared__ uint32_t s_epoch;    // value the release flags take in this call
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
     s_arrive = 0u;
     s_epoch = pq::ld_agent_u32(&hdr->epoch) + 1u;   // this call's flag value
   }
-  if (threadIdx.x < kMaxE / 32) s_emask[threadIdx.x] = 0u;
+  if (threadIdx.x < kMaxM * kMaxE / 32) (&s_tmask[0][0])[threadIdx.x] = 0u;
 
   // ---- A. routing (waves 0..M-1, one token each) -----------------------------
   if (a.routed) {
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   }
 
   __syncthreads();                            // routes and the quantised x visible
-  if (wv == 0) build_union(a, route, hdr, TP, s_emask);
+  if (wv == 0) build_union(a, route, hdr, s_tmask);
   __syncthreads();
   const int nU = ufl(route.nU);
 
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
 // ---------------------------------------------------------------------------
 // LDS the kernel declares statically (routing tables, expert bitmap, block
 // counters), reserved next to the dynamic area.
-constexpr size_t kStaticLds = sizeof(Route) + kMaxE / 8 + 256;
+constexpr size_t kStaticLds = sizeof(Route) + kMaxM * kMaxE / 8 + 256;
 
 struct MoePlan {
   size_t lds;

@@ -297,10 +297,10 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   // ---- B. live activation quantisation into LDS ------------------------------
   if (tq >= 0) {
     const int iters = (int)((totx8 + nq - 1) / nq);
-    for (int it = 0; it < iters; ++it) {
-      const long t = (long)it * nq + tq;
+    // 16 lanes share a scale, so whole waves run each step; the preloaded
+    // steps are unrolled so the raw values stay in registers
+    auto quant = [&](const uint4& raw, long t) {
       const bool valid = t < totx8;
-      const uint4 raw = it < kXPre ? xraw[it < kXPre ? it : 0] : pq::buf_load16(xr, valid ? (uint32_t)t * 16u : pq::kOOB);
       float v[8];
       pq::bf16x8_to_f32(raw, v);
       const float s = pq::fp8_block_scale16(v, valid);
@@ -308,6 +308,13 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
         reinterpret_cast<uint2*>(act)[t] = pq::fp8_codes8(v, s);
         if ((tq & 15) == 0) acts[(t * 8) / pq::kBlock] = s;
       }
+    };
+#pragma unroll
+    for (int it = 0; it < kXPre; ++it)
+      if (it < iters) quant(xraw[it], (long)it * nq + tq);
+    for (int it = kXPre; it < iters; ++it) {
+      const long t = (long)it * nq + tq;
+      quant(pq::buf_load16(xr, t < totx8 ? (uint32_t)t * 16u : pq::kOOB), t);
     }
   }
 

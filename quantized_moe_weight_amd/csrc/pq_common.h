@@ -250,15 +250,19 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Workspace layout shared by every kernel that synchronises across blocks:
-//   [0, 256)            WsHeader
-//   [256, kWsDataOff)   arrival counters (uint32), zero between calls
-//   [kWsDataOff, ...)   per-call scratch data (always written before read)
-// The counter region never moves, whatever the shape of the call, so a
-// counter address is only ever used as a counter and the zero-between-calls
-// invariant holds across calls of different shapes on one workspace.
+//   [0, 256)                   WsHeader
+//   [256, kWsZeroOff)          arrival counters (uint32), zero between calls
+//   [kWsZeroOff, kWsDataOff)   values exchanged between blocks whose zero
+//                              word means "not yet written", zero between calls
+//   [kWsDataOff, ...)          per-call scratch data (always written before read)
+// The regions never move, whatever the shape of the call, so the
+// zero-between-calls invariant holds across calls of different shapes and
+// different kernels on one workspace.
 constexpr size_t kWsCounterOff = 256;
-constexpr size_t kWsDataOff = 65536;
-constexpr size_t kWsMaxCounters = (kWsDataOff - kWsCounterOff) / 4;
+constexpr size_t kWsZeroOff = 65536;
+constexpr size_t kWsZeroBytes = (size_t)2 << 20;
+constexpr size_t kWsDataOff = kWsZeroOff + kWsZeroBytes;
+constexpr size_t kWsMaxCounters = (kWsZeroOff - kWsCounterOff) / 4;
 
 // Workspace header shared by the kernels that synchronise across blocks.
 struct WsHeader {

@@ -38,6 +38,7 @@
 // split, same reduction order), so a token's output in an M-token verify call
 // is bitwise equal to the same token decoded alone.
 #include <stdlib.h>
+#include <string.h>
 
 #include "pq_quant_dev.h"
 
@@ -70,11 +71,12 @@ struct MoeArgs {
   uint8_t* hq_dbg;
   float* hs_dbg;
   uint8_t* ws;
-  uint16_t* hbuf;   // [P][I] bf16
+  uint16_t* hbuf;   // [P][I] bf16 (stream kernel: bits inverted, zero between calls)
   int M, H, I, E, top_k;
   int routed;
   uint32_t spin_limit;
-  int ybuf_off;     // offset (in floats) of the per-block y buffer after the LDS scales
+  int xs_off, ha_off, hs_off, yb_off;   // byte offsets of the LDS regions
+  int alias;        // h codes and scales reuse the x region
 };
 
 struct Route {
@@ -83,10 +85,27 @@ struct Route {
   int uexp[kMaxUnion];            // expert id of union entry u
   int unp[kMaxUnion];             // number of (token, slot) pairs routed to u
   int upairs[kMaxUnion][kMaxM];   // their pair indices p = m * top_k + j, ascending
-  int nU;
+  int items[kMaxPairs];           // (entry u, pair slot t) = u | t << 8, in union order
+  int nU, nitems;
 };
 
 __device__ __forceinline__ int ufl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Claim the next index of a block counter in LDS.  Every lane of the (fully
+// active) wave adds 1, so the counter advances by 64 per claim and the claim
+// is the first lane's value before the add, divided by 64.  No lane-divergent
+// branch surrounds the atomic: a "lane 0 only" branch inside a loop may be
+// compiled into a divergent loop in which the lane that performed the add is
+// no longer the first active lane.
+__device__ __forceinline__ int wave_claim(uint32_t* p) {
+  const uint32_t r = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __builtin_amdgcn_readfirstlane((int)(r >> 6));
+}
+
+// true when either 16-bit half of w is zero
+__device__ __forceinline__ bool has_zero_half(uint32_t w) { return (w & 0xFFFFu) == 0u || (w >> 16) == 0u; }
 
 // total order on finite floats as unsigned keys (-0 and +0 are one key)
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -190,12 +209,22 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
   __atomic_signal_fence(__ATOMIC_SEQ_CST);       // LDS ops of one wave complete in order
   const int nw = (a.E + 31) >> 5;
   uint32_t word = 0u;                              // lane's word of the union bitmap
-  int n = 0, slot = 0;
+  int n = 0, slot = 0, below = 0, nitems = 0;      // below: pairs of lower experts
   for (int mm = 0; mm < a.M; ++mm) {
-    if (lane < nw) word |= __hip_atomic_load(&tmask[mm][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t wm = lane < nw ? __hip_atomic_load(&tmask[mm][lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0u;
+    word |= wm;
     const int has = (__hip_atomic_load(&tmask[mm][w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & bit) != 0u;
     n += has;
     slot += mm < m ? has : 0;
+    const int c = __popc(wm);
+    int inc = c;                                   // prefix popcount over token mm's words
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) {
+      const int v = __shfl_up(inc, d, pq::kWave);
+      if (lane >= d) inc += v;
+    }
+    below += __shfl(inc - c, w, pq::kWave) + __popc((uint32_t)__shfl((int)wm, w, pq::kWave) & (bit - 1u));
+    nitems += __shfl(inc, 31, pq::kWave);
   }
   const int cnt = __popc(word);
   int incl = cnt;                                  // inclusive prefix over the bitmap words
@@ -213,18 +242,81 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
       r.uexp[u] = id;
       r.unp[u] = n;
     }
-    if (!dup) r.upairs[u][slot] = lane;
+    if (!dup) {
+      r.upairs[u][slot] = lane;
+      r.items[below + slot] = u | slot << 8;
+    }
     if (dup && blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
   }
-  if (lane == 0) r.nU = total;
+  if (lane == 0) {
+    r.nU = total;
+    r.nitems = nitems;
+  }
+}
+
+// h of pair slot t of union entry uu: wait until every value is stored (none
+// reads as the zero word), then quantise it into LDS with the layout of the
+// activation quantiser (8 values per lane, 16 lanes per 128-value block).
+__device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq::WsHeader* hdr, int uu, int t,
+                                           uint8_t* ha, float* hsc) {
+  const int lane = pq::lane_id();
+  const int I = a.I;
+  const int p = ufl(r.upairs[uu][t]);
+  const int nvec = I / 8;
+  const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(a.M * a.top_k * I * 2));
+  constexpr int kSB = 4;
+  for (int v0 = 0; v0 < nvec; v0 += kSB * pq::kWave) {
+    uint4 raw[kSB];
+    for (uint32_t it = 0;; ++it) {
+      bool miss = false;
+#pragma unroll
+      for (int j = 0; j < kSB; ++j) {
+        const int idx = v0 + j * pq::kWave + lane;
+        const bool ok = idx < nvec;
+        raw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            hr, (int)(ok ? (uint32_t)(p * nvec + idx) * 16u : pq::kOOB), 0, kAuxSC1));
+        miss |= ok && (has_zero_half(raw[j].x) || has_zero_half(raw[j].y) ||
+                       has_zero_half(raw[j].z) || has_zero_half(raw[j].w));
+      }
+      if (__ballot(miss) == 0ull) break;
+      if (it >= a.spin_limit) {
+        if (lane == 0) pq::record_error(hdr, PQ_ERR_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int j = 0; j < kSB; ++j) {
+      const int idx = v0 + j * pq::kWave + lane;
+      const bool valid = idx < nvec;
+      const uint4 hv = make_uint4(~raw[j].x, ~raw[j].y, ~raw[j].z, ~raw[j].w);
+      float v[8];
+      pq::bf16x8_to_f32(hv, v);
+      const float sc = pq::fp8_block_scale16(v, valid);
+      if (valid) {
+        const int gi = p * nvec + idx;
+        const uint2 c8 = pq::fp8_codes8(v, sc);
+        reinterpret_cast<uint2*>(ha)[gi] = c8;
+        if ((lane & 15) == 0) hsc[gi / 16] = sc;
+        if (blockIdx.x == 0) {
+          if (a.hq_dbg) reinterpret_cast<uint2*>(a.hq_dbg)[gi] = c8;
+          if (a.hs_dbg && (lane & 15) == 0) a.hs_dbg[gi / 16] = sc;
+        }
+      }
+    }
+  }
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// The barrier kernel: all gate_up units of the call, then one grid-wide
+// release, then every block stages all of h and runs its down rows.  Fewer
+// instructions per step than the stream kernel below, which pays off when the
+// call streams few experts (one or two tokens).
 // TP: compile-time bound on the (token, slot) pairs routed to one expert in a
 // call (the smallest power of two >= M), so the per-pair loops unroll tightly.
 template <int TP>
-__global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
+__global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Route route;
   __shared__ int s_last;
@@ -248,9 +340,8 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   const uint32_t lane16 = 16u * (uint32_t)lane;
   const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
 
-  const size_t act_bytes = (size_t)a.M * H > (size_t)P * I ? (size_t)a.M * H : (size_t)P * I;
-  uint8_t* act = smem;                                                              // codes
-  float* acts = reinterpret_cast<float*>(smem + pqhost::align_up(act_bytes, 16));   // scales
+  uint8_t* act = smem;                                           // x codes, later h codes
+  float* acts = reinterpret_cast<float*>(smem + a.xs_off);       // their scales
 
   // ---- x loads first (independent of routing); the waves that do not route
   //      quantise x while waves 0..M-1 rank the logits ------------------------
@@ -342,9 +433,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   pq::rsrc_t gwr = pq::make_rsrc(a.w13, 0u), gsr = pq::make_rsrc(a.s13, 0u);
   auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], int& su_q, int& sch_q) {
     if (ic == nchH && more) {       // take the block's next unit
-      int u = 0;
-      if (lane == 0) u = bu0 + (int)atomicAdd(&s_next, 1u);
-      iunit = ufl(u);
+      iunit = bu0 + wave_claim(&s_next);
       ic = 0;
       more = iunit < bu1;
       if (more) {
@@ -450,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
       last = pq::atomic_add_relaxed(&hdr->done, rows) + rows == (uint32_t)gu_units;
     }
   }
-  if (ufl((int)last)) {
+  if (__builtin_amdgcn_readlane((int)last, 0)) {
     const uint32_t ep = s_epoch;
     for (int b = lane; b < (int)gridDim.x; b += pq::kWave) pq::st_agent_u32(flags + (size_t)b * kFlagStride, ep);
   }
@@ -468,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   const int v0 = ufl(pq::split_start(bunits, kWaves, wv));
   const int v1 = ufl(pq::split_start(bunits, kWaves, wv + 1));
   const int dsteps = (v1 - v0) * nchI;
-  float* ybuf = acts + a.ybuf_off;                 // [row_local][P] fp32
+  float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);   // [row_local][P] fp32
   uint4 wd[DD];
   float sd[DD];
   int ju = nrows > 0 ? v0 / nrows : 0;
@@ -622,49 +711,460 @@ __global__ __launch_bounds__(kThreads) void moe_layer_kernel(MoeArgs a) {
   }
 }
 
+// The stream kernel: no grid-wide barrier; see section C.
+// TP: compile-time bound on the (token, slot) pairs routed to one expert in a
+// call (the smallest power of two >= M), so the per-pair loops unroll tightly.
+template <int TP>
+__global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ Route route;
+  __shared__ int s_last;
+  __shared__ uint32_t s_tmask[kMaxM][kMaxE / 32];   // routed-expert bitmap of each token
+  __shared__ uint32_t s_iclaim;              // staging items of the block claimed
+  __shared__ uint32_t s_staged[kMaxUnion];  // pairs of union entry u whose h codes are in LDS
+  __shared__ uint32_t s_next;      // gate_up units of this block handed out
+  __shared__ uint32_t s_dnext;     // down units of this block handed out
+  __shared__ uint32_t s_gu_busy;   // waves still consuming gate_up steps
+
+  pq::WsHeader* hdr = reinterpret_cast<pq::WsHeader*>(a.ws);
+
+  const int lane = pq::lane_id();
+  const int wv = pq::wave_id();
+  const int H = a.H, I = a.I, K = a.top_k;
+  const int P = a.M * K;
+  const int nbH = H / pq::kBlock, nbI = I / pq::kBlock;
+  const int nchH = (H + pq::kChunk - 1) / pq::kChunk;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
+
+  uint8_t* xa = smem;                                          // x codes   [M][H]
+  float* xsc = reinterpret_cast<float*>(smem + a.xs_off);      // x scales  [M][H/128]
+  uint8_t* ha = smem + a.ha_off;                               // h codes   [P][I]
+  float* hsc = reinterpret_cast<float*>(smem + a.hs_off);      // h scales  [P][I/128]
+  float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);     // y partials [row][P]
+
+  // ---- x loads first (independent of routing); the waves that do not route
+  //      quantise x while waves 0..M-1 rank the logits ------------------------
+  const int nrt = a.routed ? a.M : 1;               // routing waves
+  const long totx8 = (long)a.M * H / 8;
+  // when the other waves cannot cover x in one pass, every wave takes a share
+  // (the routing waves after routing)
+  const bool xq_all = totx8 > (long)(kThreads - nrt * pq::kWave);
+  const int tq = xq_all ? (int)threadIdx.x : (int)threadIdx.x - nrt * pq::kWave;   // < 0: routing wave only
+  const int nq = xq_all ? kThreads : kThreads - nrt * pq::kWave;
+  const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
+  // enough loads in flight for the whole of x at H = 6144 up to M = 4 (16 bytes each)
+  constexpr int kXPre = TP == 1 ? 1 : TP == 2 ? 2 : TP == 4 ? 4 : 8;
+  uint4 xraw[kXPre];
+#pragma unroll
+  for (int it = 0; it < kXPre; ++it) {
+    const long t = (long)it * nq + tq;
+    xraw[it] = pq::buf_load16(xr, tq >= 0 && t < totx8 ? (uint32_t)t * 16u : pq::kOOB);
+  }
+
+  if (threadIdx.x == 0) {       // block counters; first used after the barriers below
+    s_next = 0u;
+    s_dnext = 0u;
+    s_iclaim = 0u;
+    s_gu_busy = (uint32_t)kWaves;
+  }
+  if (threadIdx.x < kMaxUnion) s_staged[threadIdx.x] = 0u;
+  if (threadIdx.x < kMaxM * kMaxE / 32) (&s_tmask[0][0])[threadIdx.x] = 0u;
+
+  // ---- A. routing (waves 0..M-1, one token each) -----------------------------
+  if (a.routed) {
+    if (wv < a.M) {
+      if (a.E <= 256) route_token<4>(a, route, wv);
+      else route_token<16>(a, route, wv);
+    }
+  } else if (wv == 0 && lane < P) {
+    int id = a.topk_ids[lane];
+    if (id < 0 || id >= a.E) {
+      if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
+      id = 0;
+    }
+    route.ids[lane] = id;
+    route.w[lane] = a.topk_w[lane];
+  }
+
+  // ---- B. live activation quantisation into LDS ------------------------------
+  if (tq >= 0) {
+    const int iters = (int)((totx8 + nq - 1) / nq);
+    // 16 lanes share a scale, so whole waves run each step; the preloaded
+    // steps are unrolled so the raw values stay in registers
+    auto quant = [&](const uint4& raw, long t) {
+      const bool valid = t < totx8;
+      float v[8];
+      pq::bf16x8_to_f32(raw, v);
+      const float s = pq::fp8_block_scale16(v, valid);
+      if (valid) {
+        reinterpret_cast<uint2*>(xa)[t] = pq::fp8_codes8(v, s);
+        if ((tq & 15) == 0) xsc[(t * 8) / pq::kBlock] = s;
+      }
+    };
+#pragma unroll
+    for (int it = 0; it < kXPre; ++it)
+      if (it < iters) quant(xraw[it], (long)it * nq + tq);
+    for (int it = kXPre; it < iters; ++it) {
+      const long t = (long)it * nq + tq;
+      quant(pq::buf_load16(xr, t < totx8 ? (uint32_t)t * 16u : pq::kOOB), t);
+    }
+  }
+
+  __syncthreads();                            // routes and the quantised x visible
+  if (wv == 0) build_union(a, route, hdr, s_tmask);
+  __syncthreads();
+  const int nU = ufl(route.nU);
+
+  // ---- C. per wave: gate_up units, then down units, no block barrier -------
+  // gate_up unit (union entry u, h-row i) = gate row i and up row i of expert
+  // u.  Unit k of this block is entry blockIdx.x + k * gridDim.x of the
+  // expert-major list, so every block works through the experts in union
+  // order and the h of the first experts is complete early.  down unit (u,
+  // output row n), n among this block's rows, taken expert by expert.  Waves
+  // take units from LDS counters (a wave whose loads issue later simply takes
+  // fewer); a wave out of gate_up units goes on with down units at once while
+  // other waves and other blocks still finish gate_up.  The h a down unit
+  // needs is quantised into LDS by the first wave that needs it (per pair),
+  // once every block has stored it: the stager polls the values themselves,
+  // which are stored bit-inverted so that a zero word means "not yet written".
+  const int G = (int)gridDim.x;
+  const int gu_total = nU * I;
+  const int r0 = pq::split_start(H, G, (int)blockIdx.x);
+  const int r1 = pq::split_start(H, G, (int)blockIdx.x + 1);
+  const int nrows = r1 - r0;
+  const int dn_total = nU * nrows;
+  const int nchI = (I + pq::kChunk - 1) / pq::kChunk;
+
+  // gate_up: a ring of DG steps (one 1 KB chunk of the gate row and of the up
+  // row); a slot descriptor holds valid (bit 31) | step | union entry | row.
+  {
+    uint4 wb[DG][2];
+    float sb[DG][2];
+    uint32_t sd[DG];
+    int ucur = 0, crow = 0, cstep = nchH, ce = -1;
+    bool more = true;
+    pq::rsrc_t wr = pq::make_rsrc(a.w13, 0u), sr = pq::make_rsrc(a.s13, 0u);
+    auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], uint32_t& d) {
+      if (cstep == nchH && more) {            // take the block's next unit
+        const int v = (int)blockIdx.x + wave_claim(&s_next) * G;
+        more = v < gu_total;
+        if (more) {
+          ucur = v / I;
+          crow = v - ucur * I;
+          cstep = 0;
+          const int e = ufl(route.uexp[ucur]);
+          if (e != ce) {
+            ce = e;
+            wr = pq::make_rsrc(a.w13 + (size_t)e * 2 * I * H, (uint32_t)(2 * I * H));
+            sr = pq::make_rsrc(a.s13 + (size_t)e * 2 * I * nbH, (uint32_t)(2 * I * nbH * 4));
+          }
+        }
+      }
+      const uint32_t kc = (uint32_t)(cstep * pq::kChunk);
+      const bool ok = more && kc + lane16 < (uint32_t)H;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t row = (uint32_t)(crow + j * I);
+        w[j] = pq::buf_load16_nt(wr, ok ? row * (uint32_t)H + kc + lane16 : pq::kOOB);
+        s[j] = pq::buf_load_f32_nt(sr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+      }
+      d = more ? 0x80000000u | ((uint32_t)cstep << 23) | ((uint32_t)ucur << 16) | (uint32_t)crow : 0u;
+      if (more) ++cstep;
+    };
+
+    float accg[TP], accu[TP];
+    int pr[TP], pm[TP];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) accg[t] = accu[t] = 0.0f;
+    int pairs_u = -1, cnp = 0;
+    auto consume_gu = [&](const uint4 (&w)[2], const float (&s)[2], uint32_t d) {
+      if (!(d >> 31)) return;
+      const int step = (int)((d >> 23) & 255u), uu = (int)((d >> 16) & 127u), row = (int)(d & 0xFFFFu);
+      if (uu != pairs_u) {
+        pairs_u = uu;
+        cnp = ufl(route.unp[uu]);
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          pr[t] = ufl(route.upairs[uu][t]);
+          pm[t] = pr[t] / K;
+        }
+      }
+      const uint32_t off = (uint32_t)(step * pq::kChunk) + lane16;
+      if (off < (uint32_t)H) {
+        const pq::Bf16x16 wg = pq::widen16(w[0]);
+        const pq::Bf16x16 wu = pq::widen16(w[1]);
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp) {
+            const pq::Bf16x16 xv = pq::widen16(*reinterpret_cast<const uint4*>(xa + (size_t)pm[t] * H + off));
+            const float xs = xsc[pm[t] * nbH + off / pq::kBlock];
+            accg[t] = fmaf(pq::dot16(wg, xv), s[0] * xs, accg[t]);
+            accu[t] = fmaf(pq::dot16(wu, xv), s[1] * xs, accu[t]);
+          }
+        }
+      }
+      if (step == nchH - 1) {            // unit done: h for every token routed to u
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp) {
+            const float g = pq::wave_sum(accg[t]);
+            const float u = pq::wave_sum(accu[t]);
+            if (lane == 0) {
+              uint16_t hb = pq::bf16_rne(silu_mul(g, u));
+              if (hb == 0xFFFFu) hb = 0xFFC0u;         // keep the inverted word non-zero
+              pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + row, (uint16_t)~hb);
+              if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + row] = hb;
+            }
+          }
+          accg[t] = accu[t] = 0.0f;
+        }
+      }
+    };
+
+#pragma unroll
+    for (int q = 0; q < DG; ++q) issue_gu(wb[q], sb[q], sd[q]);
+    for (;;) {
+#pragma unroll
+      for (int q = 0; q < DG; ++q) {
+        consume_gu(wb[q], sb[q], sd[q]);
+        issue_gu(wb[q], sb[q], sd[q]);
+      }
+      uint32_t busy = 0u;
+#pragma unroll
+      for (int q = 0; q < DG; ++q) busy |= sd[q];
+      if (busy == 0u) break;
+    }
+  }
+  if (lane == 0) atomicSub(&s_gu_busy, 1u);   // this wave no longer reads x
+
+  // h staging: the (entry, pair) items of the block are quantised into LDS in
+  // union order, each by the wave that claims it; a wave out of gate_up units
+  // claims items until none is left, then goes on with down units.
+  {
+    const int nitems = ufl(route.nitems);
+    for (;;) {
+      const int jj = wave_claim(&s_iclaim);
+      if (jj >= nitems) break;
+      const int it = ufl(route.items[jj]);
+      const int v = it & 255, t = it >> 8;
+      if (a.alias) {             // h codes overwrite x codes: the block must be past gate_up
+        while (ufl((int)__hip_atomic_load(&s_gu_busy, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0)
+          __builtin_amdgcn_s_sleep(1);
+      }
+      stage_pair(a, route, hdr, v, t, ha, hsc);
+      if (lane == 0) __hip_atomic_fetch_add(&s_staged[v], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+
+  // down: a ring of DD steps (one 1 KB chunk of a down row); a cycle's slots
+  // are consumed once the h of their union entries is in LDS.
+  {
+    uint4 wd[DD];
+    float sw[DD];
+    uint32_t sd[DD];
+    int ucur = 0, crow = 0, cstep = nchI, ce = -1;
+    bool more = true;
+    pq::rsrc_t wr = pq::make_rsrc(a.w2, 0u), sr = pq::make_rsrc(a.s2, 0u);
+    auto issue_dn = [&](uint4& w, float& s, uint32_t& d) {
+      if (cstep == nchI && more) {            // take the block's next unit
+        const int tt = wave_claim(&s_dnext);
+        more = tt < dn_total;
+        if (more) {
+          ucur = tt / nrows;
+          crow = tt - ucur * nrows;
+          cstep = 0;
+          const int e = ufl(route.uexp[ucur]);
+          if (e != ce) {
+            ce = e;
+            wr = pq::make_rsrc(a.w2 + (size_t)e * H * I, (uint32_t)(H * I));
+            sr = pq::make_rsrc(a.s2 + (size_t)e * H * nbI, (uint32_t)(H * nbI * 4));
+          }
+        }
+      }
+      const uint32_t kc = (uint32_t)(cstep * pq::kChunk);
+      const bool ok = more && kc + lane16 < (uint32_t)I;
+      const uint32_t row = (uint32_t)(r0 + crow);
+      w = pq::buf_load16_nt(wr, ok ? row * (uint32_t)I + kc + lane16 : pq::kOOB);
+      s = pq::buf_load_f32_nt(sr, ok ? (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+      d = more ? 0x80000000u | ((uint32_t)cstep << 23) | ((uint32_t)ucur << 16) | (uint32_t)crow : 0u;
+      if (more) ++cstep;
+    };
+
+    float acc[TP];
+    int pr[TP];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
+    int pairs_u = -1, cnp = 0, ready_next = 0;
+    auto consume_dn = [&](const uint4& w, float s, uint32_t d) {
+      if (!(d >> 31)) return;
+      const int step = (int)((d >> 23) & 255u), uu = (int)((d >> 16) & 127u), row = (int)(d & 0xFFFFu);
+      if (uu != pairs_u) {
+        pairs_u = uu;
+        cnp = ufl(route.unp[uu]);
+#pragma unroll
+        for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[uu][t]);
+      }
+      const uint32_t off = (uint32_t)(step * pq::kChunk) + lane16;
+      if (off < (uint32_t)I) {
+        const pq::Bf16x16 wv2 = pq::widen16(w);
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp) {
+            const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(ha + (size_t)pr[t] * I + off));
+            const float hs = hsc[pr[t] * nbI + off / pq::kBlock];
+            acc[t] = fmaf(pq::dot16(wv2, hv), s * hs, acc[t]);
+          }
+        }
+      }
+      if (step == nchI - 1) {             // unit (u, row) done
+#pragma unroll
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp) {
+            const float y = pq::wave_sum(acc[t]);
+            if (lane == 0) ybuf[row * P + pr[t]] = y;
+          }
+          acc[t] = 0.0f;
+        }
+      }
+    };
+    // wait until the h of union entry uu is in LDS (its stagers poll with a
+    // bounded wait, so this ends)
+    auto wait_staged = [&](int uu) {
+      const uint32_t n = (uint32_t)ufl(route.unp[uu]);
+      while ((uint32_t)ufl((int)__hip_atomic_load(&s_staged[uu], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < n)
+        __builtin_amdgcn_s_sleep(1);
+    };
+
+#pragma unroll
+    for (int q = 0; q < DD; ++q) issue_dn(wd[q], sw[q], sd[q]);
+    for (;;) {
+      int lo = nU, hi = -1;
+#pragma unroll
+      for (int q = 0; q < DD; ++q) {
+        if (sd[q] >> 31) {
+          const int uu = (int)((sd[q] >> 16) & 127u);
+          lo = uu < lo ? uu : lo;
+          hi = uu > hi ? uu : hi;
+        }
+      }
+      for (int uu = lo > ready_next ? lo : ready_next; uu <= hi; ++uu) wait_staged(uu);
+      ready_next = hi + 1 > ready_next ? hi + 1 : ready_next;
+#pragma unroll
+      for (int q = 0; q < DD; ++q) {
+        consume_dn(wd[q], sw[q], sd[q]);
+        issue_dn(wd[q], sw[q], sd[q]);
+      }
+      uint32_t busy = 0u;
+#pragma unroll
+      for (int q = 0; q < DD; ++q) busy |= sd[q];
+      if (busy == 0u) break;
+    }
+  }
+
+  // ---- D. weighted combine of each token's slots, in slot order --------------
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nrows * a.M; idx += kThreads) {
+    const int rl = idx / a.M, m = idx - (idx / a.M) * a.M;
+    float o = 0.0f;
+    for (int j = 0; j < K; ++j) o = fmaf(route.w[m * K + j], ybuf[rl * P + m * K + j], o);
+    a.out[(size_t)m * H + r0 + rl] = pq::bf16_rne(o);
+  }
+
+  // ---- E. the last block to finish clears h for the next call ----------------
+  // Every block is done reading h when it counts itself out; the waits make
+  // its own h stores complete first.
+  pq::wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = pq::atomic_add_relaxed(&hdr->exit_count, 1u);
+    s_last = old == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (s_last) {
+    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P * I * 2));
+    const int nz = P * I / 8;
+    for (int t = threadIdx.x; t < nz; t += kThreads)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, hr, t * 16, 0, kAuxSC1);
+    if (threadIdx.x == 0) pq::atomic_store_relaxed(&hdr->exit_count, 0u);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-// LDS the kernel declares statically (routing tables, expert bitmap, block
+// LDS the kernel declares statically (routing tables, expert bitmaps, block
 // counters), reserved next to the dynamic area.
-constexpr size_t kStaticLds = sizeof(Route) + kMaxM * kMaxE / 8 + 256;
+constexpr size_t kStaticLds = sizeof(Route) + kMaxM * kMaxE / 8 + kMaxUnion * 4 + 256;
+constexpr size_t kLdsBytes = 160 * 1024;
 
 struct MoePlan {
   size_t lds;
-  int ybuf_off;
+  int xs_off, ha_off, hs_off, yb_off, alias;
   size_t off_h, ws_total;
 };
 
-// num_cus bounds the rows a block can own (the grid has at least one block per
-// CU); num_cus <= 0 checks the shape and sizes the workspace only.
-int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, MoePlan* p) {
+// Which kernel runs a call: the barrier kernel for one or two tokens, the
+// stream kernel from three on (measured crossover at H = 6144, I = 2048,
+// 256 experts, top-8); PQ_MOE_PATH=barrier|stream overrides.
+enum { kPathBarrier = 0, kPathStream = 1 };
+int moe_path(int M) {
+  const char* e = getenv("PQ_MOE_PATH");
+  if (e && strcmp(e, "barrier") == 0) return kPathBarrier;
+  if (e && strcmp(e, "stream") == 0) return kPathStream;
+  return M <= 2 ? kPathBarrier : kPathStream;
+}
+
+// num_cus bounds the rows a block can own (the grid has one block per CU);
+// num_cus <= 0 checks the shape and sizes the workspace only.  The stream
+// kernel gives x and h separate LDS regions when both fit (a wave may stage h
+// while others still read x); otherwise, and always in the barrier kernel,
+// h reuses the x region once the block is past gate_up.  The workspace covers
+// both kernels: the stream kernel's h in the zero-between-calls region, the
+// barrier kernel's in the data region.
+int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePlan* p) {
   if (M < 1 || M > kMaxM || top_k < 1 || top_k > kMaxTopK || E < top_k || E > kMaxE) return PQ_ERR_SHAPE;
   if (H < pq::kBlock || H % pq::kBlock || H > 16384 || I < pq::kBlock || I % pq::kBlock || I > 16384)
     return PQ_ERR_SHAPE;
   const size_t P = (size_t)M * top_k;
-  const size_t nbI = I / pq::kBlock;
   if ((size_t)2 * I * H > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
-  const size_t act = (size_t)M * H > P * I ? (size_t)M * H : P * I;
-  const size_t nsc = (size_t)M * H / pq::kBlock > P * nbI ? (size_t)M * H / pq::kBlock : P * nbI;
-  p->ybuf_off = (int)nsc;
+  if (P * I * 2 > pq::kWsZeroBytes) return PQ_ERR_SHAPE;
+  const size_t xb = pqhost::align_up((size_t)M * H, 16), xsb = pqhost::align_up((size_t)M * (H / pq::kBlock) * 4, 16);
+  const size_t hb = pqhost::align_up(P * I, 16), hsb = pqhost::align_up(P * (I / pq::kBlock) * 4, 16);
   p->lds = 0;
+  p->xs_off = (int)xb;
+  p->alias = 0;
   if (num_cus > 0) {
-    const size_t rows_max = ((size_t)H + num_cus - 1) / num_cus;
-    p->lds = pqhost::align_up(act, 16) + (nsc + rows_max * P) * 4;
-    if (p->lds + kStaticLds > 160 * 1024) return PQ_ERR_SHAPE;
+    const size_t yb = ((size_t)H + num_cus - 1) / num_cus * P * 4;
+    const size_t sep = xb + xsb + hb + hsb + yb;
+    if (path == kPathStream && sep + kStaticLds <= kLdsBytes) {
+      p->ha_off = (int)(xb + xsb);
+      p->hs_off = (int)(xb + xsb + hb);
+      p->yb_off = (int)(xb + xsb + hb + hsb);
+      p->lds = sep;
+    } else {
+      const size_t cb = xb > hb ? xb : hb, sb = xsb > hsb ? xsb : hsb;
+      p->alias = 1;
+      p->xs_off = (int)cb;
+      p->ha_off = 0;
+      p->hs_off = (int)cb;
+      p->yb_off = (int)(cb + sb);
+      p->lds = cb + sb + yb;
+      if (p->lds + kStaticLds > kLdsBytes) return PQ_ERR_SHAPE;
+    }
   }
-  p->off_h = pq::kWsDataOff;
-  p->ws_total = pqhost::align_up(p->off_h + P * I * 2, 256);
+  p->off_h = path == kPathStream ? pq::kWsZeroOff : pq::kWsDataOff;
+  p->ws_total = pqhost::align_up(pq::kWsDataOff + P * I * 2, 256);
   return PQ_OK;
 }
 
-template <int TP>
+template <int TP, bool STREAM>
 int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& dev, hipStream_t stream) {
-  auto kern = moe_layer_kernel<TP>;
+  auto kern = STREAM ? moe_stream_kernel<TP> : moe_barrier_kernel<TP>;
   static bool attr_set = false;
   if (!attr_set) {
     PQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)(160 * 1024 - kStaticLds)));
+                                     (int)(kLdsBytes - kStaticLds)));
     attr_set = true;
   }
   int per_cu = 0;
@@ -673,10 +1173,15 @@ int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& de
   // one block per CU (blocks wait on each other, so all must be resident; one
   // per CU also keeps the per-block staging of h to one copy per CU)
   const int grid = dev.num_cus;
-  if ((size_t)grid * kFlagStride * 4 > pq::kWsDataOff - pq::kWsCounterOff) return PQ_ERR_UNSUPPORTED;
+  if (!STREAM && (size_t)grid * kFlagStride * 4 > pq::kWsZeroOff - pq::kWsCounterOff) return PQ_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), pl.lds, stream, a);
   PQ_HIP_CHECK(hipGetLastError());
   return PQ_OK;
+}
+
+template <int TP>
+int launch_moe_path(int path, const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& dev, hipStream_t s) {
+  return path == kPathStream ? launch_moe<TP, true>(a, pl, dev, s) : launch_moe<TP, false>(a, pl, dev, s);
 }
 
 }  // namespace
@@ -685,7 +1190,7 @@ extern "C" {
 
 size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k) {
   MoePlan pl;
-  if (moe_plan(M, H, I, E, top_k, 0, &pl) != PQ_OK) return 0;
+  if (moe_plan(M, H, I, E, top_k, 0, kPathStream, &pl) != PQ_OK) return 0;
   return pl.ws_total;
 }
 
@@ -695,7 +1200,8 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
                      float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !topk_ids || !topk_w || !w13 || !s13 || !w2 || !s2 || !out || !ws) return PQ_ERR_NULL;
   MoePlan pl;
-  int st = moe_plan(M, H, I, E, top_k, 0, &pl);       // shape checks (device independent)
+  const int path = moe_path(M);
+  int st = moe_plan(M, H, I, E, top_k, 0, path, &pl);   // shape checks (device independent)
   if (st != PQ_OK) return st;
   const void* ptrs[] = {x, router_logits, topk_ids, topk_w, w13, s13, w2, s2, out, h_dbg, hq_dbg, hs_dbg, ws};
   for (const void* q : ptrs)
@@ -704,7 +1210,7 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
   pqhost::DeviceInfo dev;
   st = pqhost::current_device_info(&dev);
   if (st != PQ_OK) return st;
-  st = moe_plan(M, H, I, E, top_k, dev.num_cus, &pl);
+  st = moe_plan(M, H, I, E, top_k, dev.num_cus, path, &pl);
   if (st != PQ_OK) return st;
 
   MoeArgs a;
@@ -716,15 +1222,16 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
   a.M = M; a.H = H; a.I = I; a.E = E; a.top_k = top_k;
   a.routed = router_logits != nullptr;
   a.spin_limit = kSpinLimit;
-  a.ybuf_off = pl.ybuf_off;
+  a.xs_off = pl.xs_off; a.ha_off = pl.ha_off; a.hs_off = pl.hs_off; a.yb_off = pl.yb_off;
+  a.alias = pl.alias;
   const char* lim = getenv("PQ_SPIN_LIMIT");
   if (lim && *lim) a.spin_limit = (uint32_t)strtoul(lim, nullptr, 10);
 
   hipStream_t s = (hipStream_t)stream;
-  if (M == 1) return launch_moe<1>(a, pl, dev, s);
-  if (M == 2) return launch_moe<2>(a, pl, dev, s);
-  if (M <= 4) return launch_moe<4>(a, pl, dev, s);
-  return launch_moe<8>(a, pl, dev, s);
+  if (M == 1) return launch_moe_path<1>(path, a, pl, dev, s);
+  if (M == 2) return launch_moe_path<2>(path, a, pl, dev, s);
+  if (M <= 4) return launch_moe_path<4>(path, a, pl, dev, s);
+  return launch_moe_path<8>(path, a, pl, dev, s);
 }
 
 }  // extern "C"

@@ -31,6 +31,19 @@ def pq():
     return pq
 
 
+@pytest.fixture(params=["barrier", "stream"])
+def path(request):
+    """Run the test with each of the two layer kernels (the library picks one
+    by token count; PQ_MOE_PATH forces it)."""
+    old = os.environ.get("PQ_MOE_PATH")
+    os.environ["PQ_MOE_PATH"] = request.param
+    yield request.param
+    if old is None:
+        del os.environ["PQ_MOE_PATH"]
+    else:
+        os.environ["PQ_MOE_PATH"] = old
+
+
 class Bank:
     """Expert bank with only the experts a test routes to filled in.
 
@@ -85,7 +98,7 @@ def _check(pq, bank, x_bits, res, ref, M, k):
 
 @pytest.mark.parametrize("M,E,H,I,k", [(1, 16, 512, 256, 4), (2, 16, 640, 384, 4), (3, 24, 1024, 512, 8),
                                        (8, 32, 1024, 256, 8)])
-def test_moe_small_routed(pq, M, E, H, I, k):
+def test_moe_small_routed(pq, path, M, E, H, I, k):
     import torch
     bank = Bank(pq, E, H, I, seed=M)
     x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=M)
@@ -99,7 +112,7 @@ def test_moe_small_routed(pq, M, E, H, I, k):
     _check(pq, bank, x, res, ref, M, k)
 
 
-def test_moe_given_routing_with_shared_experts(pq):
+def test_moe_given_routing_with_shared_experts(pq, path):
     import torch
     M, E, H, I, k = 4, 12, 512, 256, 3
     bank = Bank(pq, E, H, I, seed=9)
@@ -133,9 +146,39 @@ def test_moe_rows_bitwise_independent_of_M(pq):
         assert torch.equal(one["topk_w"][0], full["topk_w"][m])
 
 
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M):
+    """Both layer kernels compute every h row and every output row with the same
+    lane split and reduction order, so their results are bitwise equal."""
+    import torch
+    E, H, I, k = 24, 1024, 512, 8
+    bank = Bank(pq, E, H, I, seed=20 + M)
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=20 + M)
+    lg = workloads.verify_logits(M, E, workload=workloads.MOE_LAYER, seed=20 + M)
+    bank.fill(oracle.route_topk(lg, k)[0])
+    xt, lt = np_bf16_bits_to_torch(x), torch.from_numpy(lg).cuda()
+    res = {}
+    old = os.environ.get("PQ_MOE_PATH")
+    try:
+        for p in ("barrier", "stream"):
+            os.environ["PQ_MOE_PATH"] = p
+            res[p] = pq.moe_decode_layer(xt, bank.w13, bank.s13, bank.w2, bank.s2, logits=lt, top_k=k, debug=True)
+            assert pq.workspace_check() == 0
+    finally:
+        if old is None:
+            del os.environ["PQ_MOE_PATH"]
+        else:
+            os.environ["PQ_MOE_PATH"] = old
+    a, b = res["barrier"], res["stream"]
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+    assert torch.equal(a["h"].view(torch.int16), b["h"].view(torch.int16))
+    assert torch.equal(a["hq"], b["hq"]) and torch.equal(a["hs"], b["hs"])
+
+
 def test_moe_deterministic_and_workspace_reuse(pq):
     """Repeated calls are bitwise identical, also interleaved with calls of other
-    shapes on the same workspace (counters must be left at zero)."""
+    shapes on the same workspace (counters and the h exchange region must be
+    left at zero; M = 1, 2 run the barrier kernel, M = 5 the stream kernel)."""
     import torch
     E, H, I, k = 16, 512, 256, 4
     bank = Bank(pq, E, H, I, seed=5)
@@ -156,7 +199,7 @@ def test_moe_deterministic_and_workspace_reuse(pq):
     assert pq.workspace_check() == 0
 
 
-def test_moe_bad_expert_id_is_reported(pq):
+def test_moe_bad_expert_id_is_reported(pq, path):
     import torch
     E, H, I = 8, 256, 128
     bank = Bank(pq, E, H, I, seed=6)
@@ -169,7 +212,7 @@ def test_moe_bad_expert_id_is_reported(pq):
     assert pq.workspace_check() == 0          # the record is cleared
 
 
-def test_moe_watchdog_reports_timeout_and_next_call_is_clean(pq):
+def test_moe_watchdog_reports_timeout_and_next_call_is_clean(pq, path):
     """A zero spin budget (set from the host) makes waiting blocks give up
     instead of waiting: the call still ends, the timeout is reported, and the
     next call with the normal budget is correct."""
@@ -193,7 +236,7 @@ def test_moe_watchdog_reports_timeout_and_next_call_is_clean(pq):
 
 
 @pytest.mark.parametrize("M", [1, 4])
-def test_moe_full_size_layer(pq, M):
+def test_moe_full_size_layer(pq, path, M):
     """256 experts, hidden 6144, intermediate 2048, top-8: the routed MoE layer at
     its real shape (M=1) and a 4-token verify call, every output checked."""
     import torch
@@ -209,7 +252,7 @@ def test_moe_full_size_layer(pq, M):
     assert pq.workspace_check() == 0
     ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=shp.top_k)
     worst = _check(pq, bank, x, res, ref, M, shp.top_k)
-    print(f"full-size M={M}: union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
+    print(f"full-size M={M} ({path}): union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
 
 
 @pytest.mark.parametrize("E", [16, 200, 256, 1000])

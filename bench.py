@@ -35,11 +35,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNEL_NAME = "moe_layer_kernel"
+KERNEL_NAME = "moe_barrier_kernel"   # the layer kernel of the batch-1 workload (the counters are its)
 MOE_SRC = os.path.join(ROOT, "quantized_moe_weight_amd", "csrc", "pq_moe.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "moe_layer_kernel_e256_h6144_i2048_m1.pmc.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "moe_barrier_kernel_e256_h6144_i2048_m1.pmc.txt")
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written per dispatch
 METRIC = "achieved HBM GB/s (% of 8 TB/s) + µs/layer, batch-1 top-8 FP8 MoE GEMV"
+
+
+def layer_kernel_name(M: int) -> str:
+    """The kernel the library runs for an M-token call (one or two tokens: the
+    barrier kernel; more: the stream kernel; PQ_MOE_PATH overrides)."""
+    p = os.environ.get("PQ_MOE_PATH", "")
+    if p in ("barrier", "stream"):
+        return f"moe_{p}_kernel"
+    return "moe_barrier_kernel" if M <= 2 else "moe_stream_kernel"
 
 
 def kernel_source_sha() -> str:
@@ -212,7 +221,7 @@ def run(args):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else int(traffic),
-            "kernel": KERNEL_NAME,
+            "kernel": layer_kernel_name(M),
             "mean_launch_us": round(mean_launch_s * 1e6, 2),
         },
         "setup_s": round(setup_s, 1),

@@ -179,7 +179,13 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k);
  * Constraints: 1 <= M <= 8, 1 <= top_k <= 8, top_k <= E <= 1024,
  * H % 128 == 0, I % 128 == 0, 128 <= H <= 16384, 128 <= I <= 16384.
  * Router logits must be finite.  The kernel needs the whole GPU while it runs
- * (its blocks wait on each other; a bounded wait records PQ_ERR_TIMEOUT). */
+ * (its blocks wait on each other; a bounded wait records PQ_ERR_TIMEOUT).
+ * Two kernels implement the call with bitwise equal results: for M <= 2 one
+ * that releases the down projection with a grid-wide barrier, for M >= 3 one
+ * without (the environment variable PQ_MOE_PATH=barrier|stream forces one).
+ * The workspace (zeroed once by pq_workspace_init) may be shared with the
+ * other entry points; the call leaves its counters and its h exchange region
+ * at zero, as it found them. */
 int moe_decode_layer(const uint16_t* x, int M, int H,
                      const float* router_logits,
                      int32_t* topk_ids, float* topk_w,

@@ -20,6 +20,7 @@ Reported (one JSON line):
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m M]
+       python bench.py --workload gemv_small|gate_up|q4_stack [--m M] [--steps K]   (dense configurations)
        python bench.py --ingest-pmc FETCH.csv WRITE.csv   (writes the counter summary)
 """
 from __future__ import annotations
@@ -121,6 +122,28 @@ def cpu_baseline(shp, x_bits, lg, budget_s=12.0):
             break
     dt = (time.perf_counter() - t0) / reps
     return dt, reps, cores, res, len(experts)
+
+
+def measure_read_peak(pq, nbytes=4 << 30, reps=10):
+    """Achievable HBM read bandwidth (GB/s, median of reps) of the weight-stream
+    load path, from the library's streaming-read probe over nbytes."""
+    import numpy as np
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pq.stream_probe(src, sink)
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pq.stream_probe(src, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del src
+    return nbytes / float(np.median(ts)) / 1e9
 
 
 def run(args):
@@ -226,6 +249,16 @@ def run(args):
         },
         "setup_s": round(setup_s, 1),
     }
+    q10, q50, q90 = np.percentile(per_launch_ms, [10, 50, 90]) * 1e3
+    out["roofline"]["launch_us_p10_p50_p90"] = [round(float(q10), 2), round(float(q50), 2), round(float(q90), 2)]
+    if traffic is not None:
+        out["roofline"]["achieved_hbm_traffic_gbs"] = round(traffic / mean_launch_s / 1e9, 1)
+    peak_meas = measure_read_peak(pq)
+    out["measured_read_peak"] = {
+        "value": round(peak_meas, 1), "unit": "GB/s",
+        "how": "pq_stream_probe over 4 GiB (128-bit non-temporal loads, one block per CU), median of 10",
+        "frac_achieved": round(achieved / peak_meas, 4),
+    }
     if M > 1:
         out["config"]["bytes_per_token"] = int(bytes_per_launch / M)
         out["config"]["bytes_per_accepted_token_L3.5"] = int(bytes_per_launch / 3.5)
@@ -248,6 +281,132 @@ def run(args):
             "seconds_per_call": round(dt, 3),
         }
         out["parity_check"] = {"max_err_over_S": rel, "bound": 2e-3, "ok": rel <= 2e-3}
+    print(json.dumps(out), flush=True)
+
+
+def run_dense(args):
+    """The dense configurations: FP8 GEMV 512->256 (launch bound), one expert's
+    gate_up 6144->2x2048 with SiLU*up, and the int4 g32 stack of 64 blocks x 3
+    linears (5120->5120, 5120->2x17408 SiLU*up, 17408->5120).  Weights rotate
+    over distinct copies (>= 2 GB) or form a 10.57 GB stack so no cache serves
+    them; every launch is timed with HIP events on the launch stream."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import quantized_moe_weight_amd as pq
+    import workloads
+    torch.cuda.set_device(0)
+    lib = pq.lib()
+    M = args.m
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+    def xbits(K, wl, seed=0):
+        xb = workloads.activation_bf16(M, K, workload=wl, seed=seed, outliers=0 if wl == workloads.Q4_STACK else 2)
+        return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).cuda()
+
+    launches = []      # (callable, bytes)
+    if args.workload in ("gemv_small", "gate_up"):
+        if args.workload == "gemv_small":
+            K, N, epi, wl, desc = 512, 256, 0, workloads.FP8_GEMV_SMALL, "FP8 GEMV 512->256"
+        else:
+            K, N, epi, wl, desc = 6144, 4096, 1, workloads.FP8_GATE_UP, "FP8 expert gate_up 6144->2x2048 + SiLU*up"
+        m = workloads.master_weights_torch(N, K, workload=wl)
+        q, sc = pq.quantize_fp8(m)
+        per = q.numel() + sc.numel() * 4
+        copies = max(80, int(np.ceil((2 << 30) / per)))
+        W = q.unsqueeze(0).expand(copies, -1, -1).contiguous()
+        S = sc.unsqueeze(0).expand(copies, -1, -1).contiguous()
+        del m
+        x = xbits(K, wl)
+        n_out = N // 2 if epi else N
+        y = torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda")
+        nb = int(lib.pq_gemv_fp8_workspace(M, K, N, epi))
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+        lib.pq_workspace_init(P(ws), ws.numel(), st)
+        io = 2 * M * K + 2 * M * n_out
+        for c in range(copies):
+            wp, sp = P(W[c]), P(S[c])
+            launches.append((lambda wp=wp, sp=sp: lib.pq_gemv_fp8(P(x), M, K, wp, sp, N, epi, P(y), None, None,
+                                                                   P(ws), ws.numel(), st), per + io))
+        kernel, unit = "gemv_fp8_kernel", "call"
+        config = {"workload": f"{desc}, M={M}, E4M3 weights + fp32 block-128 scales, live FP8 act quant, "
+                              f"{copies} weight copies rotated", "M": M, "K": K, "N": N, "epilogue": "silu_mul" if epi else "none"}
+    elif args.workload == "q4_stack":
+        layers = []
+        for blk in range(64):
+            for j, (K, N, silu) in enumerate(workloads.Q4_SHAPES):
+                m = workloads.master_weights_torch(N, K, workload=workloads.Q4_STACK, tensor=workloads.T_W,
+                                                   expert=blk * 3 + j)
+                q, sc = pq.quantize_q4(m)
+                del m
+                layers.append((K, N, 1 if silu else 0, q, sc))
+        torch.cuda.synchronize()
+        xs = {K: xbits(K, workloads.Q4_STACK) for K in (5120, 17408)}
+        ys = {}
+        nb = max(int(lib.pq_gemv_q4_workspace(M, K, N, e)) for K, N, e, _, _ in layers[:3])
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
+        lib.pq_workspace_init(P(ws), ws.numel(), st)
+        for K, N, e, q, sc in layers:
+            n_out = N // 2 if e else N
+            y = ys.setdefault((n_out,), torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda"))
+            b = q.numel() + sc.numel() * 2 + 2 * M * K + 2 * M * n_out
+            launches.append((lambda K=K, N=N, e=e, q=q, sc=sc, y=y: lib.pq_gemv_q4(
+                P(xs[K]), M, K, P(q), P(sc), N, e, P(y), P(ws), ws.numel(), st), b))
+        kernel, unit = "gemv_q4 kernels", "stack pass (192 linears)"
+        config = {"workload": f"int4 g32 W4A16 decode stack, M={M}: 64 blocks x (5120->5120, 5120->2x17408 SiLU*up, "
+                              "17408->5120), fp16 group scales, 10.57 GB", "M": M, "linears": len(launches)}
+    else:
+        raise SystemExit(f"unknown workload {args.workload}")
+
+    n = len(launches)
+    for i in range(min(n, 2 * args.warmup + n // 4)):
+        launches[i % n][0]()
+    torch.cuda.synchronize()
+    K_steps = args.steps
+    total = K_steps if args.workload != "q4_stack" else K_steps * n
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    byts = 0
+    stride = 1 if args.workload == "q4_stack" else max(1, n // total) | 1   # spread the steps over every copy
+    for i in range(total):
+        fn, b = launches[(i * stride) % n]
+        ev[i][0].record()
+        rc = fn()
+        ev[i][1].record()
+        if rc != 0:
+            raise RuntimeError(f"launch returned {rc}")
+        byts += b
+    t1.record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+    wall = t0.elapsed_time(t1) * 1e-3
+    passes = K_steps
+    kern_s = per.sum() / passes
+    bytes_per_pass = byts / passes
+    achieved = bytes_per_pass / kern_s / 1e9
+    q10, q50, q90 = np.percentile(per, [10, 50, 90]) * 1e6
+    out = {
+        "metric": "achieved HBM GB/s (% of 8 TB/s) + µs per " + unit,
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": passes, "warmup": args.warmup,
+        "ms_per_step": round(kern_s * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3" if args.workload != "q4_stack" else "int4g32xbf16", "data": "synthetic",
+        "config": config,
+        "us_per_" + ("call" if unit == "call" else "pass"): round(kern_s * 1e6, 2),
+        "wall_us_per_step_with_host_gaps": round(wall / passes * 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kernel,
+                     "launch_us_p10_p50_p90": [round(float(q10), 2), round(float(q50), 2), round(float(q90), 2)],
+                     "bytes_per_step": int(bytes_per_pass)},
+    }
+    if args.workload == "q4_stack":
+        per_shape = per.reshape(passes, n)
+        out["per_linear_median_us"] = {f"{K}->{N}{' silu' if e else ''}": round(float(np.median(per_shape[:, j::3])) * 1e6, 2)
+                                       for j, (K, N, e, _, _) in enumerate(layers[:3])}
     print(json.dumps(out), flush=True)
 
 
@@ -333,6 +492,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, choices=[1, 2, 4, 8])
+    ap.add_argument("--workload", default="moe", choices=["moe", "gemv_small", "gate_up", "q4_stack"],
+                    help="moe (default: the routed layer) or one of the dense configurations")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -348,6 +509,9 @@ def main():
         return
     if args.profile_pass:
         profile_pass(args)
+        return
+    if args.workload != "moe":
+        run_dense(args)
         return
     run(args)
 

@@ -141,8 +141,9 @@ size_t pq_gemv_q4_workspace(int M, int K, int N, int epi);
  * PQ_EPI_SILU_MUL, N*K/2 < 2^31, and M*K <= 69632 (the bf16 activation and
  * its staging live in one CU's LDS; e.g. K = 17408 at M <= 4, K = 8704 at
  * M = 8); PQ_ERR_SHAPE otherwise.
- * M >= 5 with K % 256 == 0 runs on the matrix cores (bf16 MFMA on unpacked
- * nibbles), everything else on the vector units; PQ_Q4_PATH=valu or =mfma
+ * With K % 256 == 0, M >= 5 (and M == 4 when (N or N/2 under SiLU) * K >=
+ * 48 Mi) runs on the matrix cores (bf16 MFMA on unpacked nibbles), everything
+ * else on the vector units; PQ_Q4_PATH=valu or =mfma
  * forces one kernel (mfma only where K % 256 == 0).  For a given kernel the
  * output bits depend on the shape and the device's CU count only (not on M
  * or on other rows); PQ_BLOCKS_PER_CU (default 1) sets the blocks per CU. */
@@ -216,6 +217,15 @@ int pq_last_hip_error(void);
 /* Kernel launches one call makes for these arguments (1 for every entry
  * point in this library; reported by the bench as launches per layer). */
 int pq_launches_per_call(void);
+
+/* Measurement helper: stream `bytes` of device memory at `src` through the
+ * load path of the weight streams (128-bit non-temporal loads, one persistent
+ * block per CU, a contiguous share each) and store a checksum per wave into
+ * `sink` (device, 16-byte aligned, at least 65536 bytes).  Timing a call
+ * gives the achievable HBM read bandwidth that the kernels' roofline fraction
+ * can be compared with.  bytes % 16 == 0; a CU's share must stay below 2 GB
+ * (PQ_ERR_SHAPE).  Asynchronous on `stream`. */
+int pq_stream_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

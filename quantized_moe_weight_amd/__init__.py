@@ -15,7 +15,7 @@ import torch
 from . import _lib
 
 __all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemv_q4", "moe_decode_layer",
-           "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call",
+           "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call", "stream_probe",
            "EPI_NONE", "EPI_SILU_MUL", "lib"]
 
 EPI_NONE = 0
@@ -88,6 +88,14 @@ def workspace_check() -> int:
 
 def launches_per_call() -> int:
     return lib().pq_launches_per_call()
+
+
+def stream_probe(src, sink) -> None:
+    """Stream the bytes of device tensor ``src`` through the weight-stream load
+    path and store per-wave checksums into ``sink`` (uint32, >= 16384 words);
+    time it with events to get the achievable HBM read bandwidth."""
+    _check(lib().pq_stream_probe(_p(src), src.numel() * src.element_size(), _p(sink), _stream()),
+           "pq_stream_probe")
 
 
 def quantize_fp8(t: torch.Tensor):

@@ -32,6 +32,7 @@ SIGNATURES = {
     "pq_strerror": (ctypes.c_char_p, [_c_int]),
     "pq_last_hip_error": (_c_int, []),
     "pq_launches_per_call": (_c_int, []),
+    "pq_stream_probe": (_c_int, [_vp, _c_size, _vp, _vp]),
 }
 
 _lib = None

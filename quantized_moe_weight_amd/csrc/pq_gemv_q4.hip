@@ -623,7 +623,11 @@ bool use_mfma(int M, int K, int R) {
   const char* env = getenv("PQ_Q4_PATH");
   if (env && strcmp(env, "valu") == 0) return false;
   if (env && strcmp(env, "mfma") == 0) return true;
-  return M >= 5;
+  // From five tokens the vector kernel is dot-product bound on every shape; at
+  // four it still wins on small layers (5120x5120: 13.4 vs 16.5 us) and loses
+  // on large ones (17408x2x5120 with SiLU*up: 44.1 vs 37.4 us), where the
+  // matrix kernel's fixed stream-K cost is amortised.
+  return M >= 5 || (M == 4 && (size_t)R * K >= ((size_t)48 << 20));
 }
 
 // grid (blocks) and workspace bytes of the MFMA path

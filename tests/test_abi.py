@@ -64,6 +64,14 @@ def test_quantizers_host_validation(lib):
     assert lib.pq_quantize_q4(NUL, 1, 64, FAKE, FAKE, NUL) == PQ_ERR_NULL
 
 
+def test_stream_probe_host_validation(lib):
+    assert lib.pq_stream_probe(NUL, 64, FAKE, NUL) == PQ_ERR_NULL
+    assert lib.pq_stream_probe(FAKE, 64, NUL, NUL) == PQ_ERR_NULL
+    assert lib.pq_stream_probe(MIS, 64, FAKE, NUL) == PQ_ERR_ALIGN
+    assert lib.pq_stream_probe(FAKE, 0, FAKE, NUL) == PQ_ERR_SHAPE
+    assert lib.pq_stream_probe(FAKE, 40, FAKE, NUL) == PQ_ERR_SHAPE
+
+
 def test_workspace_helpers_host_validation(lib):
     assert lib.pq_workspace_init(NUL, 0, NUL) == PQ_OK
     assert lib.pq_workspace_init(NUL, 64, NUL) == PQ_ERR_NULL

@@ -1,6 +1,6 @@
 """GPU parity of pq_gemv_q4 (int4 g32 W4A16 GEMV with SiLU*up epilogue) against
 the oracle.  Two kernels: the MFMA one (K % 256 == 0, stream-K split with a
-cross-wave combine; the default for M >= 5) and the VALU one (K split inside a
+cross-wave combine; the default from M = 5, and at M = 4 for layers of >= 48 Mi weights) and the VALU one (K split inside a
 block).  PQ_Q4_PATH=valu / =mfma forces either, so both are checked on the
 same shapes.
 

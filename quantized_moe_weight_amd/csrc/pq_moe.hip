@@ -52,10 +52,10 @@ constexpr int kMaxPairs = kMaxM * kMaxTopK;   // 64 = one lane per (token, slot)
 constexpr int kMaxUnion = kMaxPairs;
 constexpr int kMaxE = 1024;
 // Ring depths in chunk-steps (gate_up: 1 KB of 2 rows per step; down: 1 KB of
-// 1 row).  Measured at M=1 on the routed layer: the barrier kernel is fastest
-// with 3 / 6 (deeper rings are slower: 8 / 8 costs 4.5 µs), the stream kernel
-// with 4 / 8.
-constexpr int DG = 4, DD = 8;        // stream kernel
+// 1 row).  Measured on the routed layer, both kernels are fastest with 3 / 6
+// (barrier kernel at M=1: 4 / 8 costs 0.7 µs, 8 / 8 4.5 µs; stream kernel at
+// M=4 / M=8: 4 / 8 costs 2 µs, 6 / 10 4–5 µs).
+constexpr int DG = 3, DD = 6;        // stream kernel
 constexpr int BDG = 3, BDD = 6;      // barrier kernel
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int kAuxSC1 = 0x10;            // buffer aux bit: agent-coherent (sc1) access

@@ -311,6 +311,23 @@ __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq:
   }
 }
 
+// One routed token: its top-k experts are distinct, so the union is its slots
+// in slot order (the order of the union entries changes no result), written
+// by the routing wave itself — no bitmap and no block barrier in between.
+__device__ void single_token_union(const MoeArgs& a, Route& r) {
+  const int lane = pq::lane_id();
+  if (lane < a.top_k) {
+    r.uexp[lane] = r.ids[lane];                  // written by this same lane
+    r.unp[lane] = 1;
+    r.upairs[lane][0] = lane;
+    r.items[lane] = lane;
+  }
+  if (lane == 0) {
+    r.nU = a.top_k;
+    r.nitems = a.top_k;
+  }
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // The barrier kernel: all gate_up units of the call, then one grid-wide
@@ -374,10 +391,12 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   if (threadIdx.x < kMaxM * kMaxE / 32) (&s_tmask[0][0])[threadIdx.x] = 0u;
 
   // ---- A. routing (waves 0..M-1, one token each) -----------------------------
+  const bool one_token = a.routed && a.M == 1;       // block-uniform
   if (a.routed) {
     if (wv < a.M) {
       if (a.E <= 256) route_token<4>(a, route, wv);
       else route_token<16>(a, route, wv);
+      if (one_token) single_token_union(a, route);
     }
   } else if (wv == 0 && lane < P) {
     int id = a.topk_ids[lane];
@@ -414,8 +433,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   }
 
   __syncthreads();                            // routes and the quantised x visible
-  if (wv == 0) build_union(a, route, hdr, s_tmask);
-  __syncthreads();
+  if (!one_token) {
+    if (wv == 0) build_union(a, route, hdr, s_tmask);
+    __syncthreads();
+  }
   const int nU = ufl(route.nU);
 
   // ---- C. gate_up + SiLU*up -------------------------------------------------
@@ -776,10 +797,12 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   if (threadIdx.x < kMaxM * kMaxE / 32) (&s_tmask[0][0])[threadIdx.x] = 0u;
 
   // ---- A. routing (waves 0..M-1, one token each) -----------------------------
+  const bool one_token = a.routed && a.M == 1;       // block-uniform
   if (a.routed) {
     if (wv < a.M) {
       if (a.E <= 256) route_token<4>(a, route, wv);
       else route_token<16>(a, route, wv);
+      if (one_token) single_token_union(a, route);
     }
   } else if (wv == 0 && lane < P) {
     int id = a.topk_ids[lane];
@@ -816,8 +839,10 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   }
 
   __syncthreads();                            // routes and the quantised x visible
-  if (wv == 0) build_union(a, route, hdr, s_tmask);
-  __syncthreads();
+  if (!one_token) {
+    if (wv == 0) build_union(a, route, hdr, s_tmask);
+    __syncthreads();
+  }
   const int nU = ufl(route.nU);
 
   // ---- C. per wave: gate_up units, then down units, no block barrier -------

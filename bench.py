@@ -10,13 +10,20 @@ combine.  Inputs are resident in HBM before timing starts.
 
 Reported (one JSON line):
   value        algorithmic bytes moved per second over the timed steps (GB/s)
-  ms_per_step  wall time per layer call
+  ms_per_step  wall time per layer call (K back-to-back calls, no other work in the timed region)
   roofline     the layer kernel against HBM peak: algorithmic bytes per launch
                divided by its mean launch duration (HIP events around each
-               launch on the launch stream); traffic = FETCH_SIZE + WRITE_SIZE
+               launch on the launch stream, in a second pass over the same
+               draws); traffic = FETCH_SIZE + WRITE_SIZE
                of the kernel from the committed rocprofv3 counter summary,
                scaled by a plain copy kernel of known size (null when the
                kernel source changed since the counters were taken)
+               (+ launch-duration p10/p50/p90, and the traffic over the mean
+               launch duration when the counters are current)
+  measured_read_peak
+               the HBM read bandwidth the library's streaming-read probe
+               reaches on this device (the practical ceiling of this load
+               path), and the layer kernel's fraction of it
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m M]
@@ -185,20 +192,26 @@ def run(args):
         call(x, pool[i % n_draws])
     torch.cuda.synchronize()
 
+    # timed region: exactly K back-to-back layer calls, nothing else on the stream
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_all0.record()
     for i in range(K):
-        starts[i].record()
         call(x, pool[i % n_draws])
-        ends[i].record()
     t_all1.record()
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
+    # a second pass over the same draws, with an event pair around each launch
+    # (on the launch stream), gives the per-launch kernel durations
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        starts[i].record()
+        call(x, pool[i % n_draws])
+        ends[i].record()
+    torch.cuda.synchronize()
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     status = call.check()
     if status != 0:

@@ -27,7 +27,8 @@ Reported (one JSON line):
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m M]
-       python bench.py --workload gemv_small|gate_up|q4_stack [--m M] [--steps K]   (dense configurations)
+       python bench.py --workload moe_tp8 [--m M]    (the layer's per-rank share under 8-way TP, I = 256)
+       python bench.py --workload gemv_small|gate_up|lm_head|q4_stack [--m M] [--steps K]   (dense GEMVs)
        python bench.py --ingest-pmc FETCH.csv WRITE.csv   (writes the counter summary)
 """
 from __future__ import annotations
@@ -161,7 +162,8 @@ def run(args):
     import workloads
 
     torch.cuda.set_device(0)
-    shp = workloads.MOE_SHAPE
+    tp8 = args.workload == "moe_tp8"
+    shp = workloads.MOE_TP8_SHAPE if tp8 else workloads.MOE_SHAPE
     M = args.m
     t_setup = time.perf_counter()
     w13, s13, w2, s2 = build_bank(pq, shp)
@@ -222,7 +224,7 @@ def run(args):
     mean_launch_s = float(np.mean(per_launch_ms)) * 1e-3
     bytes_per_launch = bytes_timed / K
     achieved = bytes_per_launch / mean_launch_s / 1e9
-    traffic = read_traffic(bytes_per_launch) if M == 1 else None
+    traffic = read_traffic(bytes_per_launch) if M == 1 and not tp8 else None
 
     out = {
         "metric": METRIC,
@@ -239,9 +241,10 @@ def run(args):
         "data": "synthetic",
         "config": {
             "workload": (f"routed FP8 MoE decode layer, M={M}: 256 experts resident in HBM, hidden 6144, "
-                         "expert intermediate 2048 (gate||up 6144->2x2048, SiLU*up, down 2048->6144), "
+                         f"expert intermediate {shp.I} (gate||up 6144->2x{shp.I}, SiLU*up, down {shp.I}->6144), "
                          "E4M3 weights with fp32 scale per 128-wide K block, top-8 of N(0,1) logits, "
-                         "live FP8 activation quantisation, bf16 in/out"),
+                         "live FP8 activation quantisation, bf16 in/out"
+                         + ("; one rank's share of the 2048-wide layer under 8-way tensor parallelism" if tp8 else "")),
             "M": M, "experts": shp.E, "hidden": shp.H, "intermediate": shp.I, "top_k": shp.top_k,
             "mean_experts_streamed": float(np.mean(uni)),
             "bytes_per_step": int(round(bytes_per_launch)),
@@ -321,15 +324,18 @@ def run_dense(args):
         return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).cuda()
 
     launches = []      # (callable, bytes)
-    if args.workload in ("gemv_small", "gate_up"):
+    if args.workload in ("gemv_small", "gate_up", "lm_head"):
         if args.workload == "gemv_small":
             K, N, epi, wl, desc = 512, 256, 0, workloads.FP8_GEMV_SMALL, "FP8 GEMV 512->256"
+        elif args.workload == "lm_head":
+            K, N, epi, wl, desc = 6144, workloads.LM_HEAD_V, 0, workloads.LM_HEAD, \
+                f"FP8 LM-head GEMV 6144->{workloads.LM_HEAD_V}"
         else:
             K, N, epi, wl, desc = 6144, 4096, 1, workloads.FP8_GATE_UP, "FP8 expert gate_up 6144->2x2048 + SiLU*up"
         m = workloads.master_weights_torch(N, K, workload=wl)
         q, sc = pq.quantize_fp8(m)
         per = q.numel() + sc.numel() * 4
-        copies = max(80, int(np.ceil((2 << 30) / per)))
+        copies = max(80, int(np.ceil((2 << 30) / per))) if args.workload != "lm_head" else 3
         W = q.unsqueeze(0).expand(copies, -1, -1).contiguous()
         S = sc.unsqueeze(0).expand(copies, -1, -1).contiguous()
         del m
@@ -505,7 +511,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, choices=[1, 2, 4, 8])
-    ap.add_argument("--workload", default="moe", choices=["moe", "gemv_small", "gate_up", "q4_stack"],
+    ap.add_argument("--workload", default="moe",
+                    choices=["moe", "moe_tp8", "gemv_small", "gate_up", "lm_head", "q4_stack"],
                     help="moe (default: the routed layer) or one of the dense configurations")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--profile-pass", action="store_true")
@@ -523,7 +530,7 @@ def main():
     if args.profile_pass:
         profile_pass(args)
         return
-    if args.workload != "moe":
+    if args.workload not in ("moe", "moe_tp8"):
         run_dense(args)
         return
     run(args)

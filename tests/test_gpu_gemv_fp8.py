@@ -157,3 +157,33 @@ def test_gemv_fp8_rejects_bad_shapes(pq):
     s = torch.ones((4, 1), dtype=torch.float32, device="cuda")
     with pytest.raises(pq.PqError):
         pq.gemv_fp8(x, w, s)
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_gemv_fp8_lm_head_sampled_rows(pq, M):
+    """LM-head GEMV at full vocabulary width (K=6144, N=151552, one launch): the
+    master weights are drawn on the device, quantised by the library, and a sample
+    of output rows (the first and last 128, plus 1536 drawn at random) is checked
+    against the oracle, which quantises just those rows' master weights (the
+    1x128 blocks of one row do not depend on any other row)."""
+    import torch
+    K, N = 6144, workloads.LM_HEAD_V
+    x = workloads.activation_bf16(M, K, workload=workloads.LM_HEAD, seed=M)
+    xt = np_bf16_bits_to_torch(x)
+    wt = workloads.master_weights_torch(N, K, workload=workloads.LM_HEAD, seed=M)
+    q, sc = pq.quantize_fp8(wt)
+    y, xq, xs = pq.gemv_fp8(xt, q, sc, debug=True)
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([np.arange(128), np.arange(N - 128, N),
+                                     rng.choice(N, 1536, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    w_rows = wt.index_select(0, ridx).cpu().numpy()
+    del wt
+    qo, so = oracle.block_quant_fp8(w_rows)
+    assert np.array_equal(q.index_select(0, ridx).cpu().numpy(), qo)
+    assert np.array_equal(sc.index_select(0, ridx).cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qx, sx = oracle.act_quant_fp8(x)
+    assert np.array_equal(xq.cpu().numpy(), qx)
+    yo, So = oracle.gemv_fp8(qx, sx, qo, so)
+    got = bf16_to_np(y)[:, rows]
+    assert_gemv_close(got, yo, So, f"lm_head M={M} rows={len(rows)}")

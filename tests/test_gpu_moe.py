@@ -255,6 +255,29 @@ def test_moe_full_size_layer(pq, path, M):
     print(f"full-size M={M} ({path}): union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
 
 
+@pytest.mark.parametrize("M", [1, 4])
+def test_moe_tp8_share_layer(pq, path, M):
+    """One GPU's share of the layer under 8-way tensor parallelism: all 256
+    experts, hidden 6144, intermediate cut to 2048/8 = 256 columns of gate/up
+    and rows of down.  The output is that share's partial sum of the combine;
+    every element is checked."""
+    import torch
+    shp = workloads.MOE_TP8_SHAPE
+    bank = Bank(pq, shp.E, shp.H, shp.I, workload=workloads.MOE_LAYER, seed=5)
+    x = workloads.activation_bf16(M, shp.H, workload=workloads.MOE_LAYER if M == 1 else workloads.MOE_VERIFY,
+                                  seed=5)
+    lg = (workloads.router_logits(1, shp.E, workload=workloads.MOE_LAYER, seed=5) if M == 1
+          else workloads.verify_logits(M, shp.E, seed=5))
+    ids, _ = oracle.route_topk(lg, shp.top_k)
+    bank.fill(ids)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              logits=torch.from_numpy(lg).cuda(), top_k=shp.top_k, debug=True)
+    assert pq.workspace_check() == 0
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=shp.top_k)
+    worst = _check(pq, bank, x, res, ref, M, shp.top_k)
+    print(f"tp8 share M={M} ({path}): union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
+
+
 @pytest.mark.parametrize("E", [16, 200, 256, 1000])
 def test_moe_routing_ties_and_signed_zero(pq, E):
     """Equal logits go to the lower expert id; -0 and +0 are equal."""

@@ -22,9 +22,9 @@ import numpy as np
 __all__ = [
     "FP8_GEMV_SMALL", "FP8_GATE_UP", "MOE_LAYER", "MOE_VERIFY", "Q4_STACK",
     "T_X", "T_W", "T_W13", "T_W2", "T_LOGITS", "T_OUTLIER",
-    "generator", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "LM_HEAD", "generator", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "activation_bf16", "master_weights", "router_logits", "verify_logits",
-    "MoEShape", "MOE_SHAPE", "Q4_SHAPES", "torch_seed", "master_weights_torch",
+    "MoEShape", "MOE_SHAPE", "MOE_TP8_SHAPE", "LM_HEAD_V", "Q4_SHAPES", "torch_seed", "master_weights_torch",
 ]
 
 # workload keys (first spawn-key component)
@@ -33,6 +33,7 @@ FP8_GATE_UP = 1
 MOE_LAYER = 2
 MOE_VERIFY = 3
 Q4_STACK = 4
+LM_HEAD = 5
 
 # tensor keys (second spawn-key component)
 T_X = 0
@@ -54,6 +55,11 @@ class MoEShape:
 
 
 MOE_SHAPE = MoEShape(E=256, H=6144, I=2048, top_k=8)
+# one rank's share of the same layer under 8-way tensor parallelism (I split 8 ways)
+MOE_TP8_SHAPE = MoEShape(E=256, H=6144, I=256, top_k=8)
+# LM-head GEMV: hidden 6144 to a vocabulary of LM_HEAD_V rows (a parameter: the
+# pages give no vocabulary size)
+LM_HEAD_V = 151552
 
 # (K, N, silu_mul) for the three linears of one int4 decoder block
 Q4_SHAPES = ((5120, 5120, False), (5120, 2 * 17408, True), (17408, 5120, False))

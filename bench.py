@@ -350,7 +350,11 @@ def run_dense(args):
             wp, sp = P(W[c]), P(S[c])
             launches.append((lambda wp=wp, sp=sp: lib.pq_gemv_fp8(P(x), M, K, wp, sp, N, epi, P(y), None, None,
                                                                    P(ws), ws.numel(), st), per + io))
-        kernel, unit = "gemv_fp8_kernel", "call"
+        fp8_path = os.environ.get("PQ_FP8_PATH", "")
+        big = M >= 3 and N * K >= (128 << 20)           # the library's default rule
+        kernel = ("gemv_fp8_mfma_kernel" if fp8_path == "mfma" or (big and fp8_path != "valu")
+                  else "gemv_fp8_kernel")
+        unit = "call"
         config = {"workload": f"{desc}, M={M}, E4M3 weights + fp32 block-128 scales, live FP8 act quant, "
                               f"{copies} weight copies rotated", "M": M, "K": K, "N": N, "epilogue": "silu_mul" if epi else "none"}
     elif args.workload == "q4_stack":
@@ -510,7 +514,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--m", type=int, default=1, choices=[1, 2, 4, 8])
+    ap.add_argument("--m", type=int, default=1, choices=range(1, 9), metavar="M")
     ap.add_argument("--workload", default="moe",
                     choices=["moe", "moe_tp8", "gemv_small", "gate_up", "lm_head", "q4_stack"],
                     help="moe (default: the routed layer) or one of the dense configurations")

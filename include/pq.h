@@ -97,9 +97,11 @@ int pq_quantize_q4(const float* w, int N, int K, uint8_t* packed, uint16_t* scal
 /* quantisation fused in ([Sionic] §1 and §4; §2 scales per K block).         */
 /* ------------------------------------------------------------------------- */
 
-/* Workspace bytes pq_gemv_fp8 needs: always 0 (where a row's K range is cut
- * between waves, the parts are reduced on chip); kept so the call has the
- * same shape of API as the others. */
+/* Workspace bytes pq_gemv_fp8 needs for this shape on the current device:
+ * 0 where the vector kernel runs (a row's K range cut between waves is
+ * reduced on chip), else the arrival counters and partial sums of the
+ * matrix-core kernel; 0 for invalid shapes (pq_gemv_fp8 then reports the
+ * error). */
 size_t pq_gemv_fp8_workspace(int M, int K, int N, int epi);
 
 /* y = epi(bf16( sum_b s_x[m,b] s_w[n,b] sum_{k in b} q_x[m,k] q_w[n,k] ))
@@ -109,11 +111,17 @@ size_t pq_gemv_fp8_workspace(int M, int K, int N, int epi);
  *   y       : bf16 [M,N] (PQ_EPI_NONE) or bf16 [M,N/2] (PQ_EPI_SILU_MUL)
  *   xq_dbg  : nullable, E4M3 [M,K]  — the quantised activation codes
  *   xs_dbg  : nullable, fp32 [M,K/128] — the activation scales
- *   ws, ws_bytes : ignored (may be NULL / 0).
+ *   ws, ws_bytes : device workspace of pq_gemv_fp8_workspace() bytes, set up
+ *            once by pq_workspace_init (may be NULL / 0 when that is 0);
+ *            too small: PQ_ERR_WORKSPACE.
  * Constraints: 1 <= M <= 8, K % 128 == 0, 128 <= K <= 16384, N >= 1,
  * N*K < 2^31, N even under PQ_EPI_SILU_MUL; PQ_ERR_SHAPE otherwise.
- * Each output row is computed by one block; its bits depend on the shape and
- * the device's CU count only (not on M or on the other rows); the variable
+ * Two kernels: a vector kernel (each output row computed by one block) and,
+ * for M >= 3 on weight matrices of at least 128 MB, a matrix-core kernel
+ * (v_mfma_f32_16x16x128_f8f6f4 per 128-wide K block, tiles of 16 rows split
+ * over the whole grid).  In either kernel an output's bits depend on the
+ * shape and the device's CU count only (not on the other tokens); the two
+ * kernels round differently.  PQ_FP8_PATH=valu|mfma forces one kernel;
  * PQ_BLOCKS_PER_CU (default 1) sets the number of blocks per CU. */
 int pq_gemv_fp8(const uint16_t* x, int M, int K,
                 const uint8_t* w, const float* w_scale, int N,

@@ -40,6 +40,23 @@ class splitk:
             os.environ["PQ_BLOCKS_PER_CU"] = self.old
 
 
+class fp8_path:
+    """Force the vector (valu) or the matrix-core (mfma) kernel via PQ_FP8_PATH."""
+
+    def __init__(self, kernel):
+        self.kernel = kernel
+
+    def __enter__(self):
+        self.old = os.environ.get("PQ_FP8_PATH")
+        os.environ["PQ_FP8_PATH"] = self.kernel
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("PQ_FP8_PATH", None)
+        else:
+            os.environ["PQ_FP8_PATH"] = self.old
+
+
 def _case(M, K, N, seed, workload=workloads.FP8_GEMV_SMALL):
     import torch
     x = workloads.activation_bf16(M, K, workload=workload, seed=seed)
@@ -93,34 +110,91 @@ def test_gemv_fp8_silu(pq, M, K, N, S):
     assert_silu_close(bf16_to_np(y), h, yo[:, :I], yo[:, I:], So[:, :I], So[:, I:], f"M={M} S={S}")
 
 
-def test_gemv_fp8_decodes_every_code(pq):
+@pytest.mark.parametrize("kernel,M", [("valu", 1), ("mfma", 1), ("mfma", 5)])
+def test_gemv_fp8_decodes_every_code(pq, kernel, M):
     """Weight rows hold each of the 256 codes at one position and x is 448 there:
-    y[n] = 448 * dq(code_n) exactly (NaN for the two NaN codes)."""
+    y[n] = 448 * dq(code_n) exactly (NaN for the two NaN codes).  With M > 1
+    the other tokens are zero: their outputs are exactly zero, except NaN on the
+    two NaN-code rows (0 * NaN is NaN, as in the dequantise-then-multiply
+    definition)."""
     import torch
     K, k0 = 256, 77
     w = np.zeros((256, K), np.uint8)
     w[:, k0] = np.arange(256, dtype=np.uint8)
     sw = np.ones((256, 2), np.float32)
-    x = np.zeros((1, K), np.uint16)
+    x = np.zeros((M, K), np.uint16)
     x[0, k0] = workloads.f32_to_bf16_bits(np.array([448.0], np.float32))[0]
-    y = pq.gemv_fp8(np_bf16_bits_to_torch(x), torch.from_numpy(w).cuda(), torch.from_numpy(sw).cuda())
-    got = bf16_to_np(y)[0]
+    with fp8_path(kernel):
+        y = pq.gemv_fp8(np_bf16_bits_to_torch(x), torch.from_numpy(w).cuda(), torch.from_numpy(sw).cuda())
+    out = bf16_to_np(y)
+    nan_rows = np.isnan(oracle.e4m3_decode(np.arange(256, dtype=np.uint8)))
+    assert np.all(np.isnan(out[1:, nan_rows])) and np.all(out[1:, ~nan_rows] == 0)
+    got = out[0]
     want = 448.0 * oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
     assert np.array_equal(np.isnan(got), np.isnan(want))
     ok = ~np.isnan(want)
     assert np.array_equal(got[ok], want[ok])
 
 
-def test_gemv_fp8_rows_bitwise_independent_of_M(pq):
+@pytest.mark.parametrize("kernel", ["valu", "mfma"])
+def test_gemv_fp8_rows_bitwise_independent_of_M(pq, kernel):
+    """On either kernel a token's outputs do not depend on the other tokens of
+    the call (the split of the rows depends on the shape and device only)."""
     import torch
     M, K, N = 6, 2048, 512
     x, w, xt, wt = _case(M, K, N, seed=17)
     q, sc = pq.quantize_fp8(wt)
-    with splitk(1):
+    with splitk(1), fp8_path(kernel):
         y = pq.gemv_fp8(xt, q, sc, epi=pq.EPI_SILU_MUL)
         for m in range(M):
             ym = pq.gemv_fp8(xt[m:m + 1].contiguous(), q, sc, epi=pq.EPI_SILU_MUL)
             assert torch.equal(ym[0].view(torch.int16), y[m].view(torch.int16))
+
+
+@pytest.mark.parametrize("M,K,N,epi,S", [
+    (4, 6144, 4096, 1, None),   # one expert gate_up, 4 draft tokens
+    (8, 6144, 4096, 1, None),
+    (8, 6144, 300, 0, None),    # ragged last tile (300 = 18 x 16 + 12)
+    (5, 128, 50, 0, None),      # one K block per row: every tile cut between waves or not at all
+    (7, 2048, 4000, 0, 2),      # two blocks per CU
+    (6, 1152, 70, 1, 3),        # SiLU with a ragged tile, odd K blocks (9)
+    (1, 640, 37, 0, None),      # the matrix kernel forced below its default range
+    (2, 4096, 1000, 1, None),
+    (3, 2560, 129, 0, 1),
+])
+def test_gemv_fp8_mfma_kernel(pq, M, K, N, epi, S):
+    """The matrix-core kernel (the default for M >= 4; forced here for every
+    case) against the oracle; the activation codes and scales bit-exact."""
+    wl = workloads.FP8_GATE_UP if epi else workloads.FP8_GEMV_SMALL
+    x, w, xt, wt = _case(M, K, N, seed=1000 + M * 7 + K + N, workload=wl)
+    with fp8_path("mfma"):
+        y, xq, xs, q, sc = _run(pq, xt, wt, pq.EPI_SILU_MUL if epi else pq.EPI_NONE, S)
+    qx, sx = oracle.act_quant_fp8(x)
+    assert np.array_equal(xq.cpu().numpy(), qx)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), sx.view(np.uint32))
+    yo, So = oracle.gemv_fp8(qx, sx, q, sc)
+    if epi:
+        I = N // 2
+        h = oracle.silu_mul(yo, I)
+        assert_silu_close(bf16_to_np(y), h, yo[:, :I], yo[:, I:], So[:, :I], So[:, I:], f"mfma M={M} N={N}")
+    else:
+        assert_gemv_close(bf16_to_np(y), yo, So, f"mfma M={M} K={K} N={N} S={S}")
+
+
+def test_gemv_fp8_mfma_repeat_calls_reset_counters(pq):
+    """Back-to-back calls on one workspace (the per-tile arrival counters are
+    reset by the last arriver) give identical bits, also across shapes."""
+    import torch
+    with fp8_path("mfma"):
+        x, w, xt, wt = _case(8, 2048, 1000, seed=5)
+        q, sc = pq.quantize_fp8(wt)
+        y0 = pq.gemv_fp8(xt, q, sc)
+        x2, w2, xt2, wt2 = _case(5, 512, 333, seed=6)
+        q2, sc2 = pq.quantize_fp8(wt2)
+        z0 = pq.gemv_fp8(xt2, q2, sc2)
+        for _ in range(10):
+            assert torch.equal(pq.gemv_fp8(xt, q, sc).view(torch.int16), y0.view(torch.int16))
+            assert torch.equal(pq.gemv_fp8(xt2, q2, sc2).view(torch.int16), z0.view(torch.int16))
 
 
 def test_gemv_fp8_deterministic_repeats(pq):

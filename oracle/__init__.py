@@ -38,7 +38,7 @@ from .codecs import (E4M3_MAX, e4m3_decode, e4m3_encode, bf16_round, bf16_bits,
                      bf16_bits_to_f64, q4_pack, q4_unpack)
 from .quant import block_quant_fp8, act_quant_fp8, dequant_fp8, q4_quant, dequant_q4
 from .linear import gemv_fp8, silu_mul, gemv_q4
-from .moe import route_topk, moe_layer, union_of_experts
+from .moe import route_topk, router_logits, moe_layer, union_of_experts
 from . import traffic
 
 __all__ = [

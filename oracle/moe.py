@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import bf16_bits
+from .codecs import bf16_bits, bf16_bits_to_f64
 from .linear import gemv_fp8, silu_mul
 from .quant import act_quant_fp8
 
@@ -50,13 +50,30 @@ def route_topk(logits, top_k: int = 8):
     return ids, wts
 
 
+def router_logits(x_bf16_bits, wr_bf16_bits) -> np.ndarray:
+    """Router logits l[m, e] = sum_k x[m, k] * Wr[e, k], float64.
+
+    [CMP], section on the 3.05bpw quality (the per-tensor bit allocation of the
+    4.05bpw build): the router stays at native precision while the experts are
+    quantised.  Reading taken: the router is a bf16 [E, H] weight applied to the
+    bf16 layer input (no FP8 quantisation, no bias); the oracle returns the
+    exact products summed in float64.  Which experts a token takes is decided
+    on the logits the kernel computed (route_topk applied to them): near-equal
+    logits may order differently under another summation order.
+    """
+    x = bf16_bits_to_f64(np.atleast_2d(np.asarray(x_bf16_bits, dtype=np.uint16)))
+    w = bf16_bits_to_f64(np.atleast_2d(np.asarray(wr_bf16_bits, dtype=np.uint16)))
+    assert x.shape[1] == w.shape[1]
+    return x @ w.T
+
+
 def union_of_experts(ids) -> np.ndarray:
     """Sorted distinct expert ids routed by any token of the call (#U = len)."""
     return np.unique(np.asarray(ids).reshape(-1))
 
 
-def moe_layer(x_bf16_bits, expert, *, logits=None, ids=None, weights=None, top_k: int = 8):
-    """One routed MoE layer for M tokens.
+def moe_layer(x_bf16_bits, expert, *, logits=None, ids=None, weights=None, top_k: int = 8, shared=None):
+    """One routed MoE layer for M tokens, with an optional shared expert.
 
     ``expert(e)`` returns the quantised bank entry of expert e as
     (q13 uint8 [2I, H], s13 fp32 [2I, H/128], q2 uint8 [H, I], s2 fp32 [H, I/128]),
@@ -73,6 +90,16 @@ def moe_layer(x_bf16_bits, expert, *, logits=None, ids=None, weights=None, top_k
 
     Reading taken: h is handed to the down projection as bf16 and re-quantised
     live exactly like the layer input (the pages fix neither).
+
+    ``shared`` (optional) is a shared expert in the layout of ``expert(e)``:
+    [CMP], section on the 3.05bpw quality, lists shared experts beside the
+    routed ones (kept at more bits).  Reading taken: every token runs it
+    through the same gate_up -> SiLU*up -> bf16 h -> live re-quant -> down
+    chain, and its output is added with weight 1 after the routed slots,
+    out[m] = sum_j w[m, j] * y_j + y_shared (float64).  Its intermediates are
+    returned as ``sh_h``, ``sh_h_bits``, ``sh_hq``, ``sh_hs`` [M, I] (and
+    ``sh_hs`` [M, I/128]), ``sh_gate``/``sh_up``/``sh_S_gate``/``sh_S_up``;
+    ``S`` then also holds sum_k |hq~_k| |w2~_nk| of the shared expert.
 
     Returns a dict with ``out`` float64 [M, H] (unrounded), ``S`` [M, H]
     (sum_j |w_j| * sum_k |hq~_k| |w2~_nk|), ``ids``, ``weights``, and the
@@ -116,6 +143,24 @@ def moe_layer(x_bf16_bits, expert, *, logits=None, ids=None, weights=None, top_k
             h_all[m, j], hb_all[m, j], hq_all[m, j], hs_all[m, j] = h, hb, hq, hs
             gate[m, j], up[m, j] = y13[:I], y13[I:]
             sg[m, j], su[m, j] = e13[:I], e13[I:]
-    return {"out": out, "S": S, "ids": ids, "weights": weights, "h": h_all, "h_bits": hb_all,
-            "hq": hq_all, "hs": hs_all, "gate": gate, "up": up, "S_gate": sg, "S_up": su,
-            "xq": qx, "xs": sx}
+    res_out = {"out": out, "S": S, "ids": ids, "weights": weights, "h": h_all, "h_bits": hb_all,
+               "hq": hq_all, "hs": hs_all, "gate": gate, "up": up, "S_gate": sg, "S_up": su,
+               "xq": qx, "xs": sx}
+    if shared is not None:
+        q13, s13, q2, s2 = shared
+        Is = q13.shape[0] // 2
+        keys = ("sh_h", "sh_h_bits", "sh_hq", "sh_hs", "sh_gate", "sh_up", "sh_S_gate", "sh_S_up")
+        acc = {k: [] for k in keys}
+        for m in range(M):                        # after the routed slots of token m
+            y13, s13err = gemv_fp8(qx[m:m + 1], sx[m:m + 1], q13, s13)
+            h = silu_mul(y13, Is)[0]
+            hb = bf16_bits(h)
+            hq, hs = act_quant_fp8(hb[None, :])
+            y2, s2err = gemv_fp8(hq, hs, q2, s2)
+            out[m] += y2[0]
+            S[m] += s2err[0]
+            for k, v in zip(keys, (h, hb, hq[0], hs[0], y13[0, :Is], y13[0, Is:], s13err[0, :Is], s13err[0, Is:])):
+                acc[k].append(v)
+        for k in keys:
+            res_out[k] = np.stack(acc[k])
+    return res_out

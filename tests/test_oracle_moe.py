@@ -108,3 +108,72 @@ def test_moe_rows_independent_of_batch():
     for m in range(3):
         rm = oracle.moe_layer(x[m:m + 1], lambda e: bank[e], logits=lg[m:m + 1], top_k=3)
         assert np.all(np.abs(rm["out"][0] - r["out"][m]) <= 2.0 ** -45 * r["S"][m])
+
+
+def test_router_logits_exact_rational_brute_force():
+    """The router's fp64 logits equal the exact rational dot products of the
+    bf16 inputs (every bf16 value is a dyadic rational; the sums of 64 of them
+    are exact in fp64 here because the magnitudes are bounded)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    M, E, H = 2, 5, 64
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    wr = workloads.f32_to_bf16_bits((0.05 * rng.standard_normal((E, H))).astype(np.float32))
+    lg = oracle.router_logits(x, wr)
+    xv = workloads.bf16_bits_to_f32(x).astype(np.float64)
+    wv = workloads.bf16_bits_to_f32(wr).astype(np.float64)
+    for m in range(M):
+        for e in range(E):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xv[m], wv[e]))
+            assert abs(Fraction(float(lg[m, e])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
+def test_router_logits_one_hot_rows_select_inputs():
+    """A router row that is 1.0 at position k and 0 elsewhere gives x[m, k]
+    exactly; a row of 2.0 gives twice the sum (closed forms)."""
+    rng = np.random.default_rng(10)
+    M, H = 3, 256
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    one = workloads.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    two = workloads.f32_to_bf16_bits(np.array([2.0], np.float32))[0]
+    wr = np.zeros((4, H), np.uint16)
+    for e, k in enumerate([0, 7, 100, 255]):
+        wr[e, k] = one
+    lg = oracle.router_logits(x, wr)
+    xv = workloads.bf16_bits_to_f32(x).astype(np.float64)
+    assert np.array_equal(lg, xv[:, [0, 7, 100, 255]])
+    lg2 = oracle.router_logits(x, np.full((1, H), two, np.uint16))
+    assert np.allclose(lg2[:, 0], 2.0 * xv.sum(axis=1), rtol=0, atol=1e-12)
+
+
+def test_router_logits_match_torch_float64():
+    """Against torch's own bf16 -> fp64 conversion and fp64 matmul."""
+    rng = np.random.default_rng(11)
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((4, 512)).astype(np.float32))
+    wr = workloads.f32_to_bf16_bits((0.02 * rng.standard_normal((32, 512))).astype(np.float32))
+    tx = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double()
+    tw = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).double()
+    ref = (tx @ tw.T).numpy()
+    assert np.allclose(oracle.router_logits(x, wr), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_shared_expert_is_a_weight_one_slot_after_the_routed_slots():
+    """The layer with a shared expert equals the layer without it whose every
+    token gets one more slot, after its routed slots, on the shared expert with
+    weight 1 (a decomposition into the already-pinned routed layer)."""
+    E, H, I, M, k = 9, 256, 256, 3, 3
+    bank = _bank(E + 1, H, I, seed=7)                 # expert E plays the shared one
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=7)
+    lg = workloads.router_logits(M, E, workload=workloads.MOE_LAYER, seed=7)
+    ids, w = oracle.route_topk(lg, k)
+    r = oracle.moe_layer(x, lambda e: bank[e], logits=lg, top_k=k, shared=bank[E])
+    ids2 = np.concatenate([ids, np.full((M, 1), E)], axis=1)
+    w2 = np.concatenate([w, np.ones((M, 1))], axis=1)
+    r2 = oracle.moe_layer(x, lambda e: bank[e], ids=ids2, weights=w2)
+    assert np.array_equal(r["out"], r2["out"])
+    assert np.array_equal(r["S"], r2["S"])
+    assert np.array_equal(r["sh_hq"], r2["hq"][:, k]) and np.array_equal(r["sh_hs"], r2["hs"][:, k])
+    assert np.array_equal(r["sh_h_bits"], r2["h_bits"][:, k])
+    # and against the explicit torch-SiLU composition
+    ref = _explicit_layer(x, bank, ids2, w2)
+    assert np.all(np.abs(r["out"] - ref) <= 1e-3 * r["S"])

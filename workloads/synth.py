@@ -8,6 +8,9 @@ Shapes follow the decode workloads this repository measures:
                       intermediate 2048, top-8 of N(0,1) router logits.
 * ``MOE_VERIFY``      the same layer for M in {1,2,4,8} draft tokens whose
                       logits share an equicorrelated component (rho = 0.5).
+* ``MOE_LAYER`` extras: bf16 router weights [E, H] (N(0,1)/sqrt(H+800), so the
+                      logits come out near N(0,1)) and a shared expert drawn
+                      like a routed one (tensor keys T_SH13 / T_SH2).
 * ``Q4_STACK``        int4 g32 dense linears K=5120 with N in
                       {5120, 2x17408 (gate||up), 17408->5120}.
 
@@ -21,7 +24,8 @@ import numpy as np
 
 __all__ = [
     "FP8_GEMV_SMALL", "FP8_GATE_UP", "MOE_LAYER", "MOE_VERIFY", "Q4_STACK",
-    "T_X", "T_W", "T_W13", "T_W2", "T_LOGITS", "T_OUTLIER",
+    "T_X", "T_W", "T_W13", "T_W2", "T_LOGITS", "T_OUTLIER", "T_ROUTER", "T_SH13", "T_SH2",
+    "router_weights_bf16",
     "LM_HEAD", "generator", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "activation_bf16", "master_weights", "router_logits", "verify_logits",
     "MoEShape", "MOE_SHAPE", "MOE_TP8_SHAPE", "LM_HEAD_V", "Q4_SHAPES", "torch_seed", "master_weights_torch",
@@ -42,6 +46,9 @@ T_W13 = 2
 T_W2 = 3
 T_LOGITS = 4
 T_OUTLIER = 5
+T_ROUTER = 6      # router weights (bf16)
+T_SH13 = 7        # shared expert gate||up
+T_SH2 = 8         # shared expert down
 
 
 class MoEShape:
@@ -122,6 +129,14 @@ def verify_logits(M: int, E: int, *, rho: float = 0.5, workload: int = MOE_VERIF
     s = g.standard_normal(E)
     e = g.standard_normal((M, E))
     return (np.sqrt(rho) * s[None, :] + np.sqrt(1.0 - rho) * e).astype(np.float32)
+
+
+def router_weights_bf16(E: int, H: int, *, workload: int = MOE_LAYER, seed: int = 0) -> np.ndarray:
+    """bf16 router weights [E, H] = bf16(N(0,1) / sqrt(H + 800)) as uint16 bits: with the
+    activation recipe (N(0,1) plus two channels x20) the logits come out near N(0,1)."""
+    g = generator(workload, T_ROUTER, 0, seed)
+    w = g.standard_normal((E, H), dtype=np.float32) / np.float32(np.sqrt(H + 800.0))
+    return f32_to_bf16_bits(w)
 
 
 def torch_seed(workload: int, tensor: int, expert: int = 0, seed: int = 0) -> int:

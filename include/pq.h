@@ -205,6 +205,39 @@ int moe_decode_layer(const uint16_t* x, int M, int H,
                      uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg,
                      void* ws, size_t ws_bytes, void* stream);
 
+/* The same layer with the steps either side of it in the launch ([CMP], on
+ * the 3.05bpw quality: the router kept at native precision, shared experts
+ * beside the routed ones):
+ *   router_w : nullable bf16 [E,H].  When given, the router GEMV runs in the
+ *            launch: l[m,e] = sum_k x[m,k] router_w[e,k] (bf16 products, fp32
+ *            accumulation), each block computing a slice of the rows and
+ *            publishing it through the workspace; routing then follows
+ *            moe_decode_layer's rule on these logits, which are written to
+ *            router_logits (nullable, fp32 [M,E]) and the ids and weights to
+ *            topk_ids / topk_w.  When router_w is NULL, router_logits and
+ *            topk_ids / topk_w mean what they mean in moe_decode_layer.
+ *   sh_w13, sh_s13, sh_w2, sh_s2 : a shared expert with the routed experts'
+ *            shapes ([2I,H], [2I,H/128], [H,I], [H,I/128]), all four or none
+ *            (else PQ_ERR_NULL).  Every token runs it like a routed slot and
+ *            its output is added with weight 1 after the routed slots:
+ *            out[m] = bf16( sum_j w[m,j] y_j + y_shared ).  Its weights are
+ *            streamed first, while the routing is still being decided.
+ *   h_dbg, hq_dbg, hs_dbg : nullable [M*top_k + M*sh, I] (and [.., I/128]):
+ *            the (token, slot) pairs, then the shared expert's pair per token.
+ * Everything else as moe_decode_layer (which is this call with router_w and
+ * the shared expert NULL).  The same workspace size serves both. */
+int moe_decode_layer_ex(const uint16_t* x, int M, int H,
+                        const uint16_t* router_w, float* router_logits,
+                        int32_t* topk_ids, float* topk_w,
+                        int E, int top_k, int I,
+                        const uint8_t* w13, const float* s13,
+                        const uint8_t* w2, const float* s2,
+                        const uint8_t* sh_w13, const float* sh_s13,
+                        const uint8_t* sh_w2, const float* sh_s2,
+                        uint16_t* out,
+                        uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg,
+                        void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Workspace and error helpers.                                               */
 /* ------------------------------------------------------------------------- */

@@ -167,13 +167,16 @@ def moe_workspace_bytes(M: int, H: int, I: int, E: int, top_k: int) -> int:
 
 
 def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=None, top_k: int = 8,
-                     debug: bool = False, out=None):
-    """One routed MoE decode layer in one launch.
+                     router_w=None, shared=None, debug: bool = False, out=None):
+    """One MoE decode layer in one launch.
 
     x bf16 [M,H]; w13 uint8 [E,2I,H], s13 fp32 [E,2I,H/128]; w2 uint8 [E,H,I], s2 fp32 [E,H,I/128].
-    Either ``logits`` fp32 [M,E] (routing computed on the GPU) or ``topk_ids`` int32 / ``topk_w`` fp32
-    [M,top_k].  Returns a dict with ``out`` (bf16 [M,H]), ``topk_ids``, ``topk_w`` and, with debug,
-    ``h`` (bf16 [M,k,I]), ``hq`` (uint8 [M,k,I]), ``hs`` (fp32 [M,k,I/128])."""
+    Routing from ``router_w`` bf16 [E,H] (the router GEMV runs in the launch; its logits are
+    returned as ``logits``), from ``logits`` fp32 [M,E], or from given ``topk_ids`` int32 /
+    ``topk_w`` fp32 [M,top_k].  ``shared`` = (w13, s13, w2, s2) of one expert of the bank's
+    shapes adds a shared expert with weight 1.  Returns a dict with ``out`` (bf16 [M,H]),
+    ``topk_ids``, ``topk_w`` and, with debug, ``h`` (bf16 [M*k + M*sh, I]: the (token, slot)
+    pairs, then the shared expert's per token), ``hq`` (uint8, same), ``hs`` (fp32 [.., I/128])."""
     _need(x, torch.bfloat16, 2, "x")
     _need(w13, torch.uint8, 3, "w13")
     _need(s13, torch.float32, 3, "s13")
@@ -183,7 +186,13 @@ def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=
     E, two_i, _ = w13.shape
     I = two_i // 2
     dev = x.device
-    if logits is not None:
+    lg_out = None
+    if router_w is not None:
+        _need(router_w, torch.bfloat16, 2, "router_w")
+        lg_out = torch.empty((M, E), dtype=torch.float32, device=dev)
+        topk_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+        topk_w = torch.empty((M, top_k), dtype=torch.float32, device=dev)
+    elif logits is not None:
         _need(logits, torch.float32, 2, "logits")
         topk_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
         topk_w = torch.empty((M, top_k), dtype=torch.float32, device=dev)
@@ -191,17 +200,32 @@ def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=
         _need(topk_ids, torch.int32, 2, "topk_ids")
         _need(topk_w, torch.float32, 2, "topk_w")
         top_k = topk_ids.shape[1]
+    sh = (None,) * 4
+    if shared is not None:
+        sh = tuple(shared)
+        for t, dt, nm in zip(sh, (torch.uint8, torch.float32, torch.uint8, torch.float32),
+                             ("shared w13", "shared s13", "shared w2", "shared s2")):
+            _need(t, dt, 2, nm)
+        if sh[0].shape != w13.shape[1:] or sh[2].shape != w2.shape[1:]:
+            raise ValueError("the shared expert must have the routed experts' shapes")
+    npairs = M * top_k + (M if shared is not None else 0)
     y = out if out is not None else torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    h = torch.empty((M, top_k, I), dtype=torch.bfloat16, device=dev) if debug else None
-    hq = torch.empty((M, top_k, I), dtype=torch.uint8, device=dev) if debug else None
-    hs = torch.empty((M, top_k, I // 128), dtype=torch.float32, device=dev) if debug else None
+    h = torch.empty((npairs, I), dtype=torch.bfloat16, device=dev) if debug else None
+    hq = torch.empty((npairs, I), dtype=torch.uint8, device=dev) if debug else None
+    hs = torch.empty((npairs, I // 128), dtype=torch.float32, device=dev) if debug else None
     ws, wsn = _workspace(moe_workspace_bytes(M, H, I, E, top_k))
-    _check(lib().moe_decode_layer(_p(x), M, H, _p(logits), _p(topk_ids), _p(topk_w), E, top_k, I,
-                                  _p(w13), _p(s13), _p(w2), _p(s2), _p(y), _p(h), _p(hq), _p(hs),
-                                  _p(ws), wsn, _stream()), "moe_decode_layer")
+    lg_arg = lg_out if router_w is not None else logits
+    _check(lib().moe_decode_layer_ex(_p(x), M, H, _p(router_w), _p(lg_arg), _p(topk_ids), _p(topk_w), E, top_k, I,
+                                     _p(w13), _p(s13), _p(w2), _p(s2), _p(sh[0]), _p(sh[1]), _p(sh[2]), _p(sh[3]),
+                                     _p(y), _p(h), _p(hq), _p(hs), _p(ws), wsn, _stream()), "moe_decode_layer_ex")
     res = {"out": y, "topk_ids": topk_ids, "topk_w": topk_w}
+    if lg_out is not None:
+        res["logits"] = lg_out
     if debug:
-        res.update(h=h, hq=hq, hs=hs)
+        P = M * top_k
+        res.update(h=h[:P].view(M, top_k, I), hq=hq[:P].view(M, top_k, I), hs=hs[:P].view(M, top_k, I // 128))
+        if shared is not None:
+            res.update(sh_h=h[P:], sh_hq=hq[P:], sh_hs=hs[P:])
     return res
 
 

@@ -49,7 +49,8 @@ constexpr int kWaves = kThreads / pq::kWave;
 constexpr int kMaxM = 8;
 constexpr int kMaxTopK = 8;
 constexpr int kMaxPairs = kMaxM * kMaxTopK;   // 64 = one lane per (token, slot)
-constexpr int kMaxUnion = kMaxPairs;
+constexpr int kMaxPairs2 = kMaxPairs + kMaxM;  // with the shared expert's pair of each token
+constexpr int kMaxUnion = kMaxPairs + 1;       // with the shared expert's entry
 constexpr int kMaxE = 1024;
 // Ring depths in chunk-steps (gate_up: 1 KB of 2 rows per step; down: 1 KB of
 // 1 row).  Measured on the routed layer, both kernels are fastest with 3 / 6
@@ -64,6 +65,13 @@ constexpr int kFlagStride = 32;          // uint32 per release flag: one 128-byt
 struct MoeArgs {
   const uint16_t* x;
   const float* logits;
+  const uint16_t* wr;     // router weights bf16 [E][H] (null: logits or ids are given)
+  float* logits_out;      // router logits computed here [M][E] (nullable)
+  uint32_t* lx;           // logit exchange [M][E]: inverted bits, zero between calls
+  const uint8_t* sw13;    // shared expert (null: none), layout of one bank entry
+  const float* ss13;
+  const uint8_t* sw2;
+  const float* ss2;
   int32_t* topk_ids;
   float* topk_w;
   const uint8_t* w13;
@@ -75,9 +83,12 @@ struct MoeArgs {
   uint8_t* hq_dbg;
   float* hs_dbg;
   uint8_t* ws;
-  uint16_t* hbuf;   // [P][I] bf16 (stream kernel: bits inverted, zero between calls)
+  uint16_t* hbuf;   // [P2][I] bf16 (stream kernel: bits inverted, zero between calls)
   int M, H, I, E, top_k;
-  int routed;
+  int routed;       // routes from logits (given or computed), else from given ids
+  int router;       // logits computed in the launch from wr
+  int sh;           // 1 with a shared expert: union entry 0, pairs P .. P + M - 1
+  int P2;           // M * top_k + sh * M
   uint32_t spin_limit;
   int xs_off, ha_off, hs_off, yb_off;   // byte offsets of the LDS regions
   int alias;        // h codes and scales reuse the x region
@@ -89,7 +100,7 @@ struct Route {
   int uexp[kMaxUnion];            // expert id of union entry u
   int unp[kMaxUnion];             // number of (token, slot) pairs routed to u
   int upairs[kMaxUnion][kMaxM];   // their pair indices p = m * top_k + j, ascending
-  int items[kMaxPairs];           // (entry u, pair slot t) = u | t << 8, in union order
+  int items[kMaxPairs2];          // (entry u, pair slot t) = u | t << 8, in union order
   int nU, nitems;
 };
 
@@ -125,14 +136,39 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // of the k rounds takes the wave-wide maximum of the lanes' current heads;
 // among lanes holding the maximum key the lowest expert id wins, so equal
 // logits go to the lower id.  KPER = candidates per lane (E <= 64 * KPER).
-template <int KPER>
+// XCH: the logits come from the exchange buffer, where the blocks that
+// computed them publish them inverted; wait until every one is there (bounded
+// wait: on a timeout the error is recorded and the routing goes on).
+template <int KPER, bool XCH>
 __device__ void route_token(const MoeArgs& a, Route& r, int m) {
   const int lane = pq::lane_id();
   // all logit loads issued before the first wait (past E: zero-filled, key 0)
-  const pq::rsrc_t lr = pq::make_rsrc(a.logits + (size_t)m * a.E, (uint32_t)a.E * 4u);
   float lv[KPER];
+  if (XCH) {
+    const pq::rsrc_t lr = pq::make_rsrc(a.lx + (size_t)m * a.E, (uint32_t)a.E * 4u);
+    uint32_t raw[KPER];
+    for (uint32_t it = 0;; ++it) {
+      bool miss = false;
 #pragma unroll
-  for (int q = 0; q < KPER; ++q) lv[q] = pq::buf_load_f32(lr, (uint32_t)(q * pq::kWave + lane) * 4u);
+      for (int q = 0; q < KPER; ++q) {
+        const int e = q * pq::kWave + lane;
+        raw[q] = __builtin_amdgcn_raw_buffer_load_b32(lr, (int)((uint32_t)e * 4u), 0, kAuxSC1);
+        miss |= e < a.E && raw[q] == 0u;
+      }
+      if (__ballot(miss) == 0ull) break;
+      if (it >= a.spin_limit) {
+        if (lane == 0) pq::record_error(reinterpret_cast<pq::WsHeader*>(a.ws), PQ_ERR_TIMEOUT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) lv[q] = __uint_as_float(~raw[q]);
+  } else {
+    const pq::rsrc_t lr = pq::make_rsrc(a.logits + (size_t)m * a.E, (uint32_t)a.E * 4u);
+#pragma unroll
+    for (int q = 0; q < KPER; ++q) lv[q] = pq::buf_load_f32(lr, (uint32_t)(q * pq::kWave + lane) * 4u);
+  }
   uint32_t key[KPER];
   int eid[KPER];
 #pragma unroll
@@ -200,7 +236,7 @@ __device__ void route_token(const MoeArgs& a, Route& r, int m) {
 // below it set in any map, a pair's place among the pairs of its expert is the
 // number of lower tokens whose map holds it.  An expert given twice to one
 // token is an error.
-__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint32_t (*tmask)[kMaxE / 32]) {
+__device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint32_t (*tmask)[kMaxE / 32], int sh) {
   const int lane = pq::lane_id();
   const int P = a.M * a.top_k;
   const bool act = lane < P;
@@ -242,19 +278,20 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
   const int u = __shfl(excl, w, pq::kWave) + __popc((uint32_t)__shfl((int)word, w, pq::kWave) & (bit - 1u));
   if (act) {
     // n <= M and slot < M; a duplicate shares its slot with the first copy
+    const int us = u + sh;                        // after the shared entry
     if (slot == 0 && !dup) {
-      r.uexp[u] = id;
-      r.unp[u] = n;
+      r.uexp[us] = id;
+      r.unp[us] = n;
     }
     if (!dup) {
-      r.upairs[u][slot] = lane;
-      r.items[below + slot] = u | slot << 8;
+      r.upairs[us][slot] = lane;
+      r.items[sh * a.M + below + slot] = us | slot << 8;
     }
     if (dup && blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
   }
   if (lane == 0) {
-    r.nU = total;
-    r.nitems = nitems;
+    r.nU = total + sh;
+    r.nitems = nitems + sh * a.M;
   }
 }
 
@@ -267,7 +304,7 @@ __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq:
   const int I = a.I;
   const int p = ufl(r.upairs[uu][t]);
   const int nvec = I / 8;
-  const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(a.M * a.top_k * I * 2));
+  const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(a.P2 * I * 2));
   constexpr int kSB = 4;
   for (int v0 = 0; v0 < nvec; v0 += kSB * pq::kWave) {
     uint4 raw[kSB];
@@ -314,65 +351,145 @@ __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq:
 // One routed token: its top-k experts are distinct, so the union is its slots
 // in slot order (the order of the union entries changes no result), written
 // by the routing wave itself — no bitmap and no block barrier in between.
-__device__ void single_token_union(const MoeArgs& a, Route& r) {
+__device__ void single_token_union(const MoeArgs& a, Route& r, int sh) {
   const int lane = pq::lane_id();
   if (lane < a.top_k) {
-    r.uexp[lane] = r.ids[lane];                  // written by this same lane
-    r.unp[lane] = 1;
-    r.upairs[lane][0] = lane;
-    r.items[lane] = lane;
+    const int us = lane + sh;                    // after the shared entry
+    r.uexp[us] = r.ids[lane];                    // written by this same lane
+    r.unp[us] = 1;
+    r.upairs[us][0] = lane;
+    r.items[sh + lane] = us;
   }
   if (lane == 0) {
-    r.nU = a.top_k;
-    r.nitems = a.top_k;
+    r.nU = a.top_k + sh;
+    r.nitems = a.top_k + sh;
+  }
+}
+
+// The shared expert as union entry 0 (expert id E stands for it): every token
+// is routed to it once, as pair P + m; its items come first in union order.
+// Independent of the routing, so every block sets it up at the start.
+__device__ void shared_entry(const MoeArgs& a, Route& r) {
+  const int lane = pq::lane_id();
+  if (lane < a.M) {
+    r.upairs[0][lane] = a.M * a.top_k + lane;
+    r.items[lane] = lane << 8;
+  }
+  if (lane == 0) {
+    r.uexp[0] = a.E;
+    r.unp[0] = a.M;
+  }
+}
+
+// Weights of union entry expert e (e == E with a shared expert: that one).
+template <bool EXT>
+__device__ __forceinline__ const uint8_t* gu_weights(const MoeArgs& a, int e) {
+  return EXT && e == a.E ? a.sw13 : a.w13 + (size_t)e * 2 * a.I * a.H;
+}
+template <bool EXT>
+__device__ __forceinline__ const float* gu_scales(const MoeArgs& a, int e) {
+  return EXT && e == a.E ? a.ss13 : a.s13 + (size_t)e * 2 * a.I * (a.H / pq::kBlock);
+}
+template <bool EXT>
+__device__ __forceinline__ const uint8_t* dn_weights(const MoeArgs& a, int e) {
+  return EXT && e == a.E ? a.sw2 : a.w2 + (size_t)e * a.H * a.I;
+}
+template <bool EXT>
+__device__ __forceinline__ const float* dn_scales(const MoeArgs& a, int e) {
+  return EXT && e == a.E ? a.ss2 : a.s2 + (size_t)e * a.H * (a.I / pq::kBlock);
+}
+
+// Router rows [e0, e1) of this block for every token: l[m][e] = sum_k x[m][k]
+// Wr[e][k] from the bf16 values, fp32 accumulation (each lane sums its 8-value
+// slices of every 1 KB chunk in chunk order, then the wave adds the lanes in a
+// fixed tree).  Published inverted (a zero word means "not yet written") with
+// agent-coherent stores; the routing waves of every block wait for them.
+template <int TP>
+__device__ void router_rows(const MoeArgs& a, int e) {
+  const int lane = pq::lane_id();
+  const int H = a.H;
+  const uint32_t rowb = (uint32_t)H * 2u;
+  const int nck = (int)((rowb + pq::kChunk - 1) / pq::kChunk);
+  const pq::rsrc_t wrr = pq::make_rsrc(a.wr + (size_t)e * H, rowb);
+  const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)a.M * rowb);
+  float acc[TP];
+#pragma unroll
+  for (int m = 0; m < TP; ++m) acc[m] = 0.0f;
+  constexpr int kB = TP <= 2 ? 4 : TP == 4 ? 2 : 1;   // chunks per batch of loads
+  for (int c0 = 0; c0 < nck; c0 += kB) {
+    uint4 wv[kB], xv[kB][TP];
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      const uint32_t off = (uint32_t)((c0 + q) * pq::kChunk) + 16u * (uint32_t)lane;
+      const bool ok = c0 + q < nck && off < rowb;
+      wv[q] = pq::buf_load16(wrr, ok ? off : pq::kOOB);
+#pragma unroll
+      for (int m = 0; m < TP; ++m)
+        xv[q][m] = pq::buf_load16(xr, ok && m < a.M ? (uint32_t)m * rowb + off : pq::kOOB);
+    }
+#pragma unroll
+    for (int q = 0; q < kB; ++q) {
+      const uint32_t w4[4] = {wv[q].x, wv[q].y, wv[q].z, wv[q].w};
+#pragma unroll
+      for (int m = 0; m < TP; ++m) {
+        const uint32_t x4[4] = {xv[q][m].x, xv[q][m].y, xv[q][m].z, xv[q][m].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pq::bf16x2, w4[i]),
+                                                   __builtin_bit_cast(pq::bf16x2, x4[i]), acc[m], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < TP; ++m) {
+    if (m < a.M) {
+      const float l = pq::wave_sum(acc[m]);
+      if (lane == 0) {
+        uint32_t inv = ~__float_as_uint(l);
+        if (inv == 0u) inv = ~0x7FC00000u;          // the all-ones NaN: keep the word non-zero
+        pq::st_agent_u32(a.lx + (size_t)m * a.E + e, inv);
+        if (a.logits_out) a.logits_out[(size_t)m * a.E + e] = l;
+      }
+    }
   }
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// The barrier kernel: all gate_up units of the call, then one grid-wide
-// release, then every block stages all of h and runs its down rows.  Fewer
-// instructions per step than the stream kernel below, which pays off when the
-// call streams few experts (one or two tokens).
-// TP: compile-time bound on the (token, slot) pairs routed to one expert in a
-// call (the smallest power of two >= M), so the per-pair loops unroll tightly.
-template <int TP>
-__global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ Route route;
-  __shared__ int s_last;
-  __shared__ uint32_t s_tmask[kMaxM][kMaxE / 32];   // routed-expert bitmap of each token
-  __shared__ uint32_t s_next;     // next gate_up unit of this block
-  __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
-  __shared__ uint32_t s_epoch;    // value the release flags take in this call
-
-  pq::WsHeader* hdr = reinterpret_cast<pq::WsHeader*>(a.ws);
-  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + pq::kWsCounterOff);   // one line per block
-
+// Phases A and B of both kernels: the router rows of this block (when the
+// logits are computed in the launch), the routing, the live quantisation of
+// x into LDS and the union of the routed experts (after the shared entry).
+// On return the quantised x is visible to the whole block; the routes are
+// visible once *ready is non-zero: at once when the logits or the ids are
+// given, else when the routing waves have waited for every block's logits
+// and ranked them (the other waves meanwhile stream the shared expert).
+template <int TP, bool EXT>
+__device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, uint32_t (*s_tmask)[kMaxE / 32],
+                                               uint32_t* s_ready, uint32_t* s_rdone, uint8_t* xa, float* xsc,
+                                               pq::WsHeader* hdr) {
   const int lane = pq::lane_id();
   const int wv = pq::wave_id();
-  const int gw = ufl((int)blockIdx.x * kWaves + wv);
-  const long T = (long)gridDim.x * kWaves;
-  const int H = a.H, I = a.I, K = a.top_k;
-  const int P = a.M * K;
-  const int nbH = H / pq::kBlock, nbI = I / pq::kBlock;
-  const int nchH = (H + pq::kChunk - 1) / pq::kChunk;
-  const int nchI = (I + pq::kChunk - 1) / pq::kChunk;
-  const uint32_t lane16 = 16u * (uint32_t)lane;
-  const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
+  const int H = a.H;
+  const int P = a.M * a.top_k;
+  const int G = (int)gridDim.x;
+  const bool router = EXT && a.router;
+  const int sh = EXT ? a.sh : 0;
 
-  uint8_t* act = smem;                                           // x codes, later h codes
-  float* acts = reinterpret_cast<float*>(smem + a.xs_off);       // their scales
-
-  // ---- x loads first (independent of routing); the waves that do not route
-  //      quantise x while waves 0..M-1 rank the logits ------------------------
-  const int nrt = a.routed ? a.M : 1;               // routing waves
+  // router rows of this block, by its top waves (before they quantise, so the
+  // logits are published as early as possible)
+  const int e0 = router ? pq::split_start(a.E, G, (int)blockIdx.x) : 0;
+  const int e1 = router ? pq::split_start(a.E, G, (int)blockIdx.x + 1) : 0;
+  const int nrw = e1 - e0 < kWaves / 2 ? e1 - e0 : kWaves / 2;
+  // waves that route before quantising (given logits or ids)
+  const int nrt = router ? 0 : (a.routed ? a.M : 1);
   const long totx8 = (long)a.M * H / 8;
+  const int qthreads = kThreads - (nrt + nrw) * pq::kWave;
   // when the other waves cannot cover x in one pass, every wave takes a share
-  // (the routing waves after routing)
-  const bool xq_all = totx8 > (long)(kThreads - nrt * pq::kWave);
-  const int tq = xq_all ? (int)threadIdx.x : (int)threadIdx.x - nrt * pq::kWave;   // < 0: routing wave only
-  const int nq = xq_all ? kThreads : kThreads - nrt * pq::kWave;
+  // (the routing and router waves after their own work)
+  const bool xq_all = totx8 > (long)qthreads;
+  const bool qwave = wv >= nrt && wv < kWaves - nrw;
+  const int tq = xq_all ? (int)threadIdx.x : (qwave ? (int)threadIdx.x - nrt * pq::kWave : -1);
+  const int nq = xq_all ? kThreads : qthreads;
   const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
   // enough loads in flight for the whole of x at H = 6144 up to M = 4 (16 bytes each)
   constexpr int kXPre = TP == 1 ? 1 : TP == 2 ? 2 : TP == 4 ? 4 : 8;
@@ -382,21 +499,25 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     const long t = (long)it * nq + tq;
     xraw[it] = pq::buf_load16(xr, tq >= 0 && t < totx8 ? (uint32_t)t * 16u : pq::kOOB);
   }
-
-  if (threadIdx.x == 0) {       // block counters; first used after the barriers below
-    s_next = 0u;
-    s_arrive = 0u;
-    s_epoch = pq::ld_agent_u32(&hdr->epoch) + 1u;   // this call's flag value
-  }
   if (threadIdx.x < kMaxM * kMaxE / 32) (&s_tmask[0][0])[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) {
+    *s_ready = router ? 0u : 1u;
+    *s_rdone = 0u;
+  }
+  if (sh && wv == 0) shared_entry(a, route);
 
-  // ---- A. routing (waves 0..M-1, one token each) -----------------------------
+  // ---- A. routing from given logits (waves 0..M-1, one token each), or the
+  //      router rows ---------------------------------------------------------
   const bool one_token = a.routed && a.M == 1;       // block-uniform
-  if (a.routed) {
+  if (router) {
+    const int k = kWaves - 1 - wv;
+    if (k < nrw)
+      for (int e = e0 + k; e < e1; e += nrw) router_rows<TP>(a, e);
+  } else if (a.routed) {
     if (wv < a.M) {
-      if (a.E <= 256) route_token<4>(a, route, wv);
-      else route_token<16>(a, route, wv);
-      if (one_token) single_token_union(a, route);
+      if (a.E <= 256) route_token<4, false>(a, route, wv);
+      else route_token<16, false>(a, route, wv);
+      if (one_token) single_token_union(a, route, sh);
     }
   } else if (wv == 0 && lane < P) {
     int id = a.topk_ids[lane];
@@ -417,10 +538,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       const bool valid = t < totx8;
       float v[8];
       pq::bf16x8_to_f32(raw, v);
-      const float s = pq::fp8_block_scale16(v, valid);
+      const float sc = pq::fp8_block_scale16(v, valid);
       if (valid) {
-        reinterpret_cast<uint2*>(act)[t] = pq::fp8_codes8(v, s);
-        if ((tq & 15) == 0) acts[(t * 8) / pq::kBlock] = s;
+        reinterpret_cast<uint2*>(xa)[t] = pq::fp8_codes8(v, sc);
+        if ((tq & 15) == 0) xsc[(t * 8) / pq::kBlock] = sc;
       }
     };
 #pragma unroll
@@ -432,41 +553,133 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     }
   }
 
-  __syncthreads();                            // routes and the quantised x visible
-  if (!one_token) {
-    if (wv == 0) build_union(a, route, hdr, s_tmask);
+  __syncthreads();                            // the quantised x (and given routes) visible
+  if (router) {
+    // routing waves: wait for every block's logits and rank them; wave 0 then
+    // builds the union once all of them are done and releases the routes
+    if (wv < a.M) {
+      if (a.E <= 256) route_token<4, true>(a, route, wv);
+      else route_token<16, true>(a, route, wv);
+      if (one_token) {
+        single_token_union(a, route, sh);
+        if (lane == 0) __hip_atomic_store(s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        if (lane == 0) __hip_atomic_fetch_add(s_rdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (wv == 0) {
+          while (ufl((int)__hip_atomic_load(s_rdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < a.M)
+            __builtin_amdgcn_s_sleep(1);
+          build_union(a, route, hdr, s_tmask, sh);
+          if (lane == 0) __hip_atomic_store(s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+  } else if (!one_token) {
+    if (wv == 0) build_union(a, route, hdr, s_tmask, sh);
     __syncthreads();
   }
-  const int nU = ufl(route.nU);
+}
+
+// Wait (wave-wide) until the routes of the call are visible.
+__device__ __forceinline__ void wait_routes(const uint32_t* s_ready) {
+  while (ufl((int)__hip_atomic_load(s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0)
+    __builtin_amdgcn_s_sleep(1);
+}
+
+// The barrier kernel: all gate_up units of the call, then one grid-wide
+// release, then every block stages all of h and runs its down rows.  Fewer
+// instructions per step than the stream kernel below, which pays off when the
+// call streams few experts (one or two tokens).
+// TP: compile-time bound on the (token, slot) pairs routed to one expert in a
+// call (the smallest power of two >= M), so the per-pair loops unroll tightly.
+template <int TP, bool EXT>
+__global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ Route route;
+  __shared__ int s_last;
+  __shared__ uint32_t s_tmask[kMaxM][kMaxE / 32];   // routed-expert bitmap of each token
+  __shared__ uint32_t s_next;     // next gate_up unit of this block
+  __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
+  __shared__ uint32_t s_epoch;    // value the release flags take in this call
+  __shared__ uint32_t s_ready;    // routes visible (set by the routing waves)
+  __shared__ uint32_t s_rdone;    // routing waves done
+
+  pq::WsHeader* hdr = reinterpret_cast<pq::WsHeader*>(a.ws);
+  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + pq::kWsCounterOff);   // one line per block
+
+  const int lane = pq::lane_id();
+  const int wv = pq::wave_id();
+  const int gw = ufl((int)blockIdx.x * kWaves + wv);
+  const long T = (long)gridDim.x * kWaves;
+  const int H = a.H, I = a.I, K = a.top_k;
+  const int P = a.M * K;
+  const int sh = EXT ? a.sh : 0;              // shared expert: union entry 0, pairs P .. P + M - 1
+  const int P2 = EXT ? a.P2 : P;
+  const bool router = EXT && a.router;
+  const int nbH = H / pq::kBlock, nbI = I / pq::kBlock;
+  const int nchH = (H + pq::kChunk - 1) / pq::kChunk;
+  const int nchI = (I + pq::kChunk - 1) / pq::kChunk;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
+
+  uint8_t* act = smem;                                           // x codes, later h codes
+  float* acts = reinterpret_cast<float*>(smem + a.xs_off);       // their scales
+
+  if (threadIdx.x == 0) {       // block counters; first used after the barriers below
+    s_next = 0u;
+    s_arrive = 0u;
+    s_epoch = pq::ld_agent_u32(&hdr->epoch) + 1u;   // this call's flag value
+  }
+  layer_prologue<TP, EXT>(a, route, s_tmask, &s_ready, &s_rdone, act, acts, hdr);
 
   // ---- C. gate_up + SiLU*up -------------------------------------------------
-  // The block owns the units [bu0, bu1) (union entry u, h-row i: one gate row
-  // and one up row); its waves take them one at a time from an LDS counter,
-  // so a wave whose loads issue later (the scheduler favours older waves)
-  // simply takes fewer.  Each wave keeps BDG chunk-steps in flight; every ring
-  // slot remembers its unit and chunk.
-  const int gu_units = nU * I;
-  const int bu0 = pq::split_start(gu_units, (int)gridDim.x, (int)blockIdx.x);
-  const int bu1 = pq::split_start(gu_units, (int)gridDim.x, (int)blockIdx.x + 1);
+  // Units (union entry u, h-row i: one gate row and one up row) are numbered
+  // u * I + i.  The block owns its share [sh0, sh0 + nsh) of the shared
+  // expert's units (entry 0; independent of the routing, so they go first)
+  // and its share [bu0, bu1) of the routed units (known once the routes are);
+  // its waves take them one at a time from an LDS counter, so a wave whose
+  // loads issue later (the scheduler favours older waves) simply takes fewer.
+  // Each wave keeps BDG chunk-steps in flight; every ring slot remembers its
+  // unit and chunk.
+  const int sh0 = pq::split_start(sh * I, (int)gridDim.x, (int)blockIdx.x);
+  const int nsh = pq::split_start(sh * I, (int)gridDim.x, (int)blockIdx.x + 1) - sh0;
+  int bu0 = 0, bu1 = 0;
+  bool routes_known = false;
+  auto know_routes = [&]() {
+    if (!routes_known) {
+      if (router) wait_routes(&s_ready);
+      const int nur = ufl(route.nU) - sh;
+      bu0 = pq::split_start(nur * I, (int)gridDim.x, (int)blockIdx.x);
+      bu1 = pq::split_start(nur * I, (int)gridDim.x, (int)blockIdx.x + 1);
+      routes_known = true;
+    }
+  };
+  if (!router) know_routes();         // the routes are visible already
 
   uint4 wb[BDG][2];
   float sb[BDG][2];
   int su[BDG], sch[BDG];              // unit (-1: none) and chunk of each slot
-  int iunit = bu0 - 1, ic = nchH;   // issue cursor
+  int iunit = -1, ic = nchH;          // issue cursor
   bool more = true;
   int cur_e = -1;
   pq::rsrc_t gwr = pq::make_rsrc(a.w13, 0u), gsr = pq::make_rsrc(a.s13, 0u);
   auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], int& su_q, int& sch_q) {
     if (ic == nchH && more) {       // take the block's next unit
-      iunit = bu0 + wave_claim(&s_next);
+      const int c = wave_claim(&s_next);
+      if (c < nsh) {
+        iunit = sh0 + c;
+      } else {
+        know_routes();
+        const int r = bu0 + (c - nsh);
+        more = r < bu1;
+        iunit = sh * I + r;
+      }
       ic = 0;
-      more = iunit < bu1;
       if (more) {
         const int e = ufl(route.uexp[iunit / I]);
         if (e != cur_e) {
           cur_e = e;
-          gwr = pq::make_rsrc(a.w13 + (size_t)e * 2 * I * H, (uint32_t)(2 * I * H));
-          gsr = pq::make_rsrc(a.s13 + (size_t)e * 2 * I * nbH, (uint32_t)(2 * I * nbH * 4));
+          gwr = pq::make_rsrc(gu_weights<EXT>(a, e), (uint32_t)(2 * I * H));
+          gsr = pq::make_rsrc(gu_scales<EXT>(a, e), (uint32_t)(2 * I * nbH * 4));
         }
       }
     }
@@ -499,7 +712,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
 #pragma unroll
       for (int t = 0; t < TP; ++t) {
         pr[t] = ufl(route.upairs[uu][t]);
-        pm[t] = pr[t] / K;
+        pm[t] = pr[t] < P ? pr[t] / K : pr[t] - P;   // the shared expert's pair P + m is token m
       }
     };
     for (;;) {
@@ -556,13 +769,15 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   // flag line (value = this call's epoch, so a flag left by an earlier call
   // never matches).
   pq::wait_vm();
+  know_routes();                      // (every wave's last claim already waited)
+  const int nU = ufl(route.nU);
+  const int gu_units = nU * I;
   uint32_t last = 0;
   if (lane == 0) {
     const uint32_t before = atomicAdd(&s_arrive, 1u);
-    if (before == (uint32_t)(kWaves - 1) && bu1 > bu0) {
-      const uint32_t rows = (uint32_t)(bu1 - bu0);
+    const uint32_t rows = (uint32_t)(nsh + bu1 - bu0);
+    if (before == (uint32_t)(kWaves - 1) && rows > 0u)
       last = pq::atomic_add_relaxed(&hdr->done, rows) + rows == (uint32_t)gu_units;
-    }
   }
   if (__builtin_amdgcn_readlane((int)last, 0)) {
     const uint32_t ep = s_epoch;
@@ -590,8 +805,8 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   pq::rsrc_t dwr, dsr;
   auto set_dn_expert = [&]() {
     const int e = ufl(route.uexp[ju < nU ? ju : 0]);
-    dwr = pq::make_rsrc(a.w2 + (size_t)e * H * I, (uint32_t)(H * I));
-    dsr = pq::make_rsrc(a.s2 + (size_t)e * H * nbI, (uint32_t)(H * nbI * 4));
+    dwr = pq::make_rsrc(dn_weights<EXT>(a, e), (uint32_t)(H * I));
+    dsr = pq::make_rsrc(dn_scales<EXT>(a, e), (uint32_t)(H * nbI * 4));
   };
   set_dn_expert();
   auto issue_dn = [&](uint4& w, float& s) {
@@ -621,8 +836,8 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   {
     // 8 values per lane, 16 lanes per 128-value block (the layout of the
     // activation quantiser); agent-coherent 16-byte loads, a batch in flight
-    const int nvec = P * I / 8;
-    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P * I * 2));
+    const int nvec = P2 * I / 8;
+    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P2 * I * 2));
     constexpr int kBatch = 2;
     for (int t0 = 0; t0 < nvec; t0 += kBatch * kThreads) {
       uint4 raw[kBatch];
@@ -686,7 +901,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
         for (int t = 0; t < TP; ++t) {
           if (t < cnp) {
             const float y = pq::wave_sum(acc[t]);
-            if (lane == 0) ybuf[cr * P + pr[t]] = y;
+            if (lane == 0) ybuf[cr * P2 + pr[t]] = y;
           }
           acc[t] = 0.0f;
         }
@@ -716,7 +931,8 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   for (int idx = threadIdx.x; idx < (r1 - r0) * a.M; idx += kThreads) {
     const int rl = idx / a.M, m = idx - (idx / a.M) * a.M;
     float o = 0.0f;
-    for (int j = 0; j < K; ++j) o = fmaf(route.w[m * K + j], ybuf[rl * P + m * K + j], o);
+    for (int j = 0; j < K; ++j) o = fmaf(route.w[m * K + j], ybuf[rl * P2 + m * K + j], o);
+    if (sh) o += ybuf[rl * P2 + P + m];              // the shared expert, weight 1, last
     a.out[(size_t)m * H + r0 + rl] = pq::bf16_rne(o);
   }
 
@@ -728,6 +944,8 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   }
   __syncthreads();
   if (s_last) {
+    if (router)
+      for (int t = threadIdx.x; t < a.M * a.E; t += kThreads) pq::st_agent_u32(a.lx + t, 0u);
     if (threadIdx.x == 0) {
       pq::atomic_store_relaxed(&hdr->done, 0u);
       pq::atomic_store_relaxed(&hdr->exit_count, 0u);
@@ -739,7 +957,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
 // The stream kernel: no grid-wide barrier; see section C.
 // TP: compile-time bound on the (token, slot) pairs routed to one expert in a
 // call (the smallest power of two >= M), so the per-pair loops unroll tightly.
-template <int TP>
+template <int TP, bool EXT>
 __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ Route route;
@@ -750,6 +968,8 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   __shared__ uint32_t s_next;      // gate_up units of this block handed out
   __shared__ uint32_t s_dnext;     // down units of this block handed out
   __shared__ uint32_t s_gu_busy;   // waves still consuming gate_up steps
+  __shared__ uint32_t s_ready;     // routes visible (set by the routing waves)
+  __shared__ uint32_t s_rdone;     // routing waves done
 
   pq::WsHeader* hdr = reinterpret_cast<pq::WsHeader*>(a.ws);
 
@@ -757,6 +977,9 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   const int wv = pq::wave_id();
   const int H = a.H, I = a.I, K = a.top_k;
   const int P = a.M * K;
+  const int sh = EXT ? a.sh : 0;              // shared expert: union entry 0, pairs P .. P + M - 1
+  const int P2 = EXT ? a.P2 : P;
+  const bool router = EXT && a.router;
   const int nbH = H / pq::kBlock, nbI = I / pq::kBlock;
   const int nchH = (H + pq::kChunk - 1) / pq::kChunk;
   const uint32_t lane16 = 16u * (uint32_t)lane;
@@ -764,28 +987,9 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
 
   uint8_t* xa = smem;                                          // x codes   [M][H]
   float* xsc = reinterpret_cast<float*>(smem + a.xs_off);      // x scales  [M][H/128]
-  uint8_t* ha = smem + a.ha_off;                               // h codes   [P][I]
-  float* hsc = reinterpret_cast<float*>(smem + a.hs_off);      // h scales  [P][I/128]
-  float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);     // y partials [row][P]
-
-  // ---- x loads first (independent of routing); the waves that do not route
-  //      quantise x while waves 0..M-1 rank the logits ------------------------
-  const int nrt = a.routed ? a.M : 1;               // routing waves
-  const long totx8 = (long)a.M * H / 8;
-  // when the other waves cannot cover x in one pass, every wave takes a share
-  // (the routing waves after routing)
-  const bool xq_all = totx8 > (long)(kThreads - nrt * pq::kWave);
-  const int tq = xq_all ? (int)threadIdx.x : (int)threadIdx.x - nrt * pq::kWave;   // < 0: routing wave only
-  const int nq = xq_all ? kThreads : kThreads - nrt * pq::kWave;
-  const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
-  // enough loads in flight for the whole of x at H = 6144 up to M = 4 (16 bytes each)
-  constexpr int kXPre = TP == 1 ? 1 : TP == 2 ? 2 : TP == 4 ? 4 : 8;
-  uint4 xraw[kXPre];
-#pragma unroll
-  for (int it = 0; it < kXPre; ++it) {
-    const long t = (long)it * nq + tq;
-    xraw[it] = pq::buf_load16(xr, tq >= 0 && t < totx8 ? (uint32_t)t * 16u : pq::kOOB);
-  }
+  uint8_t* ha = smem + a.ha_off;                               // h codes   [P2][I]
+  float* hsc = reinterpret_cast<float*>(smem + a.hs_off);      // h scales  [P2][I/128]
+  float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);     // y partials [row][P2]
 
   if (threadIdx.x == 0) {       // block counters; first used after the barriers below
     s_next = 0u;
@@ -794,56 +998,7 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
     s_gu_busy = (uint32_t)kWaves;
   }
   if (threadIdx.x < kMaxUnion) s_staged[threadIdx.x] = 0u;
-  if (threadIdx.x < kMaxM * kMaxE / 32) (&s_tmask[0][0])[threadIdx.x] = 0u;
-
-  // ---- A. routing (waves 0..M-1, one token each) -----------------------------
-  const bool one_token = a.routed && a.M == 1;       // block-uniform
-  if (a.routed) {
-    if (wv < a.M) {
-      if (a.E <= 256) route_token<4>(a, route, wv);
-      else route_token<16>(a, route, wv);
-      if (one_token) single_token_union(a, route);
-    }
-  } else if (wv == 0 && lane < P) {
-    int id = a.topk_ids[lane];
-    if (id < 0 || id >= a.E) {
-      if (blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
-      id = 0;
-    }
-    route.ids[lane] = id;
-    route.w[lane] = a.topk_w[lane];
-  }
-
-  // ---- B. live activation quantisation into LDS ------------------------------
-  if (tq >= 0) {
-    const int iters = (int)((totx8 + nq - 1) / nq);
-    // 16 lanes share a scale, so whole waves run each step; the preloaded
-    // steps are unrolled so the raw values stay in registers
-    auto quant = [&](const uint4& raw, long t) {
-      const bool valid = t < totx8;
-      float v[8];
-      pq::bf16x8_to_f32(raw, v);
-      const float s = pq::fp8_block_scale16(v, valid);
-      if (valid) {
-        reinterpret_cast<uint2*>(xa)[t] = pq::fp8_codes8(v, s);
-        if ((tq & 15) == 0) xsc[(t * 8) / pq::kBlock] = s;
-      }
-    };
-#pragma unroll
-    for (int it = 0; it < kXPre; ++it)
-      if (it < iters) quant(xraw[it], (long)it * nq + tq);
-    for (int it = kXPre; it < iters; ++it) {
-      const long t = (long)it * nq + tq;
-      quant(pq::buf_load16(xr, t < totx8 ? (uint32_t)t * 16u : pq::kOOB), t);
-    }
-  }
-
-  __syncthreads();                            // routes and the quantised x visible
-  if (!one_token) {
-    if (wv == 0) build_union(a, route, hdr, s_tmask);
-    __syncthreads();
-  }
-  const int nU = ufl(route.nU);
+  layer_prologue<TP, EXT>(a, route, s_tmask, &s_ready, &s_rdone, xa, xsc, hdr);
 
   // ---- C. per wave: gate_up units, then down units, no block barrier -------
   // gate_up unit (union entry u, h-row i) = gate row i and up row i of expert
@@ -857,12 +1012,22 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   // needs is quantised into LDS by the first wave that needs it (per pair),
   // once every block has stored it: the stager polls the values themselves,
   // which are stored bit-inverted so that a zero word means "not yet written".
+  // The shared expert is entry 0, so its units are the first I of the list and
+  // need no routes; a wave that reaches the routed units waits for them.
   const int G = (int)gridDim.x;
-  const int gu_total = nU * I;
+  int gu_total = sh * I;               // the whole list once the routes are known
+  bool routes_known = false;
+  auto know_routes = [&]() {
+    if (!routes_known) {
+      if (router) wait_routes(&s_ready);
+      gu_total = ufl(route.nU) * I;
+      routes_known = true;
+    }
+  };
+  if (!router) know_routes();         // the routes are visible already
   const int r0 = pq::split_start(H, G, (int)blockIdx.x);
   const int r1 = pq::split_start(H, G, (int)blockIdx.x + 1);
   const int nrows = r1 - r0;
-  const int dn_total = nU * nrows;
   const int nchI = (I + pq::kChunk - 1) / pq::kChunk;
 
   // gate_up: a ring of DG steps (one 1 KB chunk of the gate row and of the up
@@ -877,6 +1042,7 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
     auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], uint32_t& d) {
       if (cstep == nchH && more) {            // take the block's next unit
         const int v = (int)blockIdx.x + wave_claim(&s_next) * G;
+        if (v >= sh * I) know_routes();
         more = v < gu_total;
         if (more) {
           ucur = v / I;
@@ -885,8 +1051,8 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
           const int e = ufl(route.uexp[ucur]);
           if (e != ce) {
             ce = e;
-            wr = pq::make_rsrc(a.w13 + (size_t)e * 2 * I * H, (uint32_t)(2 * I * H));
-            sr = pq::make_rsrc(a.s13 + (size_t)e * 2 * I * nbH, (uint32_t)(2 * I * nbH * 4));
+            wr = pq::make_rsrc(gu_weights<EXT>(a, e), (uint32_t)(2 * I * H));
+            sr = pq::make_rsrc(gu_scales<EXT>(a, e), (uint32_t)(2 * I * nbH * 4));
           }
         }
       }
@@ -916,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
           pr[t] = ufl(route.upairs[uu][t]);
-          pm[t] = pr[t] / K;
+          pm[t] = pr[t] < P ? pr[t] / K : pr[t] - P;   // the shared expert's pair P + m is token m
         }
       }
       const uint32_t off = (uint32_t)(step * pq::kChunk) + lane16;
@@ -966,6 +1132,9 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
     }
   }
   if (lane == 0) atomicSub(&s_gu_busy, 1u);   // this wave no longer reads x
+  know_routes();                               // (its last claim already waited)
+  const int nU = ufl(route.nU);
+  const int dn_total = nU * nrows;
 
   // h staging: the (entry, pair) items of the block are quantised into LDS in
   // union order, each by the wave that claims it; a wave out of gate_up units
@@ -1006,8 +1175,8 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
           const int e = ufl(route.uexp[ucur]);
           if (e != ce) {
             ce = e;
-            wr = pq::make_rsrc(a.w2 + (size_t)e * H * I, (uint32_t)(H * I));
-            sr = pq::make_rsrc(a.s2 + (size_t)e * H * nbI, (uint32_t)(H * nbI * 4));
+            wr = pq::make_rsrc(dn_weights<EXT>(a, e), (uint32_t)(H * I));
+            sr = pq::make_rsrc(dn_scales<EXT>(a, e), (uint32_t)(H * nbI * 4));
           }
         }
       }
@@ -1051,7 +1220,7 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
         for (int t = 0; t < TP; ++t) {
           if (t < cnp) {
             const float y = pq::wave_sum(acc[t]);
-            if (lane == 0) ybuf[row * P + pr[t]] = y;
+            if (lane == 0) ybuf[row * P2 + pr[t]] = y;
           }
           acc[t] = 0.0f;
         }
@@ -1096,7 +1265,8 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   for (int idx = threadIdx.x; idx < nrows * a.M; idx += kThreads) {
     const int rl = idx / a.M, m = idx - (idx / a.M) * a.M;
     float o = 0.0f;
-    for (int j = 0; j < K; ++j) o = fmaf(route.w[m * K + j], ybuf[rl * P + m * K + j], o);
+    for (int j = 0; j < K; ++j) o = fmaf(route.w[m * K + j], ybuf[rl * P2 + m * K + j], o);
+    if (sh) o += ybuf[rl * P2 + P + m];              // the shared expert, weight 1, last
     a.out[(size_t)m * H + r0 + rl] = pq::bf16_rne(o);
   }
 
@@ -1111,10 +1281,12 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   }
   __syncthreads();
   if (s_last) {
-    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P * I * 2));
-    const int nz = P * I / 8;
+    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P2 * I * 2));
+    const int nz = P2 * I / 8;
     for (int t = threadIdx.x; t < nz; t += kThreads)
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, hr, t * 16, 0, kAuxSC1);
+    if (router)
+      for (int t = threadIdx.x; t < a.M * a.E; t += kThreads) pq::st_agent_u32(a.lx + t, 0u);
     if (threadIdx.x == 0) pq::atomic_store_relaxed(&hdr->exit_count, 0u);
   }
 }
@@ -1151,13 +1323,20 @@ int moe_path(int M) {
 // h reuses the x region once the block is past gate_up.  The workspace covers
 // both kernels: the stream kernel's h in the zero-between-calls region, the
 // barrier kernel's in the data region.
-int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePlan* p) {
+// The logit exchange sits at the end of the zero-between-calls region.
+constexpr size_t kLxBytes = (size_t)kMaxM * kMaxE * 4;
+constexpr size_t kWsLxOff = pq::kWsZeroOff + pq::kWsZeroBytes - kLxBytes;
+
+int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePlan* p, int sh = 1) {
   if (M < 1 || M > kMaxM || top_k < 1 || top_k > kMaxTopK || E < top_k || E > kMaxE) return PQ_ERR_SHAPE;
   if (H < pq::kBlock || H % pq::kBlock || H > 16384 || I < pq::kBlock || I % pq::kBlock || I > 16384)
     return PQ_ERR_SHAPE;
-  const size_t P = (size_t)M * top_k;
+  // pairs: (token, slot) plus, with a shared expert, one per token; the
+  // workspace is always sized for the shared expert
+  const size_t P = (size_t)M * top_k + (size_t)sh * M;
+  const size_t Pws = (size_t)M * top_k + M;
   if ((size_t)2 * I * H > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
-  if (P * I * 2 > pq::kWsZeroBytes) return PQ_ERR_SHAPE;
+  if (Pws * I * 2 > pq::kWsZeroBytes - kLxBytes) return PQ_ERR_SHAPE;
   const size_t xb = pqhost::align_up((size_t)M * H, 16), xsb = pqhost::align_up((size_t)M * (H / pq::kBlock) * 4, 16);
   const size_t hb = pqhost::align_up(P * I, 16), hsb = pqhost::align_up(P * (I / pq::kBlock) * 4, 16);
   p->lds = 0;
@@ -1183,13 +1362,13 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePl
     }
   }
   p->off_h = path == kPathStream ? pq::kWsZeroOff : pq::kWsDataOff;
-  p->ws_total = pqhost::align_up(pq::kWsDataOff + P * I * 2, 256);
+  p->ws_total = pqhost::align_up(pq::kWsDataOff + Pws * I * 2, 256);
   return PQ_OK;
 }
 
-template <int TP, bool STREAM>
+template <int TP, bool STREAM, bool EXT>
 int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& dev, hipStream_t stream) {
-  auto kern = STREAM ? moe_stream_kernel<TP> : moe_barrier_kernel<TP>;
+  auto kern = STREAM ? moe_stream_kernel<TP, EXT> : moe_barrier_kernel<TP, EXT>;
   static bool attr_set = false;
   if (!attr_set) {
     PQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1208,9 +1387,13 @@ int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& de
   return PQ_OK;
 }
 
+// EXT: the router GEMV or a shared expert in the launch (the plain layer is
+// compiled without their code, so its registers are as before)
 template <int TP>
 int launch_moe_path(int path, const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& dev, hipStream_t s) {
-  return path == kPathStream ? launch_moe<TP, true>(a, pl, dev, s) : launch_moe<TP, false>(a, pl, dev, s);
+  if (a.router || a.sh)
+    return path == kPathStream ? launch_moe<TP, true, true>(a, pl, dev, s) : launch_moe<TP, false, true>(a, pl, dev, s);
+  return path == kPathStream ? launch_moe<TP, true, false>(a, pl, dev, s) : launch_moe<TP, false, false>(a, pl, dev, s);
 }
 
 }  // namespace
@@ -1223,33 +1406,48 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k) {
   return pl.ws_total;
 }
 
-int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits, int32_t* topk_ids,
-                     float* topk_w, int E, int top_k, int I, const uint8_t* w13, const float* s13,
-                     const uint8_t* w2, const float* s2, uint16_t* out, uint16_t* h_dbg, uint8_t* hq_dbg,
-                     float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
+int moe_decode_layer_ex(const uint16_t* x, int M, int H, const uint16_t* router_w, float* router_logits,
+                        int32_t* topk_ids, float* topk_w, int E, int top_k, int I, const uint8_t* w13,
+                        const float* s13, const uint8_t* w2, const float* s2, const uint8_t* sh_w13,
+                        const float* sh_s13, const uint8_t* sh_w2, const float* sh_s2, uint16_t* out,
+                        uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !topk_ids || !topk_w || !w13 || !s13 || !w2 || !s2 || !out || !ws) return PQ_ERR_NULL;
+  const int nsh = (sh_w13 != nullptr) + (sh_s13 != nullptr) + (sh_w2 != nullptr) + (sh_s2 != nullptr);
+  if (nsh != 0 && nsh != 4) return PQ_ERR_NULL;      // all four shared-expert tensors or none
+  const int sh = nsh == 4 ? 1 : 0;
   MoePlan pl;
   const int path = moe_path(M);
-  int st = moe_plan(M, H, I, E, top_k, 0, path, &pl);   // shape checks (device independent)
+  int st = moe_plan(M, H, I, E, top_k, 0, path, &pl, sh);   // shape checks (device independent)
   if (st != PQ_OK) return st;
-  const void* ptrs[] = {x, router_logits, topk_ids, topk_w, w13, s13, w2, s2, out, h_dbg, hq_dbg, hs_dbg, ws};
+  const void* ptrs[] = {x, router_w, router_logits, topk_ids, topk_w, w13, s13, w2, s2,
+                        sh_w13, sh_s13, sh_w2, sh_s2, out, h_dbg, hq_dbg, hs_dbg, ws};
   for (const void* q : ptrs)
     if (q && !pqhost::aligned16(q)) return PQ_ERR_ALIGN;
+  if (router_w && (size_t)E * H * 2 > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
   if (ws_bytes < pl.ws_total) return PQ_ERR_WORKSPACE;
   pqhost::DeviceInfo dev;
   st = pqhost::current_device_info(&dev);
   if (st != PQ_OK) return st;
-  st = moe_plan(M, H, I, E, top_k, dev.num_cus, path, &pl);
+  st = moe_plan(M, H, I, E, top_k, dev.num_cus, path, &pl, sh);
   if (st != PQ_OK) return st;
 
   MoeArgs a;
-  a.x = x; a.logits = router_logits; a.topk_ids = topk_ids; a.topk_w = topk_w;
+  a.x = x;
+  a.wr = router_w;
+  a.logits = router_w ? nullptr : router_logits;
+  a.logits_out = router_w ? router_logits : nullptr;
+  a.lx = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kWsLxOff);
+  a.sw13 = sh_w13; a.ss13 = sh_s13; a.sw2 = sh_w2; a.ss2 = sh_s2;
+  a.topk_ids = topk_ids; a.topk_w = topk_w;
   a.w13 = w13; a.s13 = s13; a.w2 = w2; a.s2 = s2; a.out = out;
   a.h_dbg = h_dbg; a.hq_dbg = hq_dbg; a.hs_dbg = hs_dbg;
   a.ws = reinterpret_cast<uint8_t*>(ws);
   a.hbuf = reinterpret_cast<uint16_t*>(a.ws + pl.off_h);
   a.M = M; a.H = H; a.I = I; a.E = E; a.top_k = top_k;
-  a.routed = router_logits != nullptr;
+  a.router = router_w != nullptr;
+  a.routed = router_w != nullptr || router_logits != nullptr;
+  a.sh = sh;
+  a.P2 = M * top_k + sh * M;
   a.spin_limit = kSpinLimit;
   a.xs_off = pl.xs_off; a.ha_off = pl.ha_off; a.hs_off = pl.hs_off; a.yb_off = pl.yb_off;
   a.alias = pl.alias;
@@ -1261,6 +1459,15 @@ int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits
   if (M == 2) return launch_moe_path<2>(path, a, pl, dev, s);
   if (M <= 4) return launch_moe_path<4>(path, a, pl, dev, s);
   return launch_moe_path<8>(path, a, pl, dev, s);
+}
+
+int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits, int32_t* topk_ids,
+                     float* topk_w, int E, int top_k, int I, const uint8_t* w13, const float* s13,
+                     const uint8_t* w2, const float* s2, uint16_t* out, uint16_t* h_dbg, uint8_t* hq_dbg,
+                     float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
+  return moe_decode_layer_ex(x, M, H, nullptr, const_cast<float*>(router_logits), topk_ids, topk_w, E, top_k, I,
+                             w13, s13, w2, s2, nullptr, nullptr, nullptr, nullptr, out, h_dbg, hq_dbg, hs_dbg, ws,
+                             ws_bytes, stream);
 }
 
 }  // extern "C"

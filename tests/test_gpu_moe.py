@@ -80,6 +80,21 @@ class Bank:
     def expert(self, e):
         return self.cpu[e]
 
+    def shared(self):
+        """A shared expert with the bank's shapes (drawn like a routed one under
+        its own tensor keys); returns the GPU tensors, keeps the oracle's."""
+        import torch
+        m13 = workloads.master_weights(2 * self.I, self.H, workload=self.wl, tensor=workloads.T_SH13,
+                                       seed=self.seed)
+        m2 = workloads.master_weights(self.H, self.I, workload=self.wl, tensor=workloads.T_SH2, seed=self.seed)
+        q13, s13 = self.pq.quantize_fp8(torch.from_numpy(m13).cuda())
+        q2, s2 = self.pq.quantize_fp8(torch.from_numpy(m2).cuda())
+        o13, os13 = oracle.block_quant_fp8(m13)
+        o2, os2 = oracle.block_quant_fp8(m2)
+        assert np.array_equal(q13.cpu().numpy(), o13) and np.array_equal(q2.cpu().numpy(), o2)
+        self.sh_cpu = (o13, os13, o2, os2)
+        return (q13, s13, q2, s2)
+
 
 def _check(pq, bank, x_bits, res, ref, M, k):
     ids = res["topk_ids"].cpu().numpy()
@@ -300,3 +315,147 @@ def test_moe_routing_ties_and_signed_zero(pq, E):
     assert np.max(np.abs(res["topk_w"].cpu().numpy() - w_ref)) <= 1e-6
     ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k)
     assert_gemv_close(bf16_to_np(res["out"]), ref["out"], ref["S"], f"ties E={E}")
+
+
+# ---------------------------------------------------------------------------
+# The steps either side of the routed layer in the same launch: the router
+# GEMV (bf16, native precision) and a shared expert added with weight 1.
+# ---------------------------------------------------------------------------
+
+def _check_shared(res, ref):
+    """The shared expert's h (SiLU bound) and its re-quantised codes."""
+    h = bf16_to_np(res["sh_h"])
+    assert_silu_close(h, ref["sh_h"], ref["sh_gate"], ref["sh_up"], ref["sh_S_gate"], ref["sh_S_up"], "shared h")
+    diff = np.mean(res["sh_hq"].cpu().numpy() != ref["sh_hq"])
+    assert diff <= 2e-3, f"{diff:.2e} of the shared expert's h codes differ"
+
+
+@pytest.mark.parametrize("M,E,H,I,k", [(1, 16, 512, 256, 4), (3, 24, 1024, 512, 8), (8, 32, 1024, 256, 8)])
+def test_moe_shared_expert_given_logits(pq, path, M, E, H, I, k):
+    import torch
+    bank = Bank(pq, E, H, I, seed=20 + M)
+    sh = bank.shared()
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=20 + M)
+    lg = workloads.router_logits(M, E, workload=workloads.MOE_LAYER, seed=20 + M)
+    ids, _ = oracle.route_topk(lg, k)
+    bank.fill(ids)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              logits=torch.from_numpy(lg).cuda(), top_k=k, shared=sh, debug=True)
+    assert pq.workspace_check() == 0
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k, shared=bank.sh_cpu)
+    _check(pq, bank, x, res, ref, M, k)
+    _check_shared(res, ref)
+
+
+def _router_case(pq, bank, M, E, H, k, seed, predict=2):
+    """Router weights and activations; fills the experts the oracle's own
+    logits rank in the top k + ``predict`` of each token (near ties may order
+    differently in fp32), returns (x bits, router bits, router tensor)."""
+    import torch
+    x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER if M == 1 else workloads.MOE_VERIFY,
+                                  seed=seed)
+    wr = workloads.router_weights_bf16(E, H, seed=seed)
+    lo = oracle.router_logits(x, wr)
+    top = np.argsort(-lo, axis=1, kind="stable")[:, :min(E, k + predict)]
+    bank.fill(top)
+    return x, wr, np_bf16_bits_to_torch(wr)
+
+
+def _check_router(res, x, wr, bank, k, shared=None):
+    """Logits within the fp32 accumulation bound of the oracle's; routing decided on
+    the kernel's own logits; the layer output against the oracle run on those
+    routes."""
+    lg = res["logits"].cpu().numpy()
+    lo = oracle.router_logits(x, wr)
+    xs = np.abs(workloads.bf16_bits_to_f32(x).astype(np.float64))
+    ws = np.abs(workloads.bf16_bits_to_f32(wr).astype(np.float64))
+    Sr = xs @ ws.T
+    assert np.all(np.abs(lg - lo) <= 1e-4 * Sr), f"router logits: worst {np.max(np.abs(lg - lo) / Sr):.2e} of S"
+    ids, w = oracle.route_topk(lg, k)
+    assert np.array_equal(res["topk_ids"].cpu().numpy(), ids), "routing ids differ from the top-k of the kernel's logits"
+    assert np.max(np.abs(res["topk_w"].cpu().numpy() - w)) <= 1e-6
+    ids64, _ = oracle.route_topk(lo.astype(np.float32), k)
+    near = np.sort(lo, axis=1)[:, ::-1]
+    gap = np.min(np.abs(np.diff(near[:, :k + 1], axis=1)), axis=1)
+    for m in range(lg.shape[0]):
+        if gap[m] > 1e-3:          # no near tie: the fp64 routing must agree too
+            assert np.array_equal(ids[m], ids64[m])
+    for e in np.unique(ids):
+        assert int(e) in bank.cpu, "the kernel routed to an expert the test did not fill"
+    return oracle.moe_layer(x, bank.expert, ids=ids, weights=w, shared=shared)
+
+
+@pytest.mark.parametrize("M,E,H,I,k,with_shared", [(1, 16, 512, 256, 4, False), (1, 64, 1024, 256, 8, True),
+                                                   (2, 32, 1024, 512, 8, True), (5, 40, 512, 256, 6, False),
+                                                   (8, 300, 1024, 256, 8, True)])
+def test_moe_router_gemv_in_the_launch(pq, path, M, E, H, I, k, with_shared):
+    bank = Bank(pq, E, H, I, seed=40 + M)
+    sh = bank.shared() if with_shared else None
+    x, wr, wrt = _router_case(pq, bank, M, E, H, k, seed=40 + M)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              router_w=wrt, top_k=k, shared=sh, debug=True)
+    assert pq.workspace_check() == 0
+    ref = _check_router(res, x, wr, bank, k, bank.sh_cpu if with_shared else None)
+    y = bf16_to_np(res["out"])
+    assert_gemv_close(y, ref["out"], ref["S"], f"router M={M} E={E} shared={with_shared}")
+    if with_shared:
+        _check_shared(res, ref)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_moe_full_layer_with_router_and_shared_expert(pq, path, M):
+    """256 experts, hidden 6144, intermediate 2048, top-8, the router GEMV and a
+    shared expert in the launch, every output checked."""
+    shp = workloads.MOE_SHAPE
+    bank = Bank(pq, shp.E, shp.H, shp.I, workload=workloads.MOE_LAYER, seed=3)
+    sh = bank.shared()
+    x, wr, wrt = _router_case(pq, bank, M, shp.E, shp.H, shp.top_k, seed=3, predict=1)
+    res = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                              router_w=wrt, top_k=shp.top_k, shared=sh, debug=True)
+    assert pq.workspace_check() == 0
+    ref = _check_router(res, x, wr, bank, shp.top_k, bank.sh_cpu)
+    worst = assert_gemv_close(bf16_to_np(res["out"]), ref["out"], ref["S"], f"full router+shared M={M}")
+    _check_shared(res, ref)
+    print(f"full router+shared M={M} ({path}): worst |err|/S {worst:.2e}")
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_moe_router_and_shared_kernels_agree_bitwise(pq, M):
+    import torch
+    E, H, I, k = 48, 1024, 512, 8
+    bank = Bank(pq, E, H, I, seed=60 + M)
+    sh = bank.shared()
+    x, wr, wrt = _router_case(pq, bank, M, E, H, k, seed=60 + M, predict=E)
+    outs = []
+    for path in ("barrier", "stream"):
+        os.environ["PQ_MOE_PATH"] = path
+        try:
+            r = pq.moe_decode_layer(np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2,
+                                    router_w=wrt, top_k=k, shared=sh)
+        finally:
+            del os.environ["PQ_MOE_PATH"]
+        outs.append((r["out"].clone(), r["logits"].clone(), r["topk_ids"].clone()))
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+    assert torch.equal(outs[0][2], outs[1][2])
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+
+
+def test_moe_router_wait_times_out_then_recovers(pq, path):
+    """A spin limit of zero makes the routing waves give up on the logits of
+    other blocks (forced from the host: every wait is bounded); the call ends,
+    and the next call on the same workspace is correct."""
+    M, E, H, I, k = 2, 32, 512, 256, 4
+    bank = Bank(pq, E, H, I, seed=70)
+    sh = bank.shared()
+    x, wr, wrt = _router_case(pq, bank, M, E, H, k, seed=70, predict=E)
+    args = (np_bf16_bits_to_torch(x), bank.w13, bank.s13, bank.w2, bank.s2)
+    os.environ["PQ_SPIN_LIMIT"] = "0"
+    try:
+        pq.moe_decode_layer(*args, router_w=wrt, top_k=k, shared=sh)
+    finally:
+        del os.environ["PQ_SPIN_LIMIT"]
+    assert pq.workspace_check() in (0, -7)
+    res = pq.moe_decode_layer(*args, router_w=wrt, top_k=k, shared=sh, debug=True)
+    assert pq.workspace_check() == 0
+    ref = _check_router(res, x, wr, bank, k, bank.sh_cpu)
+    assert_gemv_close(bf16_to_np(res["out"]), ref["out"], ref["S"], "router after timeout")

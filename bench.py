@@ -28,6 +28,7 @@ Reported (one JSON line):
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m M]
        python bench.py --workload moe_tp8 [--m M]    (the layer's per-rank share under 8-way TP, I = 256)
+       python bench.py --workload moe_full [--m M]   (the layer with the router GEMV and a shared expert in the launch)
        python bench.py --workload gemv_small|gate_up|lm_head|q4_stack [--m M] [--steps K]   (dense GEMVs)
        python bench.py --ingest-pmc FETCH.csv WRITE.csv   (writes the counter summary)
 """
@@ -163,35 +164,51 @@ def run(args):
 
     torch.cuda.set_device(0)
     tp8 = args.workload == "moe_tp8"
+    full = args.workload == "moe_full"         # router GEMV + shared expert in the launch
     shp = workloads.MOE_TP8_SHAPE if tp8 else workloads.MOE_SHAPE
     M = args.m
     t_setup = time.perf_counter()
     w13, s13, w2, s2 = build_bank(pq, shp)
     wl = workloads.MOE_LAYER if M == 1 else workloads.MOE_VERIFY
     x_bits = workloads.activation_bf16(M, shp.H, workload=wl)
-    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    to_t = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda()
+    x = to_t(x_bits)
     n_draws = 64
-    if M == 1:
-        pool_np = [workloads.router_logits(1, shp.E, workload=wl, draw=d) for d in range(n_draws)]
+    if full:
+        # routing follows the activations: one x draw per step, logits computed in the launch
+        xs = [to_t(workloads.activation_bf16(M, shp.H, workload=wl, seed=d)) for d in range(n_draws)]
+        wr = to_t(workloads.router_weights_bf16(shp.E, shp.H))
+        sh = []
+        for t, (rows, cols) in ((workloads.T_SH13, (2 * shp.I, shp.H)), (workloads.T_SH2, (shp.H, shp.I))):
+            q, sc = pq.quantize_fp8(workloads.master_weights_torch(rows, cols, workload=workloads.MOE_LAYER, tensor=t))
+            sh += [q, sc]
+        call = pq.MoeLayerCall(w13, s13, w2, s2, M=M, top_k=shp.top_k, router_w=wr, shared=tuple(sh))
+        step = lambda i: call(xs[i % n_draws])
+        pool_np = None
     else:
-        pool_np = [workloads.verify_logits(M, shp.E, draw=d) for d in range(n_draws)]
-    pool = [torch.from_numpy(p).cuda() for p in pool_np]
-    call = pq.MoeLayerCall(w13, s13, w2, s2, M=M, top_k=shp.top_k)
+        if M == 1:
+            pool_np = [workloads.router_logits(1, shp.E, workload=wl, draw=d) for d in range(n_draws)]
+        else:
+            pool_np = [workloads.verify_logits(M, shp.E, draw=d) for d in range(n_draws)]
+        pool = [torch.from_numpy(p).cuda() for p in pool_np]
+        call = pq.MoeLayerCall(w13, s13, w2, s2, M=M, top_k=shp.top_k)
+        step = lambda i: call(x, pool[i % n_draws])
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
     # distinct experts per draw -> algorithmic bytes of each step
     expert_bytes = 2 * shp.I * shp.H + 4 * 2 * shp.I * (shp.H // 128) + shp.H * shp.I + 4 * shp.H * (shp.I // 128)
     io_bytes = M * (2 * shp.H + 2 * shp.H + 4 * shp.E)
+    extra_bytes = expert_bytes + 2 * shp.E * shp.H if full else 0   # the shared expert and the router weights
     uni = []
     for d in range(n_draws):
-        call(x, pool[d])
+        step(d)
         uni.append(len(np.unique(call.topk_ids.cpu().numpy())))
-    step_bytes = [u * expert_bytes + io_bytes for u in uni]
+    step_bytes = [u * expert_bytes + io_bytes + extra_bytes for u in uni]
     assert call.check() == 0
 
     for i in range(args.warmup):
-        call(x, pool[i % n_draws])
+        step(i)
     torch.cuda.synchronize()
 
     # timed region: exactly K back-to-back layer calls, nothing else on the stream
@@ -201,7 +218,7 @@ def run(args):
     torch.cuda.synchronize()
     t_all0.record()
     for i in range(K):
-        call(x, pool[i % n_draws])
+        step(i)
     t_all1.record()
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
@@ -211,7 +228,7 @@ def run(args):
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     for i in range(K):
         starts[i].record()
-        call(x, pool[i % n_draws])
+        step(i)
         ends[i].record()
     torch.cuda.synchronize()
     per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
@@ -224,7 +241,7 @@ def run(args):
     mean_launch_s = float(np.mean(per_launch_ms)) * 1e-3
     bytes_per_launch = bytes_timed / K
     achieved = bytes_per_launch / mean_launch_s / 1e9
-    traffic = read_traffic(bytes_per_launch) if M == 1 and not tp8 else None
+    traffic = read_traffic(bytes_per_launch) if M == 1 and not tp8 and not full else None
 
     out = {
         "metric": METRIC,
@@ -244,7 +261,9 @@ def run(args):
                          f"expert intermediate {shp.I} (gate||up 6144->2x{shp.I}, SiLU*up, down {shp.I}->6144), "
                          "E4M3 weights with fp32 scale per 128-wide K block, top-8 of N(0,1) logits, "
                          "live FP8 activation quantisation, bf16 in/out"
-                         + ("; one rank's share of the 2048-wide layer under 8-way tensor parallelism" if tp8 else "")),
+                         + ("; one rank's share of the 2048-wide layer under 8-way tensor parallelism" if tp8 else "")
+                         + ("; the router GEMV (bf16 6144->256) and a shared expert in the same launch, "
+                            "routing from the activations" if full else "")),
             "M": M, "experts": shp.E, "hidden": shp.H, "intermediate": shp.I, "top_k": shp.top_k,
             "mean_experts_streamed": float(np.mean(uni)),
             "bytes_per_step": int(round(bytes_per_launch)),
@@ -279,7 +298,7 @@ def run(args):
         out["config"]["bytes_per_token"] = int(bytes_per_launch / M)
         out["config"]["bytes_per_accepted_token_L3.5"] = int(bytes_per_launch / 3.5)
 
-    if args.cpu_baseline:
+    if args.cpu_baseline and pool_np is not None:
         dt, reps, cores, ref, nexp = cpu_baseline(shp, x_bits, pool_np[0])
         b0 = step_bytes[0]
         call(x, pool[0])
@@ -516,7 +535,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, choices=range(1, 9), metavar="M")
     ap.add_argument("--workload", default="moe",
-                    choices=["moe", "moe_tp8", "gemv_small", "gate_up", "lm_head", "q4_stack"],
+                    choices=["moe", "moe_tp8", "moe_full", "gemv_small", "gate_up", "lm_head", "q4_stack"],
                     help="moe (default: the routed layer) or one of the dense configurations")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--profile-pass", action="store_true")
@@ -534,7 +553,7 @@ def main():
     if args.profile_pass:
         profile_pass(args)
         return
-    if args.workload not in ("moe", "moe_tp8"):
+    if args.workload not in ("moe", "moe_tp8", "moe_full"):
         run_dense(args)
         return
     run(args)

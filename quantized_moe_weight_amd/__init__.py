@@ -230,11 +230,14 @@ def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=
 
 
 class MoeLayerCall:
-    """A prepared moe_decode_layer call for repeated decode steps: output, routing
-    and workspace buffers are allocated once and the raw pointers resolved up
-    front, so each step is one C call (argument marshalling only)."""
+    """A prepared MoE layer call for repeated decode steps: output, routing and
+    workspace buffers are allocated once and the raw pointers resolved up front,
+    so each step is one C call (argument marshalling only).  With ``router_w``
+    (bf16 [E,H]) the router GEMV runs in the launch and a step takes only x;
+    ``shared`` = (w13, s13, w2, s2) adds a shared expert."""
 
-    def __init__(self, w13, s13, w2, s2, M: int, top_k: int = 8, debug: bool = False):
+    def __init__(self, w13, s13, w2, s2, M: int, top_k: int = 8, debug: bool = False, router_w=None,
+                 shared=None):
         _need(w13, torch.uint8, 3, "w13")
         _need(s13, torch.float32, 3, "s13")
         _need(w2, torch.uint8, 3, "w2")
@@ -251,22 +254,32 @@ class MoeLayerCall:
         if nb == 0:
             raise PqError("moe_decode_layer_workspace", -2)
         self.ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        self.h = torch.empty((M, top_k, self.I), dtype=torch.bfloat16, device=dev) if debug else None
-        self.hq = torch.empty((M, top_k, self.I), dtype=torch.uint8, device=dev) if debug else None
-        self.hs = torch.empty((M, top_k, self.I // 128), dtype=torch.float32, device=dev) if debug else None
-        self._fn = lib().moe_decode_layer
+        npairs = M * top_k + (M if shared is not None else 0)
+        self.h = torch.empty((npairs, self.I), dtype=torch.bfloat16, device=dev) if debug else None
+        self.hq = torch.empty((npairs, self.I), dtype=torch.uint8, device=dev) if debug else None
+        self.hs = torch.empty((npairs, self.I // 128), dtype=torch.float32, device=dev) if debug else None
+        if router_w is not None:
+            _need(router_w, torch.bfloat16, 2, "router_w")
+        self.router_w = router_w
+        self.logits = torch.empty((M, self.E), dtype=torch.float32, device=dev) if router_w is not None else None
+        self.shared = tuple(shared) if shared is not None else (None,) * 4
+        self._fn = lib().moe_decode_layer_ex
         _check(lib().pq_workspace_init(_p(self.ws), nb, _stream()), "pq_workspace_init")
-        self._fixed = [_p(t) for t in (w13, s13, w2, s2, self.out, self.h, self.hq, self.hs, self.ws)]
+        self._fixed = [_p(t) for t in (w13, s13, w2, s2, *self.shared, self.out, self.h, self.hq, self.hs, self.ws)]
         self._ids, self._w = _p(self.topk_ids), _p(self.topk_w)
+        self._wr = _p(router_w)
+        self._lg = _p(self.logits)
 
-    def __call__(self, x, logits, stream=None):
-        """x bf16 [M,H], logits fp32 [M,E] (device tensors, contiguous).  Returns ``out``."""
-        w13, s13, w2, s2, out, h, hq, hs, ws = self._fixed
-        st = self._fn(_p(x), self.M, self.H, _p(logits), self._ids, self._w, self.E, self.top_k, self.I,
-                      w13, s13, w2, s2, out, h, hq, hs, ws, self.ws.numel(),
+    def __call__(self, x, logits=None, stream=None):
+        """x bf16 [M,H] (and logits fp32 [M,E] unless the router runs in the
+        launch), contiguous device tensors.  Returns ``out``."""
+        w13, s13, w2, s2, a, b, c, d, out, h, hq, hs, ws = self._fixed
+        lg = self._lg if self.router_w is not None else _p(logits)
+        st = self._fn(_p(x), self.M, self.H, self._wr, lg, self._ids, self._w, self.E, self.top_k, self.I,
+                      w13, s13, w2, s2, a, b, c, d, out, h, hq, hs, ws, self.ws.numel(),
                       ctypes.c_void_p(stream) if stream is not None else _stream())
         if st != 0:
-            raise PqError("moe_decode_layer", st)
+            raise PqError("moe_decode_layer_ex", st)
         return self.out
 
     def check(self) -> int:

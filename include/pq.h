@@ -130,6 +130,36 @@ int pq_gemv_fp8(const uint16_t* x, int M, int K,
                 void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Prefill / large-M block-scaled FP8 GEMM on the matrix cores ([M3]: prefill */
+/* reuses each prepared weight for many tokens).                              */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes pq_gemm_fp8 needs: the data-region offset of the shared
+ * workspace layout plus M*K + 4*M*K/128 bytes (rounded up) for the quantised
+ * activation; 0 for invalid shapes. */
+size_t pq_gemm_fp8_workspace(int M, int K, int N, int epi);
+
+/* The contraction of pq_gemv_fp8 for any M >= 1 (no upper bound):
+ *   y = epi(bf16( sum_b s_x[m,b] s_w[n,b] sum_{k in b} q_x[m,k] q_w[n,k] ))
+ * Two launches on `stream`: the live FP8 quantisation of x (the rule of
+ * pq_quantize_fp8) into the workspace's data region, then the GEMM
+ * (v_mfma_f32_16x16x128_f8f6f4 per 128-wide K block, 128 x 128 tiles, both
+ * block scales applied per K block in fp32).
+ *   x : bf16 [M,K]     w : E4M3 [N,K]     w_scale : fp32 [N,K/128]
+ *   y : bf16 [M,N] (PQ_EPI_NONE) or [M,N/2] (PQ_EPI_SILU_MUL, gate rows then
+ *       up rows as in pq_gemv_fp8)
+ *   ws, ws_bytes : workspace of pq_gemm_fp8_workspace() bytes (the counters
+ *       and the zeroed region of the other entry points are not touched, so
+ *       the workspace may be theirs); too small: PQ_ERR_WORKSPACE.
+ * Constraints: K % 128 == 0, N >= 1, N*K < 2^31, M*K < 2^31, N even under
+ * PQ_EPI_SILU_MUL; PQ_ERR_SHAPE otherwise.  An output's bits do not depend on
+ * the other tokens of the call. */
+int pq_gemm_fp8(const uint16_t* x, int M, int K,
+                const uint8_t* w, const float* w_scale, int N,
+                int epi, uint16_t* y,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* int4 g32 weight-streaming GEMV (W4A16): [M3] Q4 decode.                    */
 /* ------------------------------------------------------------------------- */
 

@@ -14,12 +14,13 @@ import torch
 
 from . import _lib
 
-__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemv_q4", "moe_decode_layer",
+__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemv_q4", "moe_decode_layer",
            "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call", "stream_probe",
            "EPI_NONE", "EPI_SILU_MUL", "lib"]
 
 EPI_NONE = 0
 EPI_SILU_MUL = 1
+WS_DATA_OFF = 65536 + (2 << 20)   # start of the workspace's data region (counters and a zeroed region before it)
 
 
 class PqError(RuntimeError):
@@ -143,6 +144,30 @@ def gemv_fp8(x, w, w_scale, epi: int = EPI_NONE, debug: bool = False, out=None):
     _check(lib().pq_gemv_fp8(_p(x), M, K, _p(w), _p(w_scale), N, epi, _p(y), _p(xq), _p(xs), _p(ws), wsn,
                              _stream()), "pq_gemv_fp8")
     return (y, xq, xs) if debug else y
+
+
+def gemm_fp8(x, w, w_scale, epi: int = EPI_NONE, debug: bool = False, out=None):
+    """Large-M (prefill) block-scaled FP8 GEMM on the matrix cores: x bf16 [M,K] (quantised
+    live into the workspace), w uint8 [N,K], w_scale fp32 [N,K/128].  Returns y (bf16 [M,N]
+    or [M,N/2] under SiLU*up), or (y, xq, xs) with debug (views of the workspace)."""
+    _need(x, torch.bfloat16, 2, "x")
+    _need(w, torch.uint8, 2, "w")
+    _need(w_scale, torch.float32, 2, "w_scale")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K or w_scale.shape != (N, K // 128):
+        raise ValueError("weight / scale shapes do not match x")
+    n_out = N // 2 if epi == EPI_SILU_MUL else N
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+    ws, wsn = _workspace(int(lib().pq_gemm_fp8_workspace(M, K, N, epi)))
+    _check(lib().pq_gemm_fp8(_p(x), M, K, _p(w), _p(w_scale), N, epi, _p(y), _p(ws), wsn, _stream()), "pq_gemm_fp8")
+    if not debug:
+        return y
+    off = WS_DATA_OFF
+    xq = ws[off:off + M * K].view(M, K)
+    off2 = off + (M * K + 255) // 256 * 256
+    xs = ws[off2:off2 + M * (K // 128) * 4].view(torch.float32).view(M, K // 128)
+    return y, xq, xs
 
 
 def gemv_q4(x, w, w_scale, epi: int = EPI_NONE, out=None):

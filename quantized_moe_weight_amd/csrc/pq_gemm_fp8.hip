@@ -1,0 +1,269 @@
+// Prefill / large-M block-scaled FP8 GEMM on the matrix cores:
+//   y[m, n] = epi( sum_b s_x[m,b] s_w[n,b] sum_{k in b} q_x[m,k] q_w[n,k] )
+// with the activation quantised live (the rule of pq_quantize_fp8) and the
+// weights in the layout of the GEMV (E4M3 [N,K], fp32 [N,K/128]).
+//
+// [M3]: prefill reuses each prepared weight for many tokens and wide loads
+// with merged passes raised its share of the matmul limit; with hundreds of
+// tokens per weight byte the product is bound by the matrix cores, not HBM.
+//
+// gfx950 design
+//   * a 256-thread block (2 x 2 waves) owns a 128-token x 128-weight-row tile;
+//     each wave a 64 x 64 quarter = 4 x 4 v_mfma_f32_16x16x128_f8f6f4 per
+//     128-wide K block (the scale block), whose fp32 results take both block
+//     scales (acc += d * (s_x * s_w)) in fp32 on the vector unit;
+//   * operands pass through LDS, two stages: each K step's tiles are loaded
+//     into registers with whole-line instructions (8 rows x 128 bytes per
+//     wave instruction) while the previous step computes, then stored to the
+//     other stage (rows padded to 144 bytes: the operand reads are free of bank
+//     conflicts); one block barrier per K step;
+//   * operand layout as in the matrix-core GEMV: lane l carries row l % 16 of
+//     a 16-row sub-tile, lane group g = l / 16 the bytes [16g, 16g+16) and
+//     [64+16g, 80+16g) of the block, alike in A (tokens) and B (weight rows);
+//   * SiLU(gate)*up: a tile holds 64 output columns, its 128 B rows ordered
+//     gate 0..31, up 0..31, gate 32..63, up 32..63, so each wave's column tiles
+//     b and b + 2 are the gate and the up of the same outputs, in the same
+//     lanes;
+//   * tiles are dealt to the 8 XCDs in contiguous runs, token tiles fastest,
+//     so the blocks that share a weight tile share an L2.
+#include <stdlib.h>
+#include <string.h>
+
+#include "pq_common.h"
+
+extern "C" int pq_quantize_fp8(const void* in, int in_is_f32, int rows, int K, uint8_t* codes, float* scales,
+                               void* stream);
+
+namespace {
+
+typedef int int32x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kTile = 128;                    // tokens per tile; B rows per tile
+constexpr int kRowB = pq::kBlock + 16;        // LDS row stride of an operand tile (bytes)
+constexpr int kTileB = kTile * kRowB;         // one operand tile in LDS
+constexpr int kStageB = 2 * kTileB + 2 * kTile * 4;   // A, B, their scales
+constexpr int kLdsB = 2 * kStageB;
+constexpr int kXcds = 8;
+
+struct GArgs {
+  const uint8_t* xq;     // [M][K]
+  const float* xs;       // [M][K/128]
+  const uint8_t* w;      // [N][K]
+  const float* ws;       // [N][K/128]
+  uint16_t* y;           // [M][R]
+  int M, K, N, R;        // R: output columns (N, or N/2 under SiLU*up)
+  int silu;
+  int tm, tn;            // tiles along the tokens and along the output columns
+};
+
+__device__ __forceinline__ floatx4 mfma_e4m3(int32x8 a, int32x8 b) {
+  // block-scale operands 0: the plain (unscaled) matrix instruction
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ int32x8 join8(uint4 lo, uint4 hi) {
+  return int32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Weight row of B-tile row r (-1 past the matrix).  Plain: n0 + r.  SiLU*up:
+// the tile covers output columns c0 .. c0 + 63 in the order gate 0..31, up
+// 0..31, gate 32..63, up 32..63.
+__device__ __forceinline__ int b_row(const GArgs& a, int tile_n, int r) {
+  if (!a.silu) {
+    const int n = tile_n * kTile + r;
+    return n < a.N ? n : -1;
+  }
+  const int q = r >> 5, i = r & 31;
+  const int c = tile_n * (kTile / 2) + (q >> 1) * 32 + i;
+  if (c >= a.R) return -1;
+  return (q & 1) ? c + a.R : c;
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = (int)threadIdx.x;
+  const int lane = pq::lane_id();
+  const int wv = pq::wave_id();
+  const int wm = wv >> 1, wn = wv & 1;        // this wave's quarter of the tile
+  const int rl = lane & 15, lg = lane >> 4;
+
+  // tile of this block: contiguous runs per XCD (block b runs on XCD b % 8),
+  // token tiles fastest
+  const int T = a.tm * a.tn;
+  const int T8 = T / kXcds * kXcds;
+  const int b = (int)blockIdx.x;
+  const int t = b < T8 ? (b % kXcds) * (T8 / kXcds) + b / kXcds : b;
+  const int tile_m = t % a.tm, tile_n = t / a.tm;
+  const int m0 = tile_m * kTile;
+  const int nb = a.K / pq::kBlock;
+
+  const pq::rsrc_t xr = pq::make_rsrc(a.xq, (uint32_t)((size_t)a.M * a.K));
+  const pq::rsrc_t wr = pq::make_rsrc(a.w, (uint32_t)((size_t)a.N * a.K));
+  const pq::rsrc_t xsr = pq::make_rsrc(a.xs, (uint32_t)((size_t)a.M * nb * 4));
+  const pq::rsrc_t wsr = pq::make_rsrc(a.ws, (uint32_t)((size_t)a.N * nb * 4));
+
+  // this thread's load rows (whole lines: 8 rows x 128 bytes per wave
+  // instruction) and its scale row
+  const int lrow = tid >> 3, lslot = tid & 7;
+  uint32_t aoff[4], boff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 32 * i;
+    aoff[i] = m0 + r < a.M ? (uint32_t)(m0 + r) * (uint32_t)a.K + 16u * (uint32_t)lslot : pq::kOOB;
+    const int n = b_row(a, tile_n, r);
+    boff[i] = n >= 0 ? (uint32_t)n * (uint32_t)a.K + 16u * (uint32_t)lslot : pq::kOOB;
+  }
+  uint32_t soff;                               // threads 0..127: token scales; 128..255: weight scales
+  if (tid < kTile) {
+    soff = m0 + tid < a.M ? (uint32_t)(m0 + tid) * (uint32_t)nb * 4u : pq::kOOB;
+  } else {
+    const int n = b_row(a, tile_n, tid - kTile);
+    soff = n >= 0 ? (uint32_t)n * (uint32_t)nb * 4u : pq::kOOB;
+  }
+
+  uint4 ra[4], rb[4];
+  float rs;
+  auto load = [&](int kb) {
+    const uint32_t kofs = (uint32_t)kb * pq::kBlock;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = pq::buf_load16(xr, aoff[i] == pq::kOOB ? pq::kOOB : aoff[i] + kofs);
+      rb[i] = pq::buf_load16(wr, boff[i] == pq::kOOB ? pq::kOOB : boff[i] + kofs);
+    }
+    rs = pq::buf_load_f32(tid < kTile ? xsr : wsr, soff == pq::kOOB ? pq::kOOB : soff + (uint32_t)kb * 4u);
+  };
+  auto store = [&](int st) {
+    uint8_t* base = smem + st * kStageB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 32 * i;
+      *reinterpret_cast<uint4*>(base + r * kRowB + 16 * lslot) = ra[i];
+      *reinterpret_cast<uint4*>(base + kTileB + r * kRowB + 16 * lslot) = rb[i];
+    }
+    reinterpret_cast<float*>(base + 2 * kTileB)[tid] = rs;   // token scales, then weight scales
+  };
+
+  float acc[4][4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kb = 0; kb < nb; ++kb) {
+    const int st = kb & 1;
+    if (kb + 1 < nb) load(kb + 1);            // in flight while this step computes
+    const uint8_t* base = smem + st * kStageB;
+    const float* sxs = reinterpret_cast<const float*>(base + 2 * kTileB);
+    const float* sws = sxs + kTile;
+    int32x8 bf[4];
+    float swv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint8_t* p = base + kTileB + (64 * wn + 16 * j + rl) * kRowB + 16 * lg;
+      bf[j] = join8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+      swv[j] = sws[64 * wn + 16 * j + rl];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* p = base + (64 * wm + 16 * i + rl) * kRowB + 16 * lg;
+      const int32x8 af = join8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+      const float4 sx = *reinterpret_cast<const float4*>(sxs + 64 * wm + 16 * i + 4 * lg);
+      const float sxv[4] = {sx.x, sx.y, sx.z, sx.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const floatx4 d = mfma_e4m3(af, bf[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(d[r], sxv[r] * swv[j], acc[i][j][r]);
+      }
+    }
+    if (kb + 1 < nb) store(st ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane (g, j) of sub-tile (i, b) holds tokens 4g..4g+3 of row
+  // tile i and column j of column tile b
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
+      if (m >= a.M) continue;
+      if (!a.silu) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = tile_n * kTile + 64 * wn + 16 * j + rl;
+          if (n < a.N) a.y[(size_t)m * a.R + n] = pq::bf16_rne(acc[i][j][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = tile_n * (kTile / 2) + 32 * wn + 16 * j + rl;
+          if (c < a.R) a.y[(size_t)m * a.R + c] = pq::bf16_rne(silu_mul(acc[i][j][r], acc[i][j + 2][r]));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// The quantised activation lives in the workspace's data region, so the same
+// workspace can serve the other entry points (their counters and their
+// zero-between-calls region are left alone).
+size_t pq_gemm_fp8_workspace(int M, int K, int N, int epi) {
+  if (M < 1 || K < pq::kBlock || K % pq::kBlock != 0 || N < 1) return 0;
+  (void)N;
+  (void)epi;
+  return pq::kWsDataOff + pqhost::align_up((size_t)M * K, 256) + pqhost::align_up((size_t)M * (K / pq::kBlock) * 4, 256);
+}
+
+int pq_gemm_fp8(const uint16_t* x, int M, int K, const uint8_t* w, const float* w_scale, int N, int epi,
+                uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !w || !w_scale || !y) return PQ_ERR_NULL;
+  if (M < 1 || K < pq::kBlock || K % pq::kBlock != 0 || N < 1) return PQ_ERR_SHAPE;
+  if (epi != PQ_EPI_NONE && epi != PQ_EPI_SILU_MUL) return PQ_ERR_SHAPE;
+  if (epi == PQ_EPI_SILU_MUL && N % 2 != 0) return PQ_ERR_SHAPE;
+  if ((size_t)N * K > pq::kMaxBufferBytes || (size_t)M * K > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
+  if (!pqhost::aligned16(x) || !pqhost::aligned16(w) || !pqhost::aligned16(w_scale) || !pqhost::aligned16(y))
+    return PQ_ERR_ALIGN;
+  const size_t need = pq_gemm_fp8_workspace(M, K, N, epi);
+  if (ws == nullptr || ws_bytes < need) return PQ_ERR_WORKSPACE;
+  if (!pqhost::aligned16(ws)) return PQ_ERR_ALIGN;
+  pqhost::DeviceInfo dev;
+  int st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws) + pq::kWsDataOff;
+  float* xs = reinterpret_cast<float*>(xq + pqhost::align_up((size_t)M * K, 256));
+  st = pq_quantize_fp8(x, 0, M, K, xq, xs, stream);      // the live activation rule, one pass
+  if (st != PQ_OK) return st;
+
+  GArgs a;
+  a.xq = xq; a.xs = xs; a.w = w; a.ws = w_scale; a.y = y;
+  a.M = M; a.K = K; a.N = N;
+  a.silu = epi == PQ_EPI_SILU_MUL;
+  a.R = a.silu ? N / 2 : N;
+  a.tm = (M + kTile - 1) / kTile;
+  a.tn = a.silu ? (a.R + kTile / 2 - 1) / (kTile / 2) : (N + kTile - 1) / kTile;
+  static bool attr_set = false;
+  if (!attr_set) {
+    PQ_HIP_CHECK(hipFuncSetAttribute((const void*)gemm_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsB));
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(gemm_fp8_kernel, dim3((unsigned)(a.tm * a.tn)), dim3(kThreads), kLdsB, (hipStream_t)stream, a);
+  PQ_HIP_CHECK(hipGetLastError());
+  return PQ_OK;
+}
+
+}  // extern "C"

@@ -8,21 +8,28 @@
 // tokens per weight byte the product is bound by the matrix cores, not HBM.
 //
 // gfx950 design
-//   * a 256-thread block (2 x 2 waves) owns a 128-token x 128-weight-row tile;
-//     each wave a 64 x 64 quarter = 4 x 4 v_mfma_f32_16x16x128_f8f6f4 per
-//     128-wide K block (the scale block), whose fp32 results take both block
-//     scales (acc += d * (s_x * s_w)) in fp32 on the vector unit;
-//   * operands pass through LDS, two stages: each K step's tiles are loaded
-//     into registers with whole-line instructions (8 rows x 128 bytes per
-//     wave instruction) while the previous step computes, then stored to the
-//     other stage (rows padded to 144 bytes: the operand reads are free of bank
-//     conflicts); one block barrier per K step;
+//   * a 512-thread block (8 waves, 2 x 4) owns a 256-token x 256-weight-row
+//     tile (64 KB of operands per K step for 16.8 MFLOP: large tiles keep the
+//     L2 traffic within what eight L2s deliver); each wave a 128 x 64 part =
+//     8 x 4 v_mfma_f32_16x16x128_f8f6f4 per 128-wide K block (the scale
+//     block), whose fp32 results take both block scales (acc += d * (s_x *
+//     s_w)) in fp32 on the vector unit; two waves per SIMD, so one wave's
+//     matrix work covers the other's waits;
+//   * operands stream from memory straight into LDS (buffer loads with an
+//     LDS destination: no registers) for K step k + 1 while step k computes;
+//     the two stages are separate LDS objects and the loop is unrolled by
+//     two, so the compiler knows that the operand reads of one stage do not
+//     wait for the loads into the other; one block barrier per K step, after
+//     each wave has waited for its own loads of the step;
+//   * a wave's load instruction covers 8 rows x 128 bytes (whole lines) and
+//     lands as 1 KB of LDS; in LDS the 16-byte slot s of row r holds global
+//     slot s ^ (r % 8), which spreads the operand reads over all banks;
 //   * operand layout as in the matrix-core GEMV: lane l carries row l % 16 of
 //     a 16-row sub-tile, lane group g = l / 16 the bytes [16g, 16g+16) and
 //     [64+16g, 80+16g) of the block, alike in A (tokens) and B (weight rows);
-//   * SiLU(gate)*up: a tile holds 64 output columns, its 128 B rows ordered
-//     gate 0..31, up 0..31, gate 32..63, up 32..63, so each wave's column tiles
-//     b and b + 2 are the gate and the up of the same outputs, in the same
+//   * SiLU(gate)*up: a tile holds 128 output columns, its 256 B rows ordered
+//     in runs of 32 as gate, up, gate, up, ..., so each wave's column tiles b
+//     and b + 2 are the gate and the up of the same outputs, in the same
 //     lanes;
 //   * tiles are dealt to the 8 XCDs in contiguous runs, token tiles fastest,
 //     so the blocks that share a weight tile share an L2.
@@ -39,13 +46,21 @@ namespace {
 typedef int int32x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kTile = 128;                    // tokens per tile; B rows per tile
-constexpr int kRowB = pq::kBlock + 16;        // LDS row stride of an operand tile (bytes)
-constexpr int kTileB = kTile * kRowB;         // one operand tile in LDS
-constexpr int kStageB = 2 * kTileB + 2 * kTile * 4;   // A, B, their scales
-constexpr int kLdsB = 2 * kStageB;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / pq::kWave;
+constexpr int BM = 256, BN = 256;             // tokens and weight rows per tile
+constexpr int WM = BM / 2 / 16;               // row tiles per wave (waves: 2 along the tokens)
+// one pipeline stage in LDS: A and B tiles (128-byte rows, swizzled slots)
+// and their block scales
+struct Stage {
+  uint8_t a[BM * pq::kBlock];
+  uint8_t b[BN * pq::kBlock];
+  float sa[BM];
+  float sb[BN];
+};
+typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kXcds = 8;
+static_assert(2 * sizeof(Stage) <= 160 * 1024, "stages must fit LDS");
 
 struct GArgs {
   const uint8_t* xq;     // [M][K]
@@ -70,25 +85,25 @@ __device__ __forceinline__ int32x8 join8(uint4 lo, uint4 hi) {
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 // Weight row of B-tile row r (-1 past the matrix).  Plain: n0 + r.  SiLU*up:
-// the tile covers output columns c0 .. c0 + 63 in the order gate 0..31, up
-// 0..31, gate 32..63, up 32..63.
+// the tile covers output columns c0 .. c0 + 127 in runs of 32: gate 0..31,
+// up 0..31, gate 32..63, up 32..63, ...
 __device__ __forceinline__ int b_row(const GArgs& a, int tile_n, int r) {
   if (!a.silu) {
-    const int n = tile_n * kTile + r;
+    const int n = tile_n * BN + r;
     return n < a.N ? n : -1;
   }
   const int q = r >> 5, i = r & 31;
-  const int c = tile_n * (kTile / 2) + (q >> 1) * 32 + i;
+  const int c = tile_n * (BN / 2) + (q >> 1) * 32 + i;
   if (c >= a.R) return -1;
   return (q & 1) ? c + a.R : c;
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int tid = (int)threadIdx.x;
+  __shared__ __align__(16) Stage st0;
+  __shared__ __align__(16) Stage st1;
   const int lane = pq::lane_id();
-  const int wv = pq::wave_id();
-  const int wm = wv >> 1, wn = wv & 1;        // this wave's quarter of the tile
+  const int wv = __builtin_amdgcn_readfirstlane(pq::wave_id());
+  const int wm = wv >> 2, wn = wv & 3;        // this wave's part of the tile: rows 128 wm.., cols 64 wn..
   const int rl = lane & 15, lg = lane >> 4;
 
   // tile of this block: contiguous runs per XCD (block b runs on XCD b % 8),
@@ -98,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
   const int b = (int)blockIdx.x;
   const int t = b < T8 ? (b % kXcds) * (T8 / kXcds) + b / kXcds : b;
   const int tile_m = t % a.tm, tile_n = t / a.tm;
-  const int m0 = tile_m * kTile;
+  const int m0 = tile_m * BM;
   const int nb = a.K / pq::kBlock;
 
   const pq::rsrc_t xr = pq::make_rsrc(a.xq, (uint32_t)((size_t)a.M * a.K));
@@ -106,77 +121,73 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
   const pq::rsrc_t xsr = pq::make_rsrc(a.xs, (uint32_t)((size_t)a.M * nb * 4));
   const pq::rsrc_t wsr = pq::make_rsrc(a.ws, (uint32_t)((size_t)a.N * nb * 4));
 
-  // this thread's load rows (whole lines: 8 rows x 128 bytes per wave
-  // instruction) and its scale row
-  const int lrow = tid >> 3, lslot = tid & 7;
-  uint32_t aoff[4], boff[4];
+  // this lane's loads: row 64 i + 8 wv + lane / 8 of A and of B (i < 4),
+  // global slot (lane % 8) ^ (lane / 8) of the K block (it lands in LDS slot
+  // lane % 8 of that row); one scale per lane (waves 0-3: tokens, 4-7:
+  // weight rows)
+  const int lrow = 8 * wv + (lane >> 3);
+  const uint32_t gslot = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+  uint32_t aoff[BM / 64], boff[BN / 64];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 32 * i;
-    aoff[i] = m0 + r < a.M ? (uint32_t)(m0 + r) * (uint32_t)a.K + 16u * (uint32_t)lslot : pq::kOOB;
-    const int n = b_row(a, tile_n, r);
-    boff[i] = n >= 0 ? (uint32_t)n * (uint32_t)a.K + 16u * (uint32_t)lslot : pq::kOOB;
+  for (int i = 0; i < BM / 64; ++i) {
+    const int r = 64 * i + lrow;
+    aoff[i] = m0 + r < a.M ? (uint32_t)(m0 + r) * (uint32_t)a.K + gslot : pq::kOOB;
   }
-  uint32_t soff;                               // threads 0..127: token scales; 128..255: weight scales
-  if (tid < kTile) {
-    soff = m0 + tid < a.M ? (uint32_t)(m0 + tid) * (uint32_t)nb * 4u : pq::kOOB;
+#pragma unroll
+  for (int i = 0; i < BN / 64; ++i) {
+    const int n = b_row(a, tile_n, 64 * i + lrow);
+    boff[i] = n >= 0 ? (uint32_t)n * (uint32_t)a.K + gslot : pq::kOOB;
+  }
+  uint32_t soff;
+  const bool xscale = wv < 4;
+  if (xscale) {
+    const int m = m0 + 64 * wv + lane;
+    soff = m < a.M ? (uint32_t)m * (uint32_t)nb * 4u : pq::kOOB;
   } else {
-    const int n = b_row(a, tile_n, tid - kTile);
+    const int n = b_row(a, tile_n, 64 * (wv - 4) + lane);
     soff = n >= 0 ? (uint32_t)n * (uint32_t)nb * 4u : pq::kOOB;
   }
 
-  uint4 ra[4], rb[4];
-  float rs;
-  auto load = [&](int kb) {
+  auto issue = [&](Stage& st, int kb) {
     const uint32_t kofs = (uint32_t)kb * pq::kBlock;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = pq::buf_load16(xr, aoff[i] == pq::kOOB ? pq::kOOB : aoff[i] + kofs);
-      rb[i] = pq::buf_load16(wr, boff[i] == pq::kOOB ? pq::kOOB : boff[i] + kofs);
-    }
-    rs = pq::buf_load_f32(tid < kTile ? xsr : wsr, soff == pq::kOOB ? pq::kOOB : soff + (uint32_t)kb * 4u);
-  };
-  auto store = [&](int st) {
-    uint8_t* base = smem + st * kStageB;
+    for (int i = 0; i < BM / 64; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(st.a + (64 * i + 8 * wv) * pq::kBlock), 16,
+                                               aoff[i] == pq::kOOB ? pq::kOOB : aoff[i] + kofs, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lrow + 32 * i;
-      *reinterpret_cast<uint4*>(base + r * kRowB + 16 * lslot) = ra[i];
-      *reinterpret_cast<uint4*>(base + kTileB + r * kRowB + 16 * lslot) = rb[i];
-    }
-    reinterpret_cast<float*>(base + 2 * kTileB)[tid] = rs;   // token scales, then weight scales
+    for (int i = 0; i < BN / 64; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr)(st.b + (64 * i + 8 * wv) * pq::kBlock), 16,
+                                               boff[i] == pq::kOOB ? pq::kOOB : boff[i] + kofs, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xscale ? xsr : wsr,
+                                             (lds_ptr)(xscale ? st.sa + 64 * wv : st.sb + 64 * (wv - 4)), 4,
+                                             soff == pq::kOOB ? pq::kOOB : soff + (uint32_t)kb * 4u, 0, 0, 0);
   };
 
-  float acc[4][4][4];
+  float acc[WM][4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kb = 0; kb < nb; ++kb) {
-    const int st = kb & 1;
-    if (kb + 1 < nb) load(kb + 1);            // in flight while this step computes
-    const uint8_t* base = smem + st * kStageB;
-    const float* sxs = reinterpret_cast<const float*>(base + 2 * kTileB);
-    const float* sws = sxs + kTile;
+  // operand reads: slots lg and lg + 4 of a row, after the swizzle
+  const uint32_t sw_lo = 16u * (uint32_t)(lg ^ (rl & 7)), sw_hi = 16u * (uint32_t)((lg + 4) ^ (rl & 7));
+
+  auto compute = [&](const Stage& st) {
     int32x8 bf[4];
     float swv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint8_t* p = base + kTileB + (64 * wn + 16 * j + rl) * kRowB + 16 * lg;
-      bf[j] = join8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-      swv[j] = sws[64 * wn + 16 * j + rl];
+      const uint8_t* p = st.b + (64 * wn + 16 * j + rl) * pq::kBlock;
+      bf[j] = join8(*reinterpret_cast<const uint4*>(p + sw_lo), *reinterpret_cast<const uint4*>(p + sw_hi));
+      swv[j] = st.sb[64 * wn + 16 * j + rl];
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint8_t* p = base + (64 * wm + 16 * i + rl) * kRowB + 16 * lg;
-      const int32x8 af = join8(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
-      const float4 sx = *reinterpret_cast<const float4*>(sxs + 64 * wm + 16 * i + 4 * lg);
+    for (int i = 0; i < WM; ++i) {
+      const uint8_t* p = st.a + (128 * wm + 16 * i + rl) * pq::kBlock;
+      const int32x8 af = join8(*reinterpret_cast<const uint4*>(p + sw_lo), *reinterpret_cast<const uint4*>(p + sw_hi));
+      const float4 sx = *reinterpret_cast<const float4*>(st.sa + 128 * wm + 16 * i + 4 * lg);
       const float sxv[4] = {sx.x, sx.y, sx.z, sx.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -185,28 +196,41 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
         for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(d[r], sxv[r] * swv[j], acc[i][j][r]);
       }
     }
-    if (kb + 1 < nb) store(st ^ 1);
-    __syncthreads();
+  };
+  // every wave's loads of the next stage have landed, and every wave is done
+  // with the stage about to be refilled (the memory clobber keeps the LDS
+  // accesses on their side of the barrier)
+  auto step_barrier = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  issue(st0, 0);
+  for (int kb = 0; kb < nb; kb += 2) {
+    step_barrier();
+    if (kb + 1 < nb) issue(st1, kb + 1);
+    compute(st0);
+    if (kb + 1 >= nb) break;
+    step_barrier();
+    if (kb + 2 < nb) issue(st0, kb + 2);
+    compute(st1);
   }
 
   // epilogue: lane (g, j) of sub-tile (i, b) holds tokens 4g..4g+3 of row
   // tile i and column j of column tile b
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < WM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * lg + r;
+      const int m = m0 + 128 * wm + 16 * i + 4 * lg + r;
       if (m >= a.M) continue;
       if (!a.silu) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = tile_n * kTile + 64 * wn + 16 * j + rl;
+          const int n = tile_n * BN + 64 * wn + 16 * j + rl;
           if (n < a.N) a.y[(size_t)m * a.R + n] = pq::bf16_rne(acc[i][j][r]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int c = tile_n * (kTile / 2) + 32 * wn + 16 * j + rl;
+          const int c = tile_n * (BN / 2) + 32 * wn + 16 * j + rl;
           if (c < a.R) a.y[(size_t)m * a.R + c] = pq::bf16_rne(silu_mul(acc[i][j][r], acc[i][j + 2][r]));
         }
       }
@@ -254,14 +278,9 @@ int pq_gemm_fp8(const uint16_t* x, int M, int K, const uint8_t* w, const float* 
   a.M = M; a.K = K; a.N = N;
   a.silu = epi == PQ_EPI_SILU_MUL;
   a.R = a.silu ? N / 2 : N;
-  a.tm = (M + kTile - 1) / kTile;
-  a.tn = a.silu ? (a.R + kTile / 2 - 1) / (kTile / 2) : (N + kTile - 1) / kTile;
-  static bool attr_set = false;
-  if (!attr_set) {
-    PQ_HIP_CHECK(hipFuncSetAttribute((const void*)gemm_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsB));
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(gemm_fp8_kernel, dim3((unsigned)(a.tm * a.tn)), dim3(kThreads), kLdsB, (hipStream_t)stream, a);
+  a.tm = (M + BM - 1) / BM;
+  a.tn = a.silu ? (a.R + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  hipLaunchKernelGGL(gemm_fp8_kernel, dim3((unsigned)(a.tm * a.tn)), dim3(kThreads), 0, (hipStream_t)stream, a);
   PQ_HIP_CHECK(hipGetLastError());
   return PQ_OK;
 }

@@ -29,6 +29,7 @@ Reported (one JSON line):
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--m M]
        python bench.py --workload moe_tp8 [--m M]    (the layer's per-rank share under 8-way TP, I = 256)
        python bench.py --workload moe_full [--m M]   (the layer with the router GEMV and a shared expert in the launch)
+       python bench.py --workload prefill [--tokens T]   (prefill FP8 GEMM on the matrix cores, MFMA roofline)
        python bench.py --workload gemv_small|gate_up|lm_head|q4_stack [--m M] [--steps K]   (dense GEMVs)
        python bench.py --ingest-pmc FETCH.csv WRITE.csv   (writes the counter summary)
 """
@@ -452,6 +453,91 @@ def run_dense(args):
     print(json.dumps(out), flush=True)
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 matrix peak
+
+
+def run_prefill(args):
+    """Prefill (large-M) block-scaled FP8 GEMM: one expert's gate_up (K=6144,
+    N=2x2048, SiLU*up) over args.tokens tokens.  A step is one pq_gemm_fp8
+    call (live activation quant + GEMM); the roofline is the matrix cores'
+    fp8 peak, with the GEMM launch timed alone (pq_gemm_fp8_prequant on the
+    same quantised activation, events on the launch stream)."""
+    import ctypes
+    import numpy as np
+    import torch
+
+    import quantized_moe_weight_amd as pq
+    import workloads
+
+    torch.cuda.set_device(0)
+    lib = pq.lib()
+    T, K, N, epi = args.tokens, 6144, 4096, 1
+    m = workloads.master_weights_torch(N, K, workload=workloads.FP8_GATE_UP)
+    q, sc = pq.quantize_fp8(m)
+    del m
+    g = torch.Generator(device="cuda")
+    g.manual_seed(workloads.torch_seed(workloads.FP8_GATE_UP, workloads.T_X))
+    x = torch.randn((T, K), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    y = torch.empty((T, N // 2), dtype=torch.bfloat16, device="cuda")
+    nb = int(lib.pq_gemm_fp8_workspace(T, K, N, epi))
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    xq, xs = pq.quantize_fp8(x)
+
+    def full():
+        rc = lib.pq_gemm_fp8(P(x), T, K, P(q), P(sc), N, epi, P(y), P(ws), nb, st)
+        if rc != 0:
+            raise RuntimeError(f"pq_gemm_fp8 returned {rc}")
+
+    def gemm_only():
+        rc = lib.pq_gemm_fp8_prequant(P(xq), P(xs), T, K, P(q), P(sc), N, epi, P(y), st)
+        if rc != 0:
+            raise RuntimeError(f"pq_gemm_fp8_prequant returned {rc}")
+
+    for _ in range(args.warmup):
+        full()
+    torch.cuda.synchronize()
+    Ks = args.steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(Ks):
+        full()
+    t1.record()
+    torch.cuda.synchronize()
+    step_s = t0.elapsed_time(t1) * 1e-3 / Ks
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(Ks)]
+    for a_, b_ in ev:
+        a_.record()
+        gemm_only()
+        b_.record()
+    torch.cuda.synchronize()
+    per = np.array([a_.elapsed_time(b_) for a_, b_ in ev]) * 1e-3
+    flops = 2.0 * T * N * K
+    achieved = flops / float(np.mean(per)) / 1e12
+    q10, q50, q90 = np.percentile(per, [10, 50, 90]) * 1e6
+    out = {
+        "metric": "prefill FP8 GEMM TFLOP/s (fraction of the 5.0 PFLOP/s dense fp8 matrix peak)",
+        "value": round(flops / step_s / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": Ks,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": (f"prefill block-scaled FP8 GEMM: {T} tokens through one expert's gate_up "
+                                f"(K={K}, N=2x{N // 2}, SiLU*up), E4M3 weights + fp32 block-128 scales, "
+                                "activation quantised live per token and 128-block (a second launch), bf16 out"),
+                   "tokens": T, "K": K, "N": N, "epilogue": "silu_mul", "launches_per_call": 2},
+        "us_per_call": round(step_s * 1e6, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": ("gemm_fp8_kernel_t256" if (T + 255) // 256 * ((N // 2 + 127) // 128)
+                                >= torch.cuda.get_device_properties(0).multi_processor_count else "gemm_fp8_kernel_t128"),
+                     "mean_launch_us": round(float(np.mean(per)) * 1e6, 2),
+                     "launch_us_p10_p50_p90": [round(float(q10), 2), round(float(q50), 2), round(float(q90), 2)],
+                     "flops_per_launch": int(flops)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES):
     """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) into
     the committed summary: mean KiB per dispatch of the layer kernel and of the
@@ -535,8 +621,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, choices=range(1, 9), metavar="M")
     ap.add_argument("--workload", default="moe",
-                    choices=["moe", "moe_tp8", "moe_full", "gemv_small", "gate_up", "lm_head", "q4_stack"],
+                    choices=["moe", "moe_tp8", "moe_full", "gemv_small", "gate_up", "lm_head", "q4_stack", "prefill"],
                     help="moe (default: the routed layer) or one of the dense configurations")
+    ap.add_argument("--tokens", type=int, default=4096, help="prefill workload: tokens per call")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -552,6 +639,9 @@ def main():
         return
     if args.profile_pass:
         profile_pass(args)
+        return
+    if args.workload == "prefill":
+        run_prefill(args)
         return
     if args.workload not in ("moe", "moe_tp8", "moe_full"):
         run_dense(args)

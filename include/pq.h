@@ -159,6 +159,14 @@ int pq_gemm_fp8(const uint16_t* x, int M, int K,
                 int epi, uint16_t* y,
                 void* ws, size_t ws_bytes, void* stream);
 
+/* The GEMM launch of pq_gemm_fp8 alone, on an activation already quantised by
+ * the rule of pq_quantize_fp8 (for a caller whose previous step produced it):
+ *   xq : E4M3 [M,K]     xs : fp32 [M,K/128]
+ * Other arguments, constraints and results as pq_gemm_fp8; no workspace. */
+int pq_gemm_fp8_prequant(const uint8_t* xq, const float* xs, int M, int K,
+                         const uint8_t* w, const float* w_scale, int N,
+                         int epi, uint16_t* y, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* int4 g32 weight-streaming GEMV (W4A16): [M3] Q4 decode.                    */
 /* ------------------------------------------------------------------------- */

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemv_q4", "moe_decode_layer",
+__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemm_fp8_prequant", "gemv_q4", "moe_decode_layer",
            "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call", "stream_probe",
            "EPI_NONE", "EPI_SILU_MUL", "lib"]
 
@@ -168,6 +168,24 @@ def gemm_fp8(x, w, w_scale, epi: int = EPI_NONE, debug: bool = False, out=None):
     off2 = off + (M * K + 255) // 256 * 256
     xs = ws[off2:off2 + M * (K // 128) * 4].view(torch.float32).view(M, K // 128)
     return y, xq, xs
+
+
+def gemm_fp8_prequant(xq, xs, w, w_scale, epi: int = EPI_NONE, out=None):
+    """The GEMM of gemm_fp8 on an activation already quantised (xq uint8 [M,K], xs fp32
+    [M,K/128], the rule of quantize_fp8)."""
+    _need(xq, torch.uint8, 2, "xq")
+    _need(xs, torch.float32, 2, "xs")
+    _need(w, torch.uint8, 2, "w")
+    _need(w_scale, torch.float32, 2, "w_scale")
+    M, K = xq.shape
+    N = w.shape[0]
+    if w.shape[1] != K or w_scale.shape != (N, K // 128) or xs.shape != (M, K // 128):
+        raise ValueError("shapes do not match")
+    n_out = N // 2 if epi == EPI_SILU_MUL else N
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=xq.device)
+    _check(lib().pq_gemm_fp8_prequant(_p(xq), _p(xs), M, K, _p(w), _p(w_scale), N, epi, _p(y), _stream()),
+           "pq_gemm_fp8_prequant")
+    return y
 
 
 def gemv_q4(x, w, w_scale, epi: int = EPI_NONE, out=None):

@@ -24,6 +24,7 @@ SIGNATURES = {
     "pq_gemv_fp8": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "pq_gemm_fp8_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "pq_gemm_fp8": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "pq_gemm_fp8_prequant": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "pq_gemv_q4_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "pq_gemv_q4": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
     "moe_decode_layer_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),

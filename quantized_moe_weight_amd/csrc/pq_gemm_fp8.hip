@@ -10,7 +10,8 @@
 // gfx950 design
 //   * a 512-thread block (8 waves, 2 x 4) owns a 256-token x 256-weight-row
 //     tile (64 KB of operands per K step for 16.8 MFLOP: large tiles keep the
-//     L2 traffic within what eight L2s deliver); each wave a 128 x 64 part =
+//     L2 traffic within what eight L2s deliver; 128-token tiles where 256 would
+//     leave CUs without a tile); each wave a 128 x 64 part =
 //     8 x 4 v_mfma_f32_16x16x128_f8f6f4 per 128-wide K block (the scale
 //     block), whose fp32 results take both block scales (acc += d * (s_x *
 //     s_w)) in fp32 on the vector unit; two waves per SIMD, so one wave's
@@ -48,19 +49,20 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / pq::kWave;
-constexpr int BM = 256, BN = 256;             // tokens and weight rows per tile
-constexpr int WM = BM / 2 / 16;               // row tiles per wave (waves: 2 along the tokens)
+constexpr int BN = 256;                       // weight rows per tile (tokens per tile: BM, 256 or 128)
 // one pipeline stage in LDS: A and B tiles (128-byte rows, swizzled slots)
-// and their block scales
+// and their block scales (the token-scale area always holds 256, the waves
+// 0-3 each loading 64 of them)
+template <int BM>
 struct Stage {
   uint8_t a[BM * pq::kBlock];
   uint8_t b[BN * pq::kBlock];
-  float sa[BM];
+  float sa[256];
   float sb[BN];
 };
 typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kXcds = 8;
-static_assert(2 * sizeof(Stage) <= 160 * 1024, "stages must fit LDS");
+static_assert(2 * sizeof(Stage<256>) <= 160 * 1024, "stages must fit LDS");
 
 struct GArgs {
   const uint8_t* xq;     // [M][K]
@@ -98,9 +100,11 @@ __device__ __forceinline__ int b_row(const GArgs& a, int tile_n, int r) {
   return (q & 1) ? c + a.R : c;
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
-  __shared__ __align__(16) Stage st0;
-  __shared__ __align__(16) Stage st1;
+// The kernel body for BM-token tiles; st0 and st1 are the kernel's two
+// stages (separate LDS objects, sized for the larger tile).
+template <int BM>
+__device__ __forceinline__ void gemm_body(const GArgs& a, Stage<256>& st0, Stage<256>& st1) {
+  constexpr int WM = BM / 2 / 16;             // row tiles per wave (waves: 2 along the tokens)
   const int lane = pq::lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(pq::wave_id());
   const int wm = wv >> 2, wn = wv & 3;        // this wave's part of the tile: rows 128 wm.., cols 64 wn..
@@ -142,13 +146,13 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
   const bool xscale = wv < 4;
   if (xscale) {
     const int m = m0 + 64 * wv + lane;
-    soff = m < a.M ? (uint32_t)m * (uint32_t)nb * 4u : pq::kOOB;
+    soff = 64 * wv + lane < BM && m < a.M ? (uint32_t)m * (uint32_t)nb * 4u : pq::kOOB;
   } else {
     const int n = b_row(a, tile_n, 64 * (wv - 4) + lane);
     soff = n >= 0 ? (uint32_t)n * (uint32_t)nb * 4u : pq::kOOB;
   }
 
-  auto issue = [&](Stage& st, int kb) {
+  auto issue = [&](Stage<256>& st, int kb) {
     const uint32_t kofs = (uint32_t)kb * pq::kBlock;
 #pragma unroll
     for (int i = 0; i < BM / 64; ++i)
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
   // operand reads: slots lg and lg + 4 of a row, after the swizzle
   const uint32_t sw_lo = 16u * (uint32_t)(lg ^ (rl & 7)), sw_hi = 16u * (uint32_t)((lg + 4) ^ (rl & 7));
 
-  auto compute = [&](const Stage& st) {
+  auto compute = [&](const Stage<256>& st) {
     int32x8 bf[4];
     float swv[4];
 #pragma unroll
@@ -185,9 +189,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      const uint8_t* p = st.a + (128 * wm + 16 * i + rl) * pq::kBlock;
+      const uint8_t* p = st.a + ((BM / 2) * wm + 16 * i + rl) * pq::kBlock;
       const int32x8 af = join8(*reinterpret_cast<const uint4*>(p + sw_lo), *reinterpret_cast<const uint4*>(p + sw_hi));
-      const float4 sx = *reinterpret_cast<const float4*>(st.sa + 128 * wm + 16 * i + 4 * lg);
+      const float4 sx = *reinterpret_cast<const float4*>(st.sa + (BM / 2) * wm + 16 * i + 4 * lg);
       const float sxv[4] = {sx.x, sx.y, sx.z, sx.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
   for (int i = 0; i < WM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 128 * wm + 16 * i + 4 * lg + r;
+      const int m = m0 + (BM / 2) * wm + 16 * i + 4 * lg + r;
       if (m >= a.M) continue;
       if (!a.silu) {
 #pragma unroll
@@ -238,6 +242,18 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(GArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel_t256(GArgs a) {
+  __shared__ __align__(16) Stage<256> st0;
+  __shared__ __align__(16) Stage<256> st1;
+  gemm_body<256>(a, st0, st1);
+}
+
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel_t128(GArgs a) {
+  __shared__ __align__(16) Stage<256> st0;
+  __shared__ __align__(16) Stage<256> st1;
+  gemm_body<128>(a, st0, st1);
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +268,36 @@ size_t pq_gemm_fp8_workspace(int M, int K, int N, int epi) {
   return pq::kWsDataOff + pqhost::align_up((size_t)M * K, 256) + pqhost::align_up((size_t)M * (K / pq::kBlock) * 4, 256);
 }
 
+int pq_gemm_fp8_prequant(const uint8_t* xq, const float* xs, int M, int K, const uint8_t* w, const float* w_scale,
+                         int N, int epi, uint16_t* y, void* stream) {
+  if (!xq || !xs || !w || !w_scale || !y) return PQ_ERR_NULL;
+  if (M < 1 || K < pq::kBlock || K % pq::kBlock != 0 || N < 1) return PQ_ERR_SHAPE;
+  if (epi != PQ_EPI_NONE && epi != PQ_EPI_SILU_MUL) return PQ_ERR_SHAPE;
+  if (epi == PQ_EPI_SILU_MUL && N % 2 != 0) return PQ_ERR_SHAPE;
+  if ((size_t)N * K > pq::kMaxBufferBytes || (size_t)M * K > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
+  if (!pqhost::aligned16(xq) || !pqhost::aligned16(xs) || !pqhost::aligned16(w) || !pqhost::aligned16(w_scale) ||
+      !pqhost::aligned16(y))
+    return PQ_ERR_ALIGN;
+  pqhost::DeviceInfo dev;
+  const int st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+  GArgs a;
+  a.xq = xq; a.xs = xs; a.w = w; a.ws = w_scale; a.y = y;
+  a.M = M; a.K = K; a.N = N;
+  a.silu = epi == PQ_EPI_SILU_MUL;
+  a.R = a.silu ? N / 2 : N;
+  a.tn = a.silu ? (a.R + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  // 256-token tiles where they still give every CU a tile, else 128
+  const bool big = (long)((M + 255) / 256) * a.tn >= dev.num_cus;
+  a.tm = big ? (M + 255) / 256 : (M + 127) / 128;
+  if (big)
+    hipLaunchKernelGGL(gemm_fp8_kernel_t256, dim3((unsigned)(a.tm * a.tn)), dim3(kThreads), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(gemm_fp8_kernel_t128, dim3((unsigned)(a.tm * a.tn)), dim3(kThreads), 0, (hipStream_t)stream, a);
+  PQ_HIP_CHECK(hipGetLastError());
+  return PQ_OK;
+}
+
 int pq_gemm_fp8(const uint16_t* x, int M, int K, const uint8_t* w, const float* w_scale, int N, int epi,
                 uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
   if (!x || !w || !w_scale || !y) return PQ_ERR_NULL;
@@ -264,25 +310,11 @@ int pq_gemm_fp8(const uint16_t* x, int M, int K, const uint8_t* w, const float* 
   const size_t need = pq_gemm_fp8_workspace(M, K, N, epi);
   if (ws == nullptr || ws_bytes < need) return PQ_ERR_WORKSPACE;
   if (!pqhost::aligned16(ws)) return PQ_ERR_ALIGN;
-  pqhost::DeviceInfo dev;
-  int st = pqhost::current_device_info(&dev);
-  if (st != PQ_OK) return st;
-
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws) + pq::kWsDataOff;
   float* xs = reinterpret_cast<float*>(xq + pqhost::align_up((size_t)M * K, 256));
-  st = pq_quantize_fp8(x, 0, M, K, xq, xs, stream);      // the live activation rule, one pass
+  const int st = pq_quantize_fp8(x, 0, M, K, xq, xs, stream);      // the live activation rule, one pass
   if (st != PQ_OK) return st;
-
-  GArgs a;
-  a.xq = xq; a.xs = xs; a.w = w; a.ws = w_scale; a.y = y;
-  a.M = M; a.K = K; a.N = N;
-  a.silu = epi == PQ_EPI_SILU_MUL;
-  a.R = a.silu ? N / 2 : N;
-  a.tm = (M + BM - 1) / BM;
-  a.tn = a.silu ? (a.R + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  hipLaunchKernelGGL(gemm_fp8_kernel, dim3((unsigned)(a.tm * a.tn)), dim3(kThreads), 0, (hipStream_t)stream, a);
-  PQ_HIP_CHECK(hipGetLastError());
-  return PQ_OK;
+  return pq_gemm_fp8_prequant(xq, xs, M, K, w, w_scale, N, epi, y, stream);
 }
 
 }  // extern "C"

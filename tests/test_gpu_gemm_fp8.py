@@ -102,6 +102,21 @@ def test_gemm_fp8_leaves_shared_workspace_state(pq):
     assert int(torch.count_nonzero(ws[256:pq.WS_DATA_OFF])) == 0
 
 
+def test_gemm_fp8_prequant_equals_the_fused_call(pq):
+    """The GEMM on the activation quantised beforehand (by the library's own
+    quantiser) gives the bits of the call that quantises it itself."""
+    import torch
+    M, K, N = 333, 1536, 700
+    x = workloads.activation_bf16(M, K, workload=workloads.FP8_GATE_UP, seed=12)
+    q, sc, _, _ = _weights(pq, N, K, seed=12, workload=workloads.FP8_GATE_UP)
+    xt = np_bf16_bits_to_torch(x)
+    for epi in (pq.EPI_NONE, pq.EPI_SILU_MUL):
+        y = pq.gemm_fp8(xt, q, sc, epi=epi)
+        xq, xs = pq.quantize_fp8(xt)
+        y2 = pq.gemm_fp8_prequant(xq, xs, q, sc, epi=epi)
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 def test_gemm_fp8_rejects_bad_shapes(pq):
     import torch
     x = torch.zeros((4, 100), dtype=torch.bfloat16, device="cuda")

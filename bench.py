@@ -584,7 +584,16 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES):
     txt = json.dumps(d, indent=1)
     os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
     with open(PMC_SUMMARY, "w", encoding="utf-8") as fh:
-        fh.write(txt + "\n---\n" + f"source: {fetch_csv}, {write_csv}\n")
+        fh.write(txt + "\n---\n" + f"source: {fetch_csv}, {write_csv}\n"
+                 "made by (from the repository root on the MI355X box, $REPO = that root):\n"
+                 "  cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d "
+                 "$REPO/<dir>/fetch -o f -- python3 $REPO/bench.py --profile-pass --steps 20\n"
+                 "  cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d "
+                 "$REPO/<dir>/write -o w -- python3 $REPO/bench.py --profile-pass --steps 20\n"
+                 "  python3 bench.py --ingest-pmc <dir>/fetch/f_counter_collection.csv "
+                 "<dir>/write/w_counter_collection.csv\n"
+                 "fetch_kib / write_kib: mean KiB per dispatch of the layer kernel; the scales are the copy "
+                 "kernel's known bytes over what the same counters read for it.\n")
     print(txt)
 
 

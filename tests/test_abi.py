@@ -77,3 +77,72 @@ def test_workspace_helpers_host_validation(lib):
     assert lib.pq_workspace_init(NUL, 64, NUL) == PQ_ERR_NULL
     assert lib.pq_workspace_init(MIS, 64, NUL) == PQ_ERR_ALIGN
     assert lib.pq_workspace_check(NUL, NUL) == PQ_ERR_NULL
+
+
+def test_gemv_q4_host_validation(lib):
+    g = lib.pq_gemv_q4
+    args = lambda x=FAKE, M=1, K=512, w=FAKE, s=FAKE, N=256, epi=0, y=FAKE, ws=NUL, wsn=0: (  # noqa: E731
+        x, M, K, w, s, N, epi, y, ws, wsn, NUL)
+    assert g(*args(x=NUL)) == PQ_ERR_NULL
+    assert g(*args(s=NUL)) == PQ_ERR_NULL
+    assert g(*args(M=0)) == PQ_ERR_SHAPE
+    assert g(*args(M=9)) == PQ_ERR_SHAPE
+    assert g(*args(K=48)) == PQ_ERR_SHAPE
+    assert g(*args(epi=1, N=7)) == PQ_ERR_SHAPE
+    assert g(*args(y=MIS)) == PQ_ERR_ALIGN
+
+
+def _moe_ex_args(x=FAKE, M=1, H=512, wr=NUL, lg=FAKE, ids=FAKE, w=FAKE, E=16, k=4, I=256,
+                 sh=(NUL, NUL, NUL, NUL), out=FAKE, ws=FAKE, wsn=1 << 30):
+    return (x, M, H, wr, lg, ids, w, E, k, I, FAKE, FAKE, FAKE, FAKE, *sh, out, NUL, NUL, NUL, ws, wsn, NUL)
+
+
+def test_moe_layer_host_validation(lib):
+    g = lib.moe_decode_layer_ex
+    a = _moe_ex_args
+    assert g(*a(x=NUL)) == PQ_ERR_NULL
+    assert g(*a(ws=NUL)) == PQ_ERR_NULL
+    assert g(*a(sh=(FAKE, FAKE, NUL, FAKE))) == PQ_ERR_NULL      # the shared expert: all four or none
+    assert g(*a(M=0)) == PQ_ERR_SHAPE
+    assert g(*a(M=9)) == PQ_ERR_SHAPE
+    assert g(*a(k=9)) == PQ_ERR_SHAPE
+    assert g(*a(E=3)) == PQ_ERR_SHAPE                              # fewer experts than top_k
+    assert g(*a(E=2000)) == PQ_ERR_SHAPE
+    assert g(*a(H=500)) == PQ_ERR_SHAPE
+    assert g(*a(I=200)) == PQ_ERR_SHAPE
+    assert g(*a(x=MIS)) == PQ_ERR_ALIGN
+    assert g(*a(wr=MIS)) == PQ_ERR_ALIGN
+    assert g(*a(wsn=1024)) == PQ_ERR_WORKSPACE
+    # the plain entry point forwards to the same checks
+    p = lib.moe_decode_layer
+    assert p(NUL, 1, 512, FAKE, FAKE, FAKE, 16, 4, 256, FAKE, FAKE, FAKE, FAKE, FAKE, NUL, NUL, NUL, FAKE,
+             1 << 30, NUL) == PQ_ERR_NULL
+    assert p(FAKE, 1, 512, FAKE, FAKE, FAKE, 16, 4, 256, FAKE, FAKE, FAKE, FAKE, FAKE, NUL, NUL, NUL, FAKE,
+             1024, NUL) == PQ_ERR_WORKSPACE
+
+
+def test_moe_workspace_sizes(lib):
+    ws = lib.moe_decode_layer_workspace
+    assert ws(1, 6144, 2048, 256, 8) > 0
+    assert ws(8, 6144, 2048, 256, 8) >= ws(1, 6144, 2048, 256, 8)
+    assert ws(0, 6144, 2048, 256, 8) == 0
+    assert ws(1, 6144, 2000, 256, 8) == 0
+
+
+def test_gemm_fp8_host_validation(lib):
+    g = lib.pq_gemm_fp8
+    args = lambda x=FAKE, M=64, K=512, w=FAKE, s=FAKE, N=256, epi=0, y=FAKE, ws=FAKE, wsn=1 << 30: (  # noqa: E731
+        x, M, K, w, s, N, epi, y, ws, wsn, NUL)
+    assert g(*args(x=NUL)) == PQ_ERR_NULL
+    assert g(*args(M=0)) == PQ_ERR_SHAPE
+    assert g(*args(K=300)) == PQ_ERR_SHAPE
+    assert g(*args(epi=1, N=255)) == PQ_ERR_SHAPE
+    assert g(*args(w=MIS)) == PQ_ERR_ALIGN
+    assert g(*args(ws=NUL)) == PQ_ERR_WORKSPACE
+    assert g(*args(wsn=4096)) == PQ_ERR_WORKSPACE
+    assert lib.pq_gemm_fp8_workspace(64, 512, 256, 0) >= 64 * 512 + 64 * 4 * 4
+    assert lib.pq_gemm_fp8_workspace(64, 500, 256, 0) == 0
+    q = lib.pq_gemm_fp8_prequant
+    assert q(NUL, FAKE, 64, 512, FAKE, FAKE, 256, 0, FAKE, NUL) == PQ_ERR_NULL
+    assert q(FAKE, FAKE, 64, 512, FAKE, FAKE, 256, 3, FAKE, NUL) == PQ_ERR_SHAPE
+    assert q(FAKE, MIS, 64, 512, FAKE, FAKE, 256, 0, FAKE, NUL) == PQ_ERR_ALIGN

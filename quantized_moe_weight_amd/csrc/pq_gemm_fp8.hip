@@ -18,10 +18,16 @@
 //     matrix work covers the other's waits;
 //   * operands stream from memory straight into LDS (buffer loads with an
 //     LDS destination: no registers) for K step k + 1 while step k computes;
-//     the two stages are separate LDS objects and the loop is unrolled by
-//     two, so the compiler knows that the operand reads of one stage do not
-//     wait for the loads into the other; one block barrier per K step, after
-//     each wave has waited for its own loads of the step;
+//     one block barrier per K step, after each wave has waited for its own
+//     loads of the step; the loads are issued from inline assembly, because
+//     the compiler's wait insertion cannot tell the two stages apart and
+//     otherwise waits for the next stage before reading the current one
+//     (which took away the overlap on every other step);
+//   * the block scales of sub-tile t - 1 are applied while the matrix core
+//     works on sub-tile t (on this chip the vector and matrix work of a
+//     SIMD do not overlap in time, measured with a register-only probe, so
+//     the scaling's two fp32 operations per output and block cost what the
+//     matrix instructions cost: the kernel is bound by their sum);
 //   * a wave's load instruction covers 8 rows x 128 bytes (whole lines) and
 //     lands as 1 KB of LDS; in LDS the 16-byte slot s of row r holds global
 //     slot s ^ (r % 8), which spreads the operand reads over all banks;
@@ -32,8 +38,9 @@
 //     in runs of 32 as gate, up, gate, up, ..., so each wave's column tiles b
 //     and b + 2 are the gate and the up of the same outputs, in the same
 //     lanes;
-//   * tiles are dealt to the 8 XCDs in contiguous runs, token tiles fastest,
-//     so the blocks that share a weight tile share an L2.
+//   * tiles are dealt to the 8 XCDs in contiguous runs of a grouped order
+//     (8 token tiles by as many weight tiles as the run needs), so the blocks
+//     that share an operand tile share an L2.
 #include <stdlib.h>
 #include <string.h>
 
@@ -62,6 +69,7 @@ struct Stage {
 };
 typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kXcds = 8;
+constexpr int kGroupM = 8;                    // token tiles per group of the tile order
 static_assert(2 * sizeof(Stage<256>) <= 160 * 1024, "stages must fit LDS");
 
 struct GArgs {
@@ -78,6 +86,32 @@ struct GArgs {
 __device__ __forceinline__ floatx4 mfma_e4m3(int32x8 a, int32x8 b) {
   // block-scale operands 0: the plain (unscaled) matrix instruction
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+}
+
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource (stride 0, num_records = bytes) as four scalar words,
+// for the buffer-to-LDS loads below.
+__device__ __forceinline__ int32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return int32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)(lds_ptr)p);
+}
+// Buffer-to-LDS loads (lane l's bytes land at lds + l * size).  Written as
+// assembly on purpose: the compiler's wait insertion cannot tell the two
+// stages apart and would wait for the next stage's loads before every read of
+// the current one; the kernel orders these loads itself (each wave waits for
+// its own with vmcnt(0) before the block barrier that precedes their readers).
+__device__ __forceinline__ void dma16(int32x4 r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(int32x4 r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
 }
 
 __device__ __forceinline__ int32x8 join8(uint4 lo, uint4 hi) {
@@ -110,20 +144,26 @@ __device__ __forceinline__ void gemm_body(const GArgs& a, Stage<256>& st0, Stage
   const int wm = wv >> 2, wn = wv & 3;        // this wave's part of the tile: rows 128 wm.., cols 64 wn..
   const int rl = lane & 15, lg = lane >> 4;
 
-  // tile of this block: contiguous runs per XCD (block b runs on XCD b % 8),
-  // token tiles fastest
+  // tile of this block: contiguous runs per XCD (block b runs on XCD b % 8)
+  // in an order that visits groups of kGroupM token tiles, token tiles
+  // fastest inside a group, so an XCD's run is a compact rectangle of tiles
+  // (32 tiles: 8 token tiles x 4 weight tiles, 12 operand tiles per K step
+  // from outside its L2 instead of 18 for a 16 x 2 strip)
   const int T = a.tm * a.tn;
   const int T8 = T / kXcds * kXcds;
   const int b = (int)blockIdx.x;
   const int t = b < T8 ? (b % kXcds) * (T8 / kXcds) + b / kXcds : b;
-  const int tile_m = t % a.tm, tile_n = t / a.tm;
+  const int grp = t / (kGroupM * a.tn);
+  const int gsz = min(kGroupM, a.tm - grp * kGroupM);
+  const int tg = t - grp * kGroupM * a.tn;
+  const int tile_m = grp * kGroupM + tg % gsz, tile_n = tg / gsz;
   const int m0 = tile_m * BM;
   const int nb = a.K / pq::kBlock;
 
-  const pq::rsrc_t xr = pq::make_rsrc(a.xq, (uint32_t)((size_t)a.M * a.K));
-  const pq::rsrc_t wr = pq::make_rsrc(a.w, (uint32_t)((size_t)a.N * a.K));
-  const pq::rsrc_t xsr = pq::make_rsrc(a.xs, (uint32_t)((size_t)a.M * nb * 4));
-  const pq::rsrc_t wsr = pq::make_rsrc(a.ws, (uint32_t)((size_t)a.N * nb * 4));
+  const int32x4 xr = rsrc_words(a.xq, (uint32_t)((size_t)a.M * a.K));
+  const int32x4 wr = rsrc_words(a.w, (uint32_t)((size_t)a.N * a.K));
+  const int32x4 xsr = rsrc_words(a.xs, (uint32_t)((size_t)a.M * nb * 4));
+  const int32x4 wsr = rsrc_words(a.ws, (uint32_t)((size_t)a.N * nb * 4));
 
   // this lane's loads: row 64 i + 8 wv + lane / 8 of A and of B (i < 4),
   // global slot (lane % 8) ^ (lane / 8) of the K block (it lands in LDS slot
@@ -152,19 +192,19 @@ __device__ __forceinline__ void gemm_body(const GArgs& a, Stage<256>& st0, Stage
     soff = n >= 0 ? (uint32_t)n * (uint32_t)nb * 4u : pq::kOOB;
   }
 
+  // issue(st, kb) with kb >= nb loads nothing (every offset out of range), so
+  // the call needs no branch around it
   auto issue = [&](Stage<256>& st, int kb) {
+    const bool live = kb < nb;
     const uint32_t kofs = (uint32_t)kb * pq::kBlock;
 #pragma unroll
     for (int i = 0; i < BM / 64; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(st.a + (64 * i + 8 * wv) * pq::kBlock), 16,
-                                               aoff[i] == pq::kOOB ? pq::kOOB : aoff[i] + kofs, 0, 0, 0);
+      dma16(xr, lds_addr(st.a + (64 * i + 8 * wv) * pq::kBlock), aoff[i] == pq::kOOB || !live ? pq::kOOB : aoff[i] + kofs);
 #pragma unroll
     for (int i = 0; i < BN / 64; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr)(st.b + (64 * i + 8 * wv) * pq::kBlock), 16,
-                                               boff[i] == pq::kOOB ? pq::kOOB : boff[i] + kofs, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xscale ? xsr : wsr,
-                                             (lds_ptr)(xscale ? st.sa + 64 * wv : st.sb + 64 * (wv - 4)), 4,
-                                             soff == pq::kOOB ? pq::kOOB : soff + (uint32_t)kb * 4u, 0, 0, 0);
+      dma16(wr, lds_addr(st.b + (64 * i + 8 * wv) * pq::kBlock), boff[i] == pq::kOOB || !live ? pq::kOOB : boff[i] + kofs);
+    dma4(xscale ? xsr : wsr, lds_addr(xscale ? st.sa + 64 * wv : st.sb + 64 * (wv - 4)),
+         soff == pq::kOOB || !live ? pq::kOOB : soff + (uint32_t)kb * 4u);
   };
 
   float acc[WM][4][4];
@@ -187,19 +227,33 @@ __device__ __forceinline__ void gemm_body(const GArgs& a, Stage<256>& st0, Stage
       bf[j] = join8(*reinterpret_cast<const uint4*>(p + sw_lo), *reinterpret_cast<const uint4*>(p + sw_hi));
       swv[j] = st.sb[64 * wn + 16 * j + rl];
     }
+    // software pipeline over the 4 WM sub-tiles: the block scales of sub-tile
+    // t - 1 are applied while the matrix core works on sub-tile t
+    int32x8 af;
+    float sxv[4], sxp[4];
+    floatx4 dp;
 #pragma unroll
-    for (int i = 0; i < WM; ++i) {
-      const uint8_t* p = st.a + ((BM / 2) * wm + 16 * i + rl) * pq::kBlock;
-      const int32x8 af = join8(*reinterpret_cast<const uint4*>(p + sw_lo), *reinterpret_cast<const uint4*>(p + sw_hi));
-      const float4 sx = *reinterpret_cast<const float4*>(st.sa + (BM / 2) * wm + 16 * i + 4 * lg);
-      const float sxv[4] = {sx.x, sx.y, sx.z, sx.w};
+    for (int t = 0; t < 4 * WM; ++t) {
+      const int i = t >> 2, j = t & 3;
+      if (j == 0) {
+        const uint8_t* p = st.a + ((BM / 2) * wm + 16 * i + rl) * pq::kBlock;
+        af = join8(*reinterpret_cast<const uint4*>(p + sw_lo), *reinterpret_cast<const uint4*>(p + sw_hi));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const floatx4 d = mfma_e4m3(af, bf[j]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(d[r], sxv[r] * swv[j], acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) sxp[r] = sxv[r];
+        const float4 sx = *reinterpret_cast<const float4*>(st.sa + (BM / 2) * wm + 16 * i + 4 * lg);
+        sxv[0] = sx.x; sxv[1] = sx.y; sxv[2] = sx.z; sxv[3] = sx.w;
       }
+      const floatx4 d = mfma_e4m3(af, bf[j]);
+      if (t > 0) {
+        const int ip = (t - 1) >> 2, jp = (t - 1) & 3;
+        const float* s = jp == 3 ? sxp : sxv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[ip][jp][r] = fmaf(dp[r], s[r] * swv[jp], acc[ip][jp][r]);
+      }
+      dp = d;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[WM - 1][3][r] = fmaf(dp[r], sxv[r] * swv[3], acc[WM - 1][3][r]);
   };
   // every wave's loads of the next stage have landed, and every wave is done
   // with the stage about to be refilled (the memory clobber keeps the LDS
@@ -209,13 +263,14 @@ __device__ __forceinline__ void gemm_body(const GArgs& a, Stage<256>& st0, Stage
   issue(st0, 0);
   for (int kb = 0; kb < nb; kb += 2) {
     step_barrier();
-    if (kb + 1 < nb) issue(st1, kb + 1);
+    issue(st1, kb + 1);
     compute(st0);
     if (kb + 1 >= nb) break;
     step_barrier();
-    if (kb + 2 < nb) issue(st0, kb + 2);
+    issue(st0, kb + 2);
     compute(st1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // epilogue: lane (g, j) of sub-tile (i, b) holds tokens 4g..4g+3 of row
   // tile i and column j of column tile b

@@ -100,18 +100,20 @@ __device__ __forceinline__ int32x4 rsrc_words(const void* base, uint32_t bytes) 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)(lds_ptr)p);
 }
-// Buffer-to-LDS loads (lane l's bytes land at lds + l * size).  Written as
-// assembly on purpose: the compiler's wait insertion cannot tell the two
-// stages apart and would wait for the next stage's loads before every read of
-// the current one; the kernel orders these loads itself (each wave waits for
-// its own with vmcnt(0) before the block barrier that precedes their readers).
-__device__ __forceinline__ void dma16(int32x4 r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+// Buffer-to-LDS loads (lane l's bytes land at lds + l * size) at byte offset
+// voff + soff of the buffer (voff per lane, soff wave-uniform; a lane whose
+// voff is past the buffer loads zeros).  Written as assembly on purpose: the
+// compiler's wait insertion cannot tell the two stages apart and would wait
+// for the next stage's loads before every read of the current one; the kernel
+// orders these loads itself (each wave waits for its own with vmcnt(0) before
+// the block barrier that precedes their readers).
+__device__ __forceinline__ void dma16(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(int32x4 r, uint32_t lds, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(r) : "memory", "m0");
+__device__ __forceinline__ void dma4(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 
 __device__ __forceinline__ int32x8 join8(uint4 lo, uint4 hi) {
@@ -192,19 +194,18 @@ __device__ __forceinline__ void gemm_body(const GArgs& a, Stage<256>& st0, Stage
     soff = n >= 0 ? (uint32_t)n * (uint32_t)nb * 4u : pq::kOOB;
   }
 
-  // issue(st, kb) with kb >= nb loads nothing (every offset out of range), so
-  // the call needs no branch around it
+  // the loads of K block kb into stage st (none past the last block); the
+  // block's offset rides in the scalar offset, so the per-lane offsets above
+  // (out of range for rows past the matrix) need no work per step
   auto issue = [&](Stage<256>& st, int kb) {
-    const bool live = kb < nb;
-    const uint32_t kofs = (uint32_t)kb * pq::kBlock;
+    if (kb >= nb) return;
+    const uint32_t kofs = (uint32_t)__builtin_amdgcn_readfirstlane(kb * pq::kBlock);
 #pragma unroll
-    for (int i = 0; i < BM / 64; ++i)
-      dma16(xr, lds_addr(st.a + (64 * i + 8 * wv) * pq::kBlock), aoff[i] == pq::kOOB || !live ? pq::kOOB : aoff[i] + kofs);
+    for (int i = 0; i < BM / 64; ++i) dma16(xr, lds_addr(st.a + (64 * i + 8 * wv) * pq::kBlock), aoff[i], kofs);
 #pragma unroll
-    for (int i = 0; i < BN / 64; ++i)
-      dma16(wr, lds_addr(st.b + (64 * i + 8 * wv) * pq::kBlock), boff[i] == pq::kOOB || !live ? pq::kOOB : boff[i] + kofs);
-    dma4(xscale ? xsr : wsr, lds_addr(xscale ? st.sa + 64 * wv : st.sb + 64 * (wv - 4)),
-         soff == pq::kOOB || !live ? pq::kOOB : soff + (uint32_t)kb * 4u);
+    for (int i = 0; i < BN / 64; ++i) dma16(wr, lds_addr(st.b + (64 * i + 8 * wv) * pq::kBlock), boff[i], kofs);
+    dma4(xscale ? xsr : wsr, lds_addr(xscale ? st.sa + 64 * wv : st.sb + 64 * (wv - 4)), soff,
+         (uint32_t)__builtin_amdgcn_readfirstlane(kb * 4));
   };
 
   float acc[WM][4][4];

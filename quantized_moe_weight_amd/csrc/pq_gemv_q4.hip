@@ -12,9 +12,10 @@
 //     order, so K is split inside the block wherever a row straddles two
 //     waves, and the split is reduced through LDS after one barrier: no
 //     global partials, atomics or store waits in the stream;
-//   * each wave keeps D chunks in flight in a ring of raw buffer loads issued
-//     without branches (out-of-range slots return zero without memory
-//     traffic), and the last D steps drain the ring without issuing;
+//   * each wave keeps D chunk steps in flight in a ring of raw buffer loads
+//     issued without branches (out-of-range slots return zero without memory
+//     traffic), and the last D steps drain the ring without issuing; shallow
+//     rings (3-4 steps) stream faster here than deep ones;
 //   * unpacking without a packed bf16 subtract: nibble n becomes the bf16
 //     value 1 + n/16 (n shifted into the top mantissa bits under the exponent
 //     of 1.0) with one shift and one and-or per pair, v_dot2 multiplies it with
@@ -25,6 +26,7 @@
 //     plus 1.5 times the per-group sums of x; the activation loads are issued
 //     before the weight ring so staging does not wait for weights.
 #include <stdlib.h>
+#include <type_traits>
 #include <string.h>
 
 #include "pq_common.h"
@@ -131,7 +133,13 @@ __device__ __forceinline__ void stage_group(uint4* xs_l, float* gsum, int slot, 
   gsum[slot] = dot32(th, xv);
 }
 
-template <int NROW, int D, int MT>
+// PAIR (the groups per row, K / 32, even): each lane loads the aligned dword
+// that holds its group's scale and its neighbour's (lanes 2i and 2i + 1 share
+// it) and keeps its own half.  A 16-bit scale per ring slot made the compiler
+// pack the slots' scales pairwise at the end of every ring cycle, which waited
+// for nearly every load in flight (the ring drained to two loads once per
+// cycle); 32-bit values are never packed.
+template <int NROW, int D, int MT, bool PAIR>
 __global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint4* xs_l = reinterpret_cast<uint4*>(smem);
@@ -168,18 +176,23 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
   const pq::rsrc_t sr = pq::make_rsrc(a.wsc, (uint32_t)((size_t)a.N * ng * 2));
   const uint32_t lane16 = 16u * (uint32_t)lane;
 
+  typedef typename std::conditional<PAIR, uint32_t, _Float16>::type SType;
   uint4 wbuf[D][NROW];
-  _Float16 sbuf[D][NROW];
+  SType sbuf[D][NROW];
   int ir = u0 / a.nch, ic = u0 - (u0 / a.nch) * a.nch, left = nsteps;
-  auto issue = [&](uint4 (&wb)[NROW], _Float16 (&sb)[NROW]) {
+  auto issue = [&](uint4 (&wb)[NROW], SType (&sb)[NROW]) {
     const uint32_t off = (uint32_t)(ic * pq::kChunk) + lane16;     // packed byte in the row
     const bool ok = left > 0 && off < rowb;
 #pragma unroll
     for (int j = 0; j < NROW; ++j) {
       const uint32_t row = (uint32_t)(r0 + ir + j * a.R);
       wb[j] = pq::buf_load16_nt(wr, ok ? row * rowb + off : pq::kOOB);
-      sb[j] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
-          sr, (int)(ok ? (row * (uint32_t)ng + off / 16u) * 2u : pq::kOOB), 0, pq::kAuxNT));
+      if constexpr (PAIR)
+        sb[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            sr, (int)(ok ? (row * (uint32_t)ng + ((off / 16u) & ~1u)) * 2u : pq::kOOB), 0, pq::kAuxNT);
+      else
+        sb[j] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
+            sr, (int)(ok ? (row * (uint32_t)ng + off / 16u) * 2u : pq::kOOB), 0, pq::kAuxNT));
     }
     --left;
     if (++ic == a.nch) { ic = 0; ++ir; }
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
     for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
 
   int cr = u0 / a.nch, cc = u0 - (u0 / a.nch) * a.nch;    // consume cursor (local row, chunk)
-  auto consume = [&](const uint4 (&wb)[NROW], const _Float16 (&sb)[NROW], bool last) {
+  auto consume = [&](const uint4 (&wb)[NROW], const SType (&sb)[NROW], bool last) {
     const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
     if (off < rowb) {
       const int g = (int)(off / 16u);                  // this lane's group in the row
@@ -221,7 +234,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
 #pragma unroll
       for (int j = 0; j < NROW; ++j) {
         w[j] = unpack32(wb[j], one);
-        sc[j] = 16.0f * (float)sb[j];
+        if constexpr (PAIR)      // this lane's group is g; its parity is the lane's
+          sc[j] = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(sb[j] >> (16u * ((uint32_t)lane & 1u))));
+        else
+          sc[j] = 16.0f * (float)sb[j];
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -569,9 +585,9 @@ int check_shape(int M, int K, int N, int epi) {
   return PQ_OK;
 }
 
-template <int NROW, int D, int MT>
+template <int NROW, int D, int MT, bool PAIR>
 hipError_t launch_m(const Q4Args& a, int num_cus, hipStream_t stream) {
-  auto kern = gemv_q4_kernel<NROW, D, MT>;
+  auto kern = gemv_q4_kernel<NROW, D, MT, PAIR>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
@@ -593,18 +609,23 @@ hipError_t launch_m(const Q4Args& a, int num_cus, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int NROW, int D, bool PAIR>
+hipError_t launch_p(const Q4Args& a, int num_cus, hipStream_t s) {
+  switch (a.M) {
+    case 1: return launch_m<NROW, D, 1, PAIR>(a, num_cus, s);
+    case 2: return launch_m<NROW, D, 2, PAIR>(a, num_cus, s);
+    case 3: return launch_m<NROW, D, 3, PAIR>(a, num_cus, s);
+    case 4: return launch_m<NROW, D, 4, PAIR>(a, num_cus, s);
+    case 5: return launch_m<NROW, D, 5, PAIR>(a, num_cus, s);
+    case 6: return launch_m<NROW, D, 6, PAIR>(a, num_cus, s);
+    case 7: return launch_m<NROW, D, 7, PAIR>(a, num_cus, s);
+    default: return launch_m<NROW, D, 8, PAIR>(a, num_cus, s);
+  }
+}
+
 template <int NROW, int D>
 hipError_t launch(const Q4Args& a, int num_cus, hipStream_t s) {
-  switch (a.M) {
-    case 1: return launch_m<NROW, D, 1>(a, num_cus, s);
-    case 2: return launch_m<NROW, D, 2>(a, num_cus, s);
-    case 3: return launch_m<NROW, D, 3>(a, num_cus, s);
-    case 4: return launch_m<NROW, D, 4>(a, num_cus, s);
-    case 5: return launch_m<NROW, D, 5>(a, num_cus, s);
-    case 6: return launch_m<NROW, D, 6>(a, num_cus, s);
-    case 7: return launch_m<NROW, D, 7>(a, num_cus, s);
-    default: return launch_m<NROW, D, 8>(a, num_cus, s);
-  }
+  return (a.K / kGroup) % 2 == 0 ? launch_p<NROW, D, true>(a, num_cus, s) : launch_p<NROW, D, false>(a, num_cus, s);
 }
 
 // ---- MFMA path -----------------------------------------------------------
@@ -715,8 +736,12 @@ int pq_gemv_q4(const uint16_t* x, int M, int K, const uint8_t* w, const uint16_t
     a.M = M; a.K = K; a.N = N;
     a.R = R;
     a.nch = (K / 2 + pq::kChunk - 1) / pq::kChunk;
-    e = epi == PQ_EPI_SILU_MUL ? launch<2, 8>(a, dev.num_cus, (hipStream_t)stream)
-                               : launch<1, 16>(a, dev.num_cus, (hipStream_t)stream);
+    // ring depths (1 KB chunks per row in flight per wave): 3 with two rows
+    // per chunk step, 4 with one; deeper rings were slower on every dense-stack
+    // layer (5120x5120 M=1: 6.8 us at 4, 7.6 at 6, 8.6 at 16; 17408->5120: 13.2,
+    // 13.4, 16.5; SiLU*up 5120->2x17408: 21.8 us at 3, 22.2 at 4, 24.3 at 8)
+    e = epi == PQ_EPI_SILU_MUL ? launch<2, 3>(a, dev.num_cus, (hipStream_t)stream)
+                               : launch<1, 4>(a, dev.num_cus, (hipStream_t)stream);
   }
   if (e != hipSuccess) {
     pqhost::set_last_hip_error((int)e);

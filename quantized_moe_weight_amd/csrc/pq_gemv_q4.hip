@@ -728,8 +728,11 @@ int pq_gemv_q4(const uint16_t* x, int M, int K, const uint8_t* w, const uint16_t
     a.nrb = (R + kRB - 1) / kRB;
     a.nkc = K / kKStep;
     a.U = a.nrb * a.nkc;
-    e = epi == PQ_EPI_SILU_MUL ? launch_mfma<2, 4>(a, grid, (hipStream_t)stream)
-                               : launch_mfma<1, 8>(a, grid, (hipStream_t)stream);
+    // ring depths (256-k steps in flight per wave): 2 with two rows per tile
+    // step, 3 with one; deeper rings were slower (17408->5120 M=4: 24.8 us at
+    // 3, 27.5 at 8; SiLU*up 5120->2x17408 M=8: 38.1 at 2, 39.5 at 4)
+    e = epi == PQ_EPI_SILU_MUL ? launch_mfma<2, 2>(a, grid, (hipStream_t)stream)
+                               : launch_mfma<1, 3>(a, grid, (hipStream_t)stream);
   } else {
     Q4Args a;
     a.x = x; a.w = w; a.wsc = w_scale; a.y = y;

@@ -712,8 +712,12 @@ int pq_gemv_fp8(const uint16_t* x, int M, int K, const uint8_t* w, const float* 
   const int grid = grid_for(a.R, dev.num_cus);
   if (lds_bytes(M, K, (a.R + grid - 1) / grid, epi == PQ_EPI_SILU_MUL ? 2 : 1) > 160 * 1024) return PQ_ERR_SHAPE;
 
-  hipError_t e = epi == PQ_EPI_SILU_MUL ? launch<2, 8>(a, grid, (hipStream_t)stream)
-                                        : launch<1, 16>(a, grid, (hipStream_t)stream);
+  // ring depths (chunk steps in flight per wave): 3 either way; deeper rings
+  // were slower on expert-sized matrices (gate_up 6144->2x2048 M=1: 7.4 us at
+  // 3, 8.6 at 8; down 2048->6144 M=8: 12.4 vs 14.1 at 16) and equal on the
+  // 931 MB LM head
+  hipError_t e = epi == PQ_EPI_SILU_MUL ? launch<2, 3>(a, grid, (hipStream_t)stream)
+                                        : launch<1, 3>(a, grid, (hipStream_t)stream);
   if (e != hipSuccess) {
     pqhost::set_last_hip_error((int)e);
     return PQ_ERR_HIP;

@@ -298,7 +298,7 @@ def run(args):
     peak_meas = measure_read_peak(pq)
     out["measured_read_peak"] = {
         "value": round(peak_meas, 1), "unit": "GB/s",
-        "how": "pq_stream_probe over 4 GiB (128-bit non-temporal loads, one block per CU), median of 10",
+        "how": "pq_stream_probe over 4 GiB (128-bit non-temporal loads, one 512-thread block per CU, 3 loads in flight per lane: the fastest shape of a sweep), median of 10",
         "frac_achieved": round(achieved / peak_meas, 4),
     }
     if M > 1:

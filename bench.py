@@ -273,7 +273,7 @@ def run(args):
             "M": M, "experts": shp.E, "hidden": shp.H, "intermediate": shp.I, "top_k": shp.top_k,
             "mean_experts_streamed": float(np.mean(uni)),
             "bytes_per_step": int(round(bytes_per_launch)),
-            "launches_per_layer": pq.launches_per_call(),
+            "launches_per_layer": pq.launches_per_call("moe_decode_layer_ex"),
             "parallelism": "single GPU",
         },
         "us_per_layer": round(total_ms / K * 1e3, 2),
@@ -545,7 +545,7 @@ def run_prefill(args):
         "config": {"workload": (f"prefill block-scaled FP8 GEMM: {T} tokens through one expert's gate_up "
                                 f"(K={K}, N=2x{N // 2}, SiLU*up), E4M3 weights + fp32 block-128 scales, "
                                 "activation quantised live per token and 128-block (a second launch), bf16 out"),
-                   "tokens": T, "K": K, "N": N, "epilogue": "silu_mul", "launches_per_call": 2},
+                   "tokens": T, "K": K, "N": N, "epilogue": "silu_mul", "launches_per_call": pq.launches_per_call("pq_gemm_fp8")},
         "us_per_call": round(step_s * 1e6, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None,

@@ -225,8 +225,15 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k);
  *   ws  : workspace of ws_bytes >= moe_decode_layer_workspace(...)
  * Constraints: 1 <= M <= 8, 1 <= top_k <= 8, top_k <= E <= 1024,
  * H % 128 == 0, I % 128 == 0, 128 <= H <= 16384, 128 <= I <= 16384.
- * Router logits must be finite.  The kernel needs the whole GPU while it runs
- * (its blocks wait on each other; a bounded wait records PQ_ERR_TIMEOUT).
+ * Router logits must be finite.  The kernel needs the whole GPU while it runs:
+ * its blocks (one per CU) wait on each other, so every block must be resident
+ * at once.  Another kernel running concurrently on the device can keep a block
+ * from starting; the waits are bounded, and a wait that gives up records
+ * PQ_ERR_TIMEOUT in the workspace.  The outputs of a call are therefore
+ * defined only if pq_workspace_check on its workspace returns PQ_OK (callers
+ * that cannot guarantee an idle device check it, or set
+ * PQ_MOE_LAUNCH=cooperative, which makes the runtime guarantee co-residency or
+ * refuse the launch with PQ_ERR_HIP).
  * Two kernels implement the call with bitwise equal results: for M <= 2 one
  * that releases the down projection with a grid-wide barrier, for M >= 3 one
  * without (the environment variable PQ_MOE_PATH=barrier|stream forces one).
@@ -242,6 +249,21 @@ int moe_decode_layer(const uint16_t* x, int M, int H,
                      uint16_t* out,
                      uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Which kernel and LDS layout moe_decode_layer / moe_decode_layer_ex use for
+ * a call of this shape on the current device (the same rule, including the
+ * PQ_MOE_PATH override): *kernel = 0 for the kernel with a grid-wide release
+ * before the down projection, 1 for the one without; *alias = 1 when the
+ * re-quantised h reuses the LDS region of the quantised x (always in kernel 0,
+ * which stages h after its release; in kernel 1 when x, h and the output
+ * partials do not fit side by side, and h is then staged only once every
+ * wave of the block is past gate_up);
+ * *lds_bytes = the dynamic LDS per block.  shared: 1 with a shared expert.
+ * Returns PQ_OK, or the status the call itself would return for this shape
+ * (PQ_ERR_SHAPE, PQ_ERR_UNSUPPORTED without a gfx950 device); PQ_ERR_NULL if
+ * an output pointer is NULL.  Host pointers; launches nothing. */
+int moe_decode_layer_config(int M, int H, int I, int E, int top_k, int shared,
+                            int* kernel, int* alias, size_t* lds_bytes);
 
 /* The same layer with the steps either side of it in the launch ([CMP], on
  * the 3.05bpw quality: the router kept at native precision, shared experts
@@ -293,9 +315,11 @@ const char* pq_strerror(int status);
 /* HIP error code of the last PQ_ERR_HIP returned on the calling thread. */
 int pq_last_hip_error(void);
 
-/* Kernel launches one call makes for these arguments (1 for every entry
- * point in this library; reported by the bench as launches per layer). */
-int pq_launches_per_call(void);
+/* Kernel launches one call of the named entry point makes ("pq_gemm_fp8": 2,
+ * the activation quantisation and the GEMM; every other compute entry point:
+ * 1, including the whole MoE layer).  PQ_ERR_NULL for NULL,
+ * PQ_ERR_UNSUPPORTED for a name that is not a compute entry point. */
+int pq_launches_per_call(const char* entry_point);
 
 /* Measurement helper: stream `bytes` of device memory at `src` through the
  * load path of the weight streams (128-bit non-temporal loads, one persistent

@@ -15,7 +15,8 @@ import torch
 from . import _lib
 
 __all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemm_fp8_prequant", "gemv_q4", "moe_decode_layer",
-           "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call", "stream_probe",
+           "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call", "moe_layer_config",
+           "stream_probe",
            "EPI_NONE", "EPI_SILU_MUL", "lib"]
 
 EPI_NONE = 0
@@ -87,8 +88,22 @@ def workspace_check() -> int:
     return lib().pq_workspace_check(_p(ws), _stream())
 
 
-def launches_per_call() -> int:
-    return lib().pq_launches_per_call()
+def launches_per_call(entry_point: str = "moe_decode_layer") -> int:
+    """Kernel launches one call of the named C entry point makes."""
+    n = lib().pq_launches_per_call(entry_point.encode())
+    if n < 0:
+        raise PqError("pq_launches_per_call", n)
+    return n
+
+
+def moe_layer_config(M: int, H: int, I: int, E: int, top_k: int, shared: bool = False) -> dict:
+    """Which layer kernel and LDS layout a moe_decode_layer call of this shape
+    uses on the current device: {"kernel": "barrier"|"stream", "alias": bool,
+    "lds_bytes": int}."""
+    k, al, lds = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_size_t(0)
+    _check(lib().moe_decode_layer_config(M, H, I, E, top_k, int(bool(shared)), ctypes.byref(k), ctypes.byref(al),
+                                         ctypes.byref(lds)), "moe_decode_layer_config")
+    return {"kernel": ("barrier", "stream")[k.value], "alias": bool(al.value), "lds_bytes": int(lds.value)}
 
 
 def stream_probe(src, sink) -> None:

@@ -37,7 +37,8 @@ SIGNATURES = {
     "pq_workspace_check": (_c_int, [_vp, _vp]),
     "pq_strerror": (ctypes.c_char_p, [_c_int]),
     "pq_last_hip_error": (_c_int, []),
-    "pq_launches_per_call": (_c_int, []),
+    "pq_launches_per_call": (_c_int, [ctypes.c_char_p]),
+    "moe_decode_layer_config": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "pq_stream_probe": (_c_int, [_vp, _c_size, _vp, _vp]),
 }
 

@@ -11,6 +11,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/pq.h"
 
 namespace pq {
@@ -269,7 +271,7 @@ struct WsHeader {
   uint32_t error;       // first pq_status recorded by a kernel (0 = none)
   uint32_t done;        // phase counter of the running call
   uint32_t exit_count;  // blocks that finished the running call
-  uint32_t epoch;       // calls completed on this workspace (wraps)
+  uint32_t reserved;    // unused (zero)
   uint32_t pad[60];     // keep the header one 256-byte line
 };
 static_assert(sizeof(WsHeader) == 256, "workspace header is one 256-byte line");
@@ -322,6 +324,25 @@ int current_device_info(DeviceInfo* out);
 void set_last_hip_error(int e);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The dynamic-LDS limit of one kernel, raised once per device.  Host threads
+// that make their first call at the same time all wait for the one setter
+// (std::call_once), and every later call returns the recorded status.
+constexpr int kMaxDevices = 64;
+struct KernelAttrOnce {
+  std::once_flag once[kMaxDevices];
+  hipError_t status[kMaxDevices] = {};
+};
+inline hipError_t set_dynamic_lds_once(KernelAttrOnce& o, const void* kern, int bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(o.once[dev], [&] {
+    o.status[dev] = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  });
+  return o.status[dev];
+}
 
 __host__ __device__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

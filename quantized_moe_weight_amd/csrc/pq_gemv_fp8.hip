@@ -599,11 +599,10 @@ void mfma_plan(int nrow, int num_cus, int* grid, size_t* ws) {
 template <int NROW, int D, int MT>
 hipError_t launch_mfma_m(const MArgs& a, int grid, hipStream_t stream) {
   auto kern = gemv_fp8_mfma_kernel<NROW, D, MT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static pqhost::KernelAttrOnce attr;
+  {
+    hipError_t e = pqhost::set_dynamic_lds_once(attr, (const void*)kern, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), m_lds_bytes(MT, a.K, NROW), stream, a);
   return hipGetLastError();
@@ -627,11 +626,10 @@ hipError_t launch_mfma(const MArgs& a, int grid, hipStream_t s) {
 template <int NROW, int D, int MT>
 hipError_t launch_m(const GemvArgs& a, int grid, hipStream_t stream) {
   auto kern = gemv_fp8_kernel<NROW, D, MT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  static pqhost::KernelAttrOnce attr;
+  {
+    hipError_t e = pqhost::set_dynamic_lds_once(attr, (const void*)kern, 160 * 1024);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int rows = (a.R + grid - 1) / grid;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes(a.M, a.K, rows, NROW), stream, a);

@@ -588,11 +588,10 @@ int check_shape(int M, int K, int N, int epi) {
 template <int NROW, int D, int MT, bool PAIR>
 hipError_t launch_m(const Q4Args& a, int num_cus, hipStream_t stream) {
   auto kern = gemv_q4_kernel<NROW, D, MT, PAIR>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  static pqhost::KernelAttrOnce attr;
+  {
+    hipError_t e = pqhost::set_dynamic_lds_once(attr, (const void*)kern, (int)kMaxLds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   // Blocks: PQ_BLOCKS_PER_CU per CU (default 1), at most one per row and at
   // least enough for kRowsCap rows per block.  The grid depends on R and the
@@ -661,11 +660,10 @@ void mfma_plan(int M, int R, int nrow, int num_cus, int* grid, size_t* ws) {
 template <int NROW, int D, int MT>
 hipError_t launch_mfma_m(const Q4MArgs& a, int grid, hipStream_t stream) {
   auto kern = gemv_q4_mfma_kernel<NROW, D, MT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  static pqhost::KernelAttrOnce attr;
+  {
+    hipError_t e = pqhost::set_dynamic_lds_once(attr, (const void*)kern, (int)kMaxLds);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const size_t lds = ((size_t)a.M * a.K / 8 + 2) * 16;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);

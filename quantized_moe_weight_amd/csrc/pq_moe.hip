@@ -59,8 +59,15 @@ constexpr int kMaxE = 1024;
 constexpr int DG = 3, DD = 6;        // stream kernel
 constexpr int BDG = 3, BDD = 6;      // barrier kernel
 constexpr uint32_t kSpinLimit = 1u << 20;
+// Polls of an LDS word before a wait inside a block gives up.  Every such word
+// is set by waves of the same block that themselves only wait on bounded
+// conditions, so in a correct run these waits end in microseconds; the bound
+// turns a defect (a producer wave that never arrives) into PQ_ERR_TIMEOUT
+// instead of a hung GPU.
+constexpr uint32_t kLdsSpinLimit = 1u << 21;
 constexpr int kAuxSC1 = 0x10;            // buffer aux bit: agent-coherent (sc1) access
 constexpr int kFlagStride = 32;          // uint32 per release flag: one 128-byte line each
+constexpr uint32_t kReleased = 1u;       // a release flag's value once the down phase may start
 
 struct MoeArgs {
   const uint16_t* x;
@@ -117,6 +124,30 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int wave_claim(uint32_t* p) {
   const uint32_t r = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   return __builtin_amdgcn_readfirstlane((int)(r >> 6));
+}
+
+// Wave-wide bounded wait on an LDS word that other waves of the block set:
+// returns once done(value) holds, or after kLdsSpinLimit polls with
+// PQ_ERR_TIMEOUT recorded.  After a timeout the wave goes on with whatever the
+// block's tables hold; the route tables only ever hold in-range entries (see
+// layer_prologue), so the results are wrong but every access stays in bounds.
+template <class Done>
+__device__ __forceinline__ void lds_wait(const uint32_t* p, Done done, pq::WsHeader* hdr) {
+  for (uint32_t it = 0;; ++it) {
+    const uint32_t v = (uint32_t)ufl((int)__hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (done(v)) return;
+    if (it >= kLdsSpinLimit) {
+      if (pq::lane_id() == 0) pq::record_error(hdr, PQ_ERR_TIMEOUT);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Number of union entries of the call, read after the routes are released
+// (acquire: the union tables written before it are visible).
+__device__ __forceinline__ int routes_nU(const Route& r) {
+  return ufl(__hip_atomic_load(&r.nU, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
 }
 
 // true when either 16-bit half of w is zero
@@ -240,7 +271,9 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
   const int lane = pq::lane_id();
   const int P = a.M * a.top_k;
   const bool act = lane < P;
-  const int id = act ? r.ids[lane] : 0;
+  // ids are in range whenever the routes are complete; the clamp keeps the
+  // bitmaps in bounds should a bounded wait have ended early
+  const int id = act ? min(max(r.ids[lane], 0), a.E - 1) : 0;
   const int m = act ? lane / a.top_k : 0;
   const int w = id >> 5;
   const uint32_t bit = 1u << (id & 31);
@@ -290,8 +323,8 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
     if (dup && blockIdx.x == 0) pq::record_error(hdr, PQ_ERR_BAD_EXPERT);
   }
   if (lane == 0) {
-    r.nU = total + sh;
     r.nitems = nitems + sh * a.M;
+    __hip_atomic_store(&r.nU, total + sh, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -361,8 +394,8 @@ __device__ void single_token_union(const MoeArgs& a, Route& r, int sh) {
     r.items[sh + lane] = us;
   }
   if (lane == 0) {
-    r.nU = a.top_k + sh;
     r.nitems = a.top_k + sh;
+    __hip_atomic_store(&r.nU, a.top_k + sh, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -503,6 +536,10 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
   if (threadIdx.x == 0) {
     *s_ready = router ? 0u : 1u;
     *s_rdone = 0u;
+    // until the union is built, only the shared entry (set up below) is known;
+    // a wave whose wait for the routes timed out sees exactly that
+    route.nitems = sh * a.M;
+    route.nU = sh;
   }
   if (sh && wv == 0) shared_entry(a, route);
 
@@ -566,8 +603,8 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
       } else {
         if (lane == 0) __hip_atomic_fetch_add(s_rdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (wv == 0) {
-          while (ufl((int)__hip_atomic_load(s_rdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < a.M)
-            __builtin_amdgcn_s_sleep(1);
+          const uint32_t nm = (uint32_t)a.M;
+          lds_wait(s_rdone, [nm](uint32_t v) { return v >= nm; }, hdr);
           build_union(a, route, hdr, s_tmask, sh);
           if (lane == 0) __hip_atomic_store(s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
@@ -579,10 +616,9 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
   }
 }
 
-// Wait (wave-wide) until the routes of the call are visible.
-__device__ __forceinline__ void wait_routes(const uint32_t* s_ready) {
-  while (ufl((int)__hip_atomic_load(s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == 0)
-    __builtin_amdgcn_s_sleep(1);
+// Wait (wave-wide, bounded) until the routes of the call are visible.
+__device__ __forceinline__ void wait_routes(const uint32_t* s_ready, pq::WsHeader* hdr) {
+  lds_wait(s_ready, [](uint32_t v) { return v != 0u; }, hdr);
 }
 
 // The barrier kernel: all gate_up units of the call, then one grid-wide
@@ -599,7 +635,6 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   __shared__ uint32_t s_tmask[kMaxM][kMaxE / 32];   // routed-expert bitmap of each token
   __shared__ uint32_t s_next;     // next gate_up unit of this block
   __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
-  __shared__ uint32_t s_epoch;    // value the release flags take in this call
   __shared__ uint32_t s_ready;    // routes visible (set by the routing waves)
   __shared__ uint32_t s_rdone;    // routing waves done
 
@@ -627,7 +662,6 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   if (threadIdx.x == 0) {       // block counters; first used after the barriers below
     s_next = 0u;
     s_arrive = 0u;
-    s_epoch = pq::ld_agent_u32(&hdr->epoch) + 1u;   // this call's flag value
   }
   layer_prologue<TP, EXT>(a, route, s_tmask, &s_ready, &s_rdone, act, acts, hdr);
 
@@ -642,12 +676,13 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   // unit and chunk.
   const int sh0 = pq::split_start(sh * I, (int)gridDim.x, (int)blockIdx.x);
   const int nsh = pq::split_start(sh * I, (int)gridDim.x, (int)blockIdx.x + 1) - sh0;
-  int bu0 = 0, bu1 = 0;
+  int bu0 = 0, bu1 = 0, nU = sh;
   bool routes_known = false;
   auto know_routes = [&]() {
     if (!routes_known) {
-      if (router) wait_routes(&s_ready);
-      const int nur = ufl(route.nU) - sh;
+      if (router) wait_routes(&s_ready, hdr);
+      nU = routes_nU(route);
+      const int nur = nU - sh;
       bu0 = pq::split_start(nur * I, (int)gridDim.x, (int)blockIdx.x);
       bu1 = pq::split_start(nur * I, (int)gridDim.x, (int)blockIdx.x + 1);
       routes_known = true;
@@ -766,11 +801,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   // the phase counter (one device atomic per block: they serialise on one
   // address).
   // The block that completes the count releases every block through its own
-  // flag line (value = this call's epoch, so a flag left by an earlier call
-  // never matches).
+  // flag line (set to kReleased; the last block to exit clears every line, so
+  // the flags are zero between calls like the other counters of the region).
   pq::wait_vm();
   know_routes();                      // (every wave's last claim already waited)
-  const int nU = ufl(route.nU);
   const int gu_units = nU * I;
   uint32_t last = 0;
   if (lane == 0) {
@@ -780,8 +814,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       last = pq::atomic_add_relaxed(&hdr->done, rows) + rows == (uint32_t)gu_units;
   }
   if (__builtin_amdgcn_readlane((int)last, 0)) {
-    const uint32_t ep = s_epoch;
-    for (int b = lane; b < (int)gridDim.x; b += pq::kWave) pq::st_agent_u32(flags + (size_t)b * kFlagStride, ep);
+    for (int b = lane; b < (int)gridDim.x; b += pq::kWave) pq::st_agent_u32(flags + (size_t)b * kFlagStride, kReleased);
   }
 
   // ---- D. down projection + weighted combine --------------------------------
@@ -831,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   // wait for every h row of the call, then quantise h into LDS: every block
   // derives the same codes and scales from the same values (block 0 also
   // writes them out when asked)
-  if (threadIdx.x == 0) pq::spin_wait_eq(flags + (size_t)blockIdx.x * kFlagStride, s_epoch, hdr, a.spin_limit);
+  if (threadIdx.x == 0) pq::spin_wait_eq(flags + (size_t)blockIdx.x * kFlagStride, kReleased, hdr, a.spin_limit);
   __syncthreads();
   {
     // 8 values per lane, 16 lanes per 128-value block (the layout of the
@@ -936,7 +969,11 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     a.out[(size_t)m * H + r0 + rl] = pq::bf16_rne(o);
   }
 
-  // ---- E. the last block resets the counters of this call -------------------
+  // ---- E. the last block resets the counters and flags of this call ---------
+  // Every block has passed its flag wait when it counts itself out, and the
+  // releasing block's flag stores are complete (wait_vm) before it does, so
+  // the clearing stores below are the last writes to the flag lines.
+  pq::wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t old = pq::atomic_add_relaxed(&hdr->exit_count, 1u);
@@ -946,10 +983,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   if (s_last) {
     if (router)
       for (int t = threadIdx.x; t < a.M * a.E; t += kThreads) pq::st_agent_u32(a.lx + t, 0u);
+    for (int b = threadIdx.x; b < (int)gridDim.x; b += kThreads) pq::st_agent_u32(flags + (size_t)b * kFlagStride, 0u);
     if (threadIdx.x == 0) {
       pq::atomic_store_relaxed(&hdr->done, 0u);
       pq::atomic_store_relaxed(&hdr->exit_count, 0u);
-      pq::atomic_store_relaxed(&hdr->epoch, s_epoch);
     }
   }
 }
@@ -1016,11 +1053,13 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   // need no routes; a wave that reaches the routed units waits for them.
   const int G = (int)gridDim.x;
   int gu_total = sh * I;               // the whole list once the routes are known
+  int nU = sh;
   bool routes_known = false;
   auto know_routes = [&]() {
     if (!routes_known) {
-      if (router) wait_routes(&s_ready);
-      gu_total = ufl(route.nU) * I;
+      if (router) wait_routes(&s_ready, hdr);
+      nU = routes_nU(route);
+      gu_total = nU * I;
       routes_known = true;
     }
   };
@@ -1133,23 +1172,23 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   }
   if (lane == 0) atomicSub(&s_gu_busy, 1u);   // this wave no longer reads x
   know_routes();                               // (its last claim already waited)
-  const int nU = ufl(route.nU);
   const int dn_total = nU * nrows;
 
   // h staging: the (entry, pair) items of the block are quantised into LDS in
   // union order, each by the wave that claims it; a wave out of gate_up units
   // claims items until none is left, then goes on with down units.
   {
-    const int nitems = ufl(route.nitems);
+    // (a routed union always has more entries than the shared one: nU == sh
+    // only if the wait for the routes ended early, and then only the shared
+    // entry's items are known)
+    const int nitems = nU > sh ? ufl(route.nitems) : sh * a.M;
     for (;;) {
       const int jj = wave_claim(&s_iclaim);
       if (jj >= nitems) break;
       const int it = ufl(route.items[jj]);
       const int v = it & 255, t = it >> 8;
-      if (a.alias) {             // h codes overwrite x codes: the block must be past gate_up
-        while (ufl((int)__hip_atomic_load(&s_gu_busy, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0)
-          __builtin_amdgcn_s_sleep(1);
-      }
+      if (a.alias)               // h codes overwrite x codes: the block must be past gate_up
+        lds_wait(&s_gu_busy, [](uint32_t v) { return v == 0u; }, hdr);
       stage_pair(a, route, hdr, v, t, ha, hsc);
       if (lane == 0) __hip_atomic_fetch_add(&s_staged[v], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -1227,11 +1266,10 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
       }
     };
     // wait until the h of union entry uu is in LDS (its stagers poll with a
-    // bounded wait, so this ends)
+    // bounded wait, and this wait is bounded too)
     auto wait_staged = [&](int uu) {
       const uint32_t n = (uint32_t)ufl(route.unp[uu]);
-      while ((uint32_t)ufl((int)__hip_atomic_load(&s_staged[uu], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) < n)
-        __builtin_amdgcn_s_sleep(1);
+      lds_wait(&s_staged[uu], [n](uint32_t v) { return v >= n; }, hdr);
     };
 
 #pragma unroll
@@ -1366,15 +1404,22 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePl
   return PQ_OK;
 }
 
+// PQ_MOE_LAUNCH=cooperative launches the layer kernels with
+// hipLaunchCooperativeKernel, which makes the runtime guarantee that every
+// block of the grid is resident at once (or refuse the launch); the default
+// plain launch relies on the grid being one block per CU of an otherwise idle
+// device, and a block that is kept waiting anyway ends its bounded waits with
+// PQ_ERR_TIMEOUT.
+bool cooperative_launch() {
+  const char* e = getenv("PQ_MOE_LAUNCH");
+  return e && strcmp(e, "cooperative") == 0;
+}
+
 template <int TP, bool STREAM, bool EXT>
 int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& dev, hipStream_t stream) {
   auto kern = STREAM ? moe_stream_kernel<TP, EXT> : moe_barrier_kernel<TP, EXT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    PQ_HIP_CHECK(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)(kLdsBytes - kStaticLds)));
-    attr_set = true;
-  }
+  static pqhost::KernelAttrOnce attr;
+  PQ_HIP_CHECK(pqhost::set_dynamic_lds_once(attr, (const void*)kern, (int)(kLdsBytes - kStaticLds)));
   int per_cu = 0;
   PQ_HIP_CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kern, kThreads, pl.lds));
   if (per_cu < 1) return PQ_ERR_SHAPE;
@@ -1382,6 +1427,13 @@ int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& de
   // per CU also keeps the per-block staging of h to one copy per CU)
   const int grid = dev.num_cus;
   if (!STREAM && (size_t)grid * kFlagStride * 4 > pq::kWsZeroOff - pq::kWsCounterOff) return PQ_ERR_UNSUPPORTED;
+  if (cooperative_launch()) {
+    MoeArgs arg = a;
+    void* params[] = {&arg};
+    PQ_HIP_CHECK(hipLaunchCooperativeKernel((const void*)kern, dim3(grid), dim3(kThreads), params,
+                                            (unsigned)pl.lds, stream));
+    return PQ_OK;
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), pl.lds, stream, a);
   PQ_HIP_CHECK(hipGetLastError());
   return PQ_OK;
@@ -1404,6 +1456,24 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k) {
   MoePlan pl;
   if (moe_plan(M, H, I, E, top_k, 0, kPathStream, &pl) != PQ_OK) return 0;
   return pl.ws_total;
+}
+
+int moe_decode_layer_config(int M, int H, int I, int E, int top_k, int shared, int* kernel, int* alias,
+                            size_t* lds_bytes) {
+  if (!kernel || !alias || !lds_bytes) return PQ_ERR_NULL;
+  MoePlan pl;
+  const int path = moe_path(M);
+  int st = moe_plan(M, H, I, E, top_k, 0, path, &pl, shared ? 1 : 0);
+  if (st != PQ_OK) return st;
+  pqhost::DeviceInfo dev;
+  st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+  st = moe_plan(M, H, I, E, top_k, dev.num_cus, path, &pl, shared ? 1 : 0);
+  if (st != PQ_OK) return st;
+  *kernel = path;
+  *alias = pl.alias;
+  *lds_bytes = pl.lds;
+  return PQ_OK;
 }
 
 int moe_decode_layer_ex(const uint16_t* x, int M, int H, const uint16_t* router_w, float* router_logits,

@@ -60,7 +60,18 @@ const char* pq_strerror(int status) {
 
 int pq_last_hip_error(void) { return pqhost::g_last_hip_error; }
 
-int pq_launches_per_call(void) { return 1; }
+int pq_launches_per_call(const char* entry_point) {
+  if (entry_point == nullptr) return PQ_ERR_NULL;
+  // pq_gemm_fp8 quantises the activation in a launch of its own before the
+  // GEMM; every other compute entry point is one launch
+  static const char* const kOne[] = {"pq_quantize_fp8", "pq_quantize_q4", "pq_gemv_fp8", "pq_gemm_fp8_prequant",
+                                     "pq_gemv_q4", "moe_decode_layer", "moe_decode_layer_ex",
+                                     "pq_stream_probe"};
+  if (strcmp(entry_point, "pq_gemm_fp8") == 0) return 2;
+  for (const char* n : kOne)
+    if (strcmp(entry_point, n) == 0) return 1;
+  return PQ_ERR_UNSUPPORTED;
+}
 
 int pq_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (ws == nullptr) return ws_bytes == 0 ? PQ_OK : PQ_ERR_NULL;

@@ -34,7 +34,29 @@ def test_every_header_function_is_exported(lib):
 def test_strerror_covers_every_status(lib):
     for st in range(-8, 1):
         assert b"unknown" not in lib.pq_strerror(st)
-    assert lib.pq_launches_per_call() == 1
+
+
+def test_launches_per_call_per_entry_point(lib):
+    """Every compute entry point is one launch, except pq_gemm_fp8 (the
+    activation quantisation, then the GEMM)."""
+    f = lib.pq_launches_per_call
+    assert f(b"pq_gemm_fp8") == 2
+    for name in (b"pq_gemv_fp8", b"pq_gemv_q4", b"moe_decode_layer", b"moe_decode_layer_ex",
+                 b"pq_gemm_fp8_prequant", b"pq_quantize_fp8", b"pq_quantize_q4", b"pq_stream_probe"):
+        assert f(name) == 1, name
+    assert f(b"pq_strerror") == PQ_ERR_UNSUPPORTED
+    assert f(None) == PQ_ERR_NULL
+
+
+def test_moe_layer_config_host_validation(lib):
+    k, al, lds = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_size_t(0)
+    g = lib.moe_decode_layer_config
+    assert g(1, 6144, 2048, 256, 8, 0, NUL, ctypes.byref(al), ctypes.byref(lds)) == PQ_ERR_NULL
+    assert g(0, 6144, 2048, 256, 8, 0, ctypes.byref(k), ctypes.byref(al), ctypes.byref(lds)) == PQ_ERR_SHAPE
+    assert g(1, 6000, 2048, 256, 8, 0, ctypes.byref(k), ctypes.byref(al), ctypes.byref(lds)) == PQ_ERR_SHAPE
+    # valid shapes stop at the device query on a machine without a gfx950 device
+    st = g(8, 6144, 2048, 256, 8, 0, ctypes.byref(k), ctypes.byref(al), ctypes.byref(lds))
+    assert st in (PQ_OK, PQ_ERR_UNSUPPORTED, -6)
 
 
 def test_gemv_fp8_host_validation(lib):

@@ -68,3 +68,16 @@ def test_quantize_q4_bit_exact(pq, N, K):
     po, so = oracle.q4_quant(w)
     assert np.array_equal(p.cpu().numpy(), po)
     assert np.array_equal(s.cpu().numpy().view(np.uint16), so.view(np.uint16))
+
+
+def test_quantize_q4_hand_derived_scale_goldens(pq):
+    """The library's int4 quantiser on the hand-derived fp16 tie cases (normal,
+    subnormal, overflow): every scale equals the fixture's value."""
+    import torch
+    from test_oracle_quant import q4_golden_rows
+    w, exp = q4_golden_rows()
+    p, s = pq.quantize_q4(torch.from_numpy(w).cuda())
+    got = s.cpu().numpy().view(np.uint16)[:, 0]
+    assert np.array_equal(got, exp), [f"0x{g:04x}/0x{e:04x}" for g, e in zip(got, exp)]
+    po, _ = oracle.q4_quant(w)
+    assert np.array_equal(p.cpu().numpy(), po)

@@ -3,6 +3,7 @@ encode, int4 g32).  Expected values come from the mathematics: the amax element
 maps to +-448, each code is the nearest representable value (checked by
 exhaustive search over the torch-decoded table), the reconstruction error is at
 most half a code step, and the scale is the fp32 quotient amax / 448."""
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -133,3 +134,88 @@ def test_q4_zero_group():
     q = oracle.q4_unpack(p)
     assert s16[0, 0] == 0 and np.all(q[0, :32] == 0)
     assert q[0, 40] == -7
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "q4_scale_rounding.txt")
+
+
+def q4_scale_goldens():
+    """(name, amax fp32, expected fp16 bits) from the hand-derived fixture."""
+    out = []
+    for line in open(GOLDEN, encoding="utf-8"):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, a_hex, s_hex = line.split()[:3]
+        amax = np.array([int(a_hex, 16)], np.uint32).view(np.float32)[0]
+        out.append((name, amax, int(s_hex, 16)))
+    return out
+
+
+def q4_golden_rows():
+    """One 32-value group per golden case: amax at position 5 (negated for odd
+    cases), smaller values elsewhere.  Returns (w fp32 [n, 32], expected scale
+    bits [n])."""
+    cases = q4_scale_goldens()
+    w = np.zeros((len(cases), 32), np.float32)
+    exp = np.zeros(len(cases), np.uint16)
+    for i, (_, amax, sbits) in enumerate(cases):
+        row = (np.linspace(-0.9, 0.9, 32) * amax).astype(np.float32)
+        row[5] = -amax if i % 2 else amax
+        w[i] = row
+        exp[i] = sbits
+    return w, exp
+
+
+def test_q4_scale_hand_derived_goldens():
+    """The int4 scale rule against hand-derived values at fp16 rounding ties
+    (normal, subnormal, overflow): ties to even, no truncation, no rounding
+    half away from zero, divisor 7."""
+    w, exp = q4_golden_rows()
+    p, s16 = oracle.q4_quant(w)
+    got = s16[:, 0].view(np.uint16)
+    names = [c[0] for c in q4_scale_goldens()]
+    for n, g, e in zip(names, got, exp):
+        assert g == e, f"case {n}: scale 0x{g:04x}, expected 0x{e:04x}"
+    q = oracle.q4_unpack(p)
+    for i, e in enumerate(exp):
+        if e == 0x7C00:                      # infinite scale: every code 0
+            assert np.all(q[i] == 0)
+        else:
+            # the amax element's code: amax / s rounded to the nearest integer
+            # (these quotients are far from .5), clipped; a coarse subnormal
+            # scale can put it below 7 (case E: 49/8 -> 6) or above (F: 35/4 -> 7)
+            # (the range is asymmetric: -8.75 clips to -8, +8.75 to +7)
+            sv = Fraction(float(np.uint16(e).view(np.float16)))
+            r = Fraction(float(w[i, 5])) / sv
+            assert q[i, 5] == min(max(round(r), -8), 7)
+
+
+def _fp16_nearest_even(fr):
+    """The fp16 nearest to the exact positive rational fr (ties to the even
+    mantissa; >= 65520 -> inf), by exact comparison of fr with the fp16
+    neighbours of a first guess."""
+    if fr >= 65520:
+        return 0x7C00
+    guess = np.float16(float(fr)).view(np.uint16)
+    cands = [int(b) for b in (guess - 1, guess, guess + 1) if 0 <= b < 0x7C00]
+    vals = [Fraction(float(np.uint16(b).view(np.float16))) for b in cands]
+    d = [abs(v - fr) for v in vals]
+    best = [b for b, dd in zip(cands, d) if dd == min(d)]
+    return best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+
+
+def test_q4_scale_is_nearest_fp16_to_exact_quotient():
+    """For amax spread over fp16's normal and subnormal range, the scale is the
+    fp16 nearest to the exact rational amax / 7 (ties to even).  (Rounding the
+    fp32 quotient cannot create a tie that the exact quotient does not have:
+    neighbouring fp32 quotients of amax / 7 lie at least 4/7 of an fp32 ulp
+    apart, so the one fp32 value within half an ulp of an fp16 midpoint is
+    the midpoint itself.)"""
+    rng = np.random.default_rng(7)
+    amax = np.exp2(rng.uniform(-26, 18, size=400)).astype(np.float32)
+    w = np.zeros((len(amax), 32), np.float32)
+    w[:, 0] = amax
+    w[:, 1:] = (rng.uniform(-1, 1, size=(len(amax), 31)) * amax[:, None]).astype(np.float32)
+    _, s16 = oracle.q4_quant(w)
+    for a, s in zip(amax, s16[:, 0].view(np.uint16)):
+        assert s == _fp16_nearest_even(Fraction(float(a)) / 7), f"amax {a!r}: scale 0x{s:04x}"

@@ -57,7 +57,8 @@ typedef enum {
   PQ_ERR_UNSUPPORTED = -5, /* the current device is not gfx950, or no device     */
   PQ_ERR_HIP = -6,         /* a HIP runtime call failed (see pq_last_hip_error)  */
   PQ_ERR_TIMEOUT = -7,     /* a kernel's bounded spin-wait gave up (workspace)   */
-  PQ_ERR_BAD_EXPERT = -8   /* a top-k expert id in device memory was out of range */
+  PQ_ERR_BAD_EXPERT = -8,  /* a top-k expert id in device memory was out of range */
+  PQ_ERR_SCRATCH = -9      /* the call needs more than the static scratch holds  */
 } pq_status;
 
 typedef enum {
@@ -298,6 +299,40 @@ int moe_decode_layer_ex(const uint16_t* x, int M, int H,
                         uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free form of moe_decode_layer_ex, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and constraints as
+ * moe_decode_layer_ex, except:
+ *   - there is no workspace argument: the layer's workspace is a static
+ *     device array inside the library (4 MiB, one copy per GPU the library
+ *     runs on, held until the process ends; the first call on a device looks
+ *     it up and zeroes it with one extra kernel launch on `stream`).  A call
+ *     whose layer needs more (moe_decode_layer_workspace() > 4 MiB, e.g.
+ *     M = 8, top_k = 8 at I >= 14208) returns PQ_ERR_SCRATCH and launches
+ *     nothing.  The call allocates nothing (no hipMalloc, no allocating
+ *     library routine).
+ *   - every call on one GPU shares that GPU's array: calls that can overlap
+ *     in time on one GPU (other streams, other threads) race and must not be
+ *     issued; calls ordered on one stream are safe (each leaves the array's
+ *     counters and exchange regions at zero, as the workspace form does).
+ *   - status: nullable device int32.  When given, the kernel writes the call's
+ *     device-side status there as it ends (PQ_OK, PQ_ERR_TIMEOUT or
+ *     PQ_ERR_BAD_EXPERT) and clears the record; a status recorded by a call
+ *     given NULL stays until a later call with a status pointer reports it.
+ *     16-byte aligned.
+ * Host-side validation errors are returned as by moe_decode_layer_ex. */
+int moe_decode_layer_noalloc(const uint16_t* x, int M, int H,
+                             const uint16_t* router_w, float* router_logits,
+                             int32_t* topk_ids, float* topk_w,
+                             int E, int top_k, int I,
+                             const uint8_t* w13, const float* s13,
+                             const uint8_t* w2, const float* s2,
+                             const uint8_t* sh_w13, const float* sh_s13,
+                             const uint8_t* sh_w2, const float* sh_s2,
+                             uint16_t* out,
+                             uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg,
+                             int32_t* status, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Workspace and error helpers.                                               */
 /* ------------------------------------------------------------------------- */
@@ -317,7 +352,8 @@ int pq_last_hip_error(void);
 
 /* Kernel launches one call of the named entry point makes ("pq_gemm_fp8": 2,
  * the activation quantisation and the GEMM; every other compute entry point:
- * 1, including the whole MoE layer).  PQ_ERR_NULL for NULL,
+ * 1, including the whole MoE layer; moe_decode_layer_noalloc adds one
+ * zeroing launch on the first call on each device).  PQ_ERR_NULL for NULL,
  * PQ_ERR_UNSUPPORTED for a name that is not a compute entry point. */
 int pq_launches_per_call(const char* entry_point);
 

@@ -15,7 +15,8 @@ import torch
 from . import _lib
 
 __all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemm_fp8_prequant", "gemv_q4", "moe_decode_layer",
-           "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check", "launches_per_call", "moe_layer_config",
+           "moe_decode_layer_noalloc", "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check",
+           "launches_per_call", "moe_layer_config",
            "stream_probe",
            "EPI_NONE", "EPI_SILU_MUL", "lib"]
 
@@ -285,6 +286,36 @@ def moe_decode_layer(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=
         if shared is not None:
             res.update(sh_h=h[P:], sh_hq=hq[P:], sh_hs=hs[P:])
     return res
+
+
+def moe_decode_layer_noalloc(x, w13, s13, w2, s2, *, logits=None, topk_ids=None, topk_w=None, top_k: int = 8,
+                             router_w=None, shared=None, out=None, status=None):
+    """moe_decode_layer through the allocation-free entry point: the layer's
+    workspace is the library's static per-GPU scratch, so the call itself
+    allocates nothing on the device when ``out``, the routing buffers and
+    ``status`` (int32 [4], receives the call's device-side status in element 0)
+    are passed in.  Calls that overlap in time on one GPU race."""
+    _need(x, torch.bfloat16, 2, "x")
+    M, H = x.shape
+    E, two_i, _ = w13.shape
+    I = two_i // 2
+    dev = x.device
+    if router_w is not None or logits is not None:
+        if topk_ids is None:
+            topk_ids = torch.empty((M, top_k), dtype=torch.int32, device=dev)
+            topk_w = torch.empty((M, top_k), dtype=torch.float32, device=dev)
+    else:
+        top_k = topk_ids.shape[1]
+    lg = logits
+    if router_w is not None and lg is None:
+        lg = torch.empty((M, E), dtype=torch.float32, device=dev)
+    sh = tuple(shared) if shared is not None else (None,) * 4
+    y = out if out is not None else torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    st = status if status is not None else torch.zeros(4, dtype=torch.int32, device=dev)
+    _check(lib().moe_decode_layer_noalloc(_p(x), M, H, _p(router_w), _p(lg), _p(topk_ids), _p(topk_w), E, top_k, I,
+                                          _p(w13), _p(s13), _p(w2), _p(s2), _p(sh[0]), _p(sh[1]), _p(sh[2]), _p(sh[3]),
+                                          _p(y), None, None, None, _p(st), _stream()), "moe_decode_layer_noalloc")
+    return {"out": y, "topk_ids": topk_ids, "topk_w": topk_w, "status": st, "logits": lg}
 
 
 class MoeLayerCall:

@@ -33,6 +33,9 @@ SIGNATURES = {
     "moe_decode_layer_ex": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _c_size, _vp]),
+    "moe_decode_layer_noalloc": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp]),
     "pq_workspace_init": (_c_int, [_vp, _c_size, _vp]),
     "pq_workspace_check": (_c_int, [_vp, _vp]),
     "pq_strerror": (ctypes.c_char_p, [_c_int]),

@@ -40,6 +40,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "pq_quant_dev.h"
 
 namespace {
@@ -90,6 +92,7 @@ struct MoeArgs {
   uint8_t* hq_dbg;
   float* hs_dbg;
   uint8_t* ws;
+  int32_t* status_out;   // nullable: the call's device-side status, written by the last block
   uint16_t* hbuf;   // [P2][I] bf16 (stream kernel: bits inverted, zero between calls)
   int M, H, I, E, top_k;
   int routed;       // routes from logits (given or computed), else from given ids
@@ -616,6 +619,15 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
   }
 }
 
+// The last block hands the call's recorded status to the caller when asked
+// (and clears the record, so every call reports its own).  Every block's waves
+// made their memory operations complete before the block counted itself out,
+// so every error of the call is recorded by now.
+__device__ __forceinline__ void report_status(const MoeArgs& a, pq::WsHeader* hdr) {
+  if (a.status_out)
+    *a.status_out = (int32_t)__hip_atomic_exchange(&hdr->error, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait (wave-wide, bounded) until the routes of the call are visible.
 __device__ __forceinline__ void wait_routes(const uint32_t* s_ready, pq::WsHeader* hdr) {
   lds_wait(s_ready, [](uint32_t v) { return v != 0u; }, hdr);
@@ -987,6 +999,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     if (threadIdx.x == 0) {
       pq::atomic_store_relaxed(&hdr->done, 0u);
       pq::atomic_store_relaxed(&hdr->exit_count, 0u);
+      report_status(a, hdr);
     }
   }
 }
@@ -1325,7 +1338,10 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, hr, t * 16, 0, kAuxSC1);
     if (router)
       for (int t = threadIdx.x; t < a.M * a.E; t += kThreads) pq::st_agent_u32(a.lx + t, 0u);
-    if (threadIdx.x == 0) pq::atomic_store_relaxed(&hdr->exit_count, 0u);
+    if (threadIdx.x == 0) {
+      pq::atomic_store_relaxed(&hdr->exit_count, 0u);
+      report_status(a, hdr);
+    }
   }
 }
 
@@ -1448,6 +1464,126 @@ int launch_moe_path(int path, const MoeArgs& a, const MoePlan& pl, const pqhost:
   return path == kPathStream ? launch_moe<TP, true, false>(a, pl, dev, s) : launch_moe<TP, false, false>(a, pl, dev, s);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry point: the layer's workspace in a static device array
+// ---------------------------------------------------------------------------
+// moe_decode_layer_noalloc serves callers that cannot allocate device memory
+// (code under HIP graph capture, tight serving loops).  Its workspace is this
+// file-scope array: one copy per GPU the library runs on, held until the
+// process ends.  The host only ever uses the device address that
+// hipGetSymbolAddress returns for it (the array's name is a host-side stand-in
+// in host code).  Every call on a GPU shares that GPU's copy, so calls that
+// can overlap in time on one GPU race.  The layer kernels leave the counters,
+// flags and exchange regions at zero when they finish, as they do in a
+// caller's workspace; the copy is zeroed once, when the device first uses it.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint4* p, int n16) {
+  for (int i = (int)(blockIdx.x * 256 + threadIdx.x); i < n16; i += (int)(gridDim.x * 256)) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+struct DeviceScratch {
+  std::once_flag once;
+  void* ptr = nullptr;
+  int status = PQ_OK;
+  int hip_error = 0;
+};
+DeviceScratch g_scratch[pqhost::kMaxDevices];
+
+// The device address of this device's scratch copy, looked up (and the copy
+// zeroed on `stream`) the first time the device uses it.
+int device_scratch(int device, hipStream_t stream, void** out) {
+  if (device < 0 || device >= pqhost::kMaxDevices) return PQ_ERR_UNSUPPORTED;
+  DeviceScratch& d = g_scratch[device];
+  std::call_once(d.once, [&] {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p == nullptr) e = hipErrorInvalidSymbol;
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream, reinterpret_cast<uint4*>(p),
+                         (int)(kScratchBytes / 16));
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) {
+      d.status = PQ_ERR_HIP;
+      d.hip_error = (int)e;
+      return;
+    }
+    d.ptr = p;
+  });
+  if (d.status != PQ_OK) {
+    pqhost::set_last_hip_error(d.hip_error);
+    return d.status;
+  }
+  *out = d.ptr;
+  return PQ_OK;
+}
+
+// The layer call behind moe_decode_layer_ex (caller's workspace) and
+// moe_decode_layer_noalloc (ws == NULL: the device's static scratch).
+int layer_call(const uint16_t* x, int M, int H, const uint16_t* router_w, float* router_logits, int32_t* topk_ids,
+               float* topk_w, int E, int top_k, int I, const uint8_t* w13, const float* s13, const uint8_t* w2,
+               const float* s2, const uint8_t* sh_w13, const float* sh_s13, const uint8_t* sh_w2,
+               const float* sh_s2, uint16_t* out, uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg, void* ws,
+               size_t ws_bytes, int32_t* status_out, void* stream) {
+  if (!x || !topk_ids || !topk_w || !w13 || !s13 || !w2 || !s2 || !out) return PQ_ERR_NULL;
+  const int nsh = (sh_w13 != nullptr) + (sh_s13 != nullptr) + (sh_w2 != nullptr) + (sh_s2 != nullptr);
+  if (nsh != 0 && nsh != 4) return PQ_ERR_NULL;      // all four shared-expert tensors or none
+  const int sh = nsh == 4 ? 1 : 0;
+  MoePlan pl;
+  const int path = moe_path(M);
+  int st = moe_plan(M, H, I, E, top_k, 0, path, &pl, sh);   // shape checks (device independent)
+  if (st != PQ_OK) return st;
+  const void* ptrs[] = {x, router_w, router_logits, topk_ids, topk_w, w13, s13, w2, s2,
+                        sh_w13, sh_s13, sh_w2, sh_s2, out, h_dbg, hq_dbg, hs_dbg, ws};
+  for (const void* q : ptrs)
+    if (q && !pqhost::aligned16(q)) return PQ_ERR_ALIGN;
+  if (router_w && (size_t)E * H * 2 > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
+  if (ws == nullptr && pl.ws_total > kScratchBytes) return PQ_ERR_SCRATCH;
+  if (ws != nullptr && ws_bytes < pl.ws_total) return PQ_ERR_WORKSPACE;
+  pqhost::DeviceInfo dev;
+  st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+  if (ws == nullptr) {                 // allocation-free call: this device's static scratch
+    st = device_scratch(dev.device, (hipStream_t)stream, &ws);
+    if (st != PQ_OK) return st;
+  }
+  st = moe_plan(M, H, I, E, top_k, dev.num_cus, path, &pl, sh);
+  if (st != PQ_OK) return st;
+
+  MoeArgs a;
+  a.x = x;
+  a.wr = router_w;
+  a.logits = router_w ? nullptr : router_logits;
+  a.logits_out = router_w ? router_logits : nullptr;
+  a.lx = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kWsLxOff);
+  a.sw13 = sh_w13; a.ss13 = sh_s13; a.sw2 = sh_w2; a.ss2 = sh_s2;
+  a.topk_ids = topk_ids; a.topk_w = topk_w;
+  a.w13 = w13; a.s13 = s13; a.w2 = w2; a.s2 = s2; a.out = out;
+  a.h_dbg = h_dbg; a.hq_dbg = hq_dbg; a.hs_dbg = hs_dbg;
+  a.ws = reinterpret_cast<uint8_t*>(ws);
+  a.status_out = status_out;
+  a.hbuf = reinterpret_cast<uint16_t*>(a.ws + pl.off_h);
+  a.M = M; a.H = H; a.I = I; a.E = E; a.top_k = top_k;
+  a.router = router_w != nullptr;
+  a.routed = router_w != nullptr || router_logits != nullptr;
+  a.sh = sh;
+  a.P2 = M * top_k + sh * M;
+  a.spin_limit = kSpinLimit;
+  a.xs_off = pl.xs_off; a.ha_off = pl.ha_off; a.hs_off = pl.hs_off; a.yb_off = pl.yb_off;
+  a.alias = pl.alias;
+  const char* lim = getenv("PQ_SPIN_LIMIT");
+  if (lim && *lim) a.spin_limit = (uint32_t)strtoul(lim, nullptr, 10);
+
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 1) return launch_moe_path<1>(path, a, pl, dev, s);
+  if (M == 2) return launch_moe_path<2>(path, a, pl, dev, s);
+  if (M <= 4) return launch_moe_path<4>(path, a, pl, dev, s);
+  return launch_moe_path<8>(path, a, pl, dev, s);
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -1481,54 +1617,19 @@ int moe_decode_layer_ex(const uint16_t* x, int M, int H, const uint16_t* router_
                         const float* s13, const uint8_t* w2, const float* s2, const uint8_t* sh_w13,
                         const float* sh_s13, const uint8_t* sh_w2, const float* sh_s2, uint16_t* out,
                         uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg, void* ws, size_t ws_bytes, void* stream) {
-  if (!x || !topk_ids || !topk_w || !w13 || !s13 || !w2 || !s2 || !out || !ws) return PQ_ERR_NULL;
-  const int nsh = (sh_w13 != nullptr) + (sh_s13 != nullptr) + (sh_w2 != nullptr) + (sh_s2 != nullptr);
-  if (nsh != 0 && nsh != 4) return PQ_ERR_NULL;      // all four shared-expert tensors or none
-  const int sh = nsh == 4 ? 1 : 0;
-  MoePlan pl;
-  const int path = moe_path(M);
-  int st = moe_plan(M, H, I, E, top_k, 0, path, &pl, sh);   // shape checks (device independent)
-  if (st != PQ_OK) return st;
-  const void* ptrs[] = {x, router_w, router_logits, topk_ids, topk_w, w13, s13, w2, s2,
-                        sh_w13, sh_s13, sh_w2, sh_s2, out, h_dbg, hq_dbg, hs_dbg, ws};
-  for (const void* q : ptrs)
-    if (q && !pqhost::aligned16(q)) return PQ_ERR_ALIGN;
-  if (router_w && (size_t)E * H * 2 > pq::kMaxBufferBytes) return PQ_ERR_SHAPE;
-  if (ws_bytes < pl.ws_total) return PQ_ERR_WORKSPACE;
-  pqhost::DeviceInfo dev;
-  st = pqhost::current_device_info(&dev);
-  if (st != PQ_OK) return st;
-  st = moe_plan(M, H, I, E, top_k, dev.num_cus, path, &pl, sh);
-  if (st != PQ_OK) return st;
+  if (!ws) return PQ_ERR_NULL;
+  return layer_call(x, M, H, router_w, router_logits, topk_ids, topk_w, E, top_k, I, w13, s13, w2, s2, sh_w13,
+                    sh_s13, sh_w2, sh_s2, out, h_dbg, hq_dbg, hs_dbg, ws, ws_bytes, nullptr, stream);
+}
 
-  MoeArgs a;
-  a.x = x;
-  a.wr = router_w;
-  a.logits = router_w ? nullptr : router_logits;
-  a.logits_out = router_w ? router_logits : nullptr;
-  a.lx = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kWsLxOff);
-  a.sw13 = sh_w13; a.ss13 = sh_s13; a.sw2 = sh_w2; a.ss2 = sh_s2;
-  a.topk_ids = topk_ids; a.topk_w = topk_w;
-  a.w13 = w13; a.s13 = s13; a.w2 = w2; a.s2 = s2; a.out = out;
-  a.h_dbg = h_dbg; a.hq_dbg = hq_dbg; a.hs_dbg = hs_dbg;
-  a.ws = reinterpret_cast<uint8_t*>(ws);
-  a.hbuf = reinterpret_cast<uint16_t*>(a.ws + pl.off_h);
-  a.M = M; a.H = H; a.I = I; a.E = E; a.top_k = top_k;
-  a.router = router_w != nullptr;
-  a.routed = router_w != nullptr || router_logits != nullptr;
-  a.sh = sh;
-  a.P2 = M * top_k + sh * M;
-  a.spin_limit = kSpinLimit;
-  a.xs_off = pl.xs_off; a.ha_off = pl.ha_off; a.hs_off = pl.hs_off; a.yb_off = pl.yb_off;
-  a.alias = pl.alias;
-  const char* lim = getenv("PQ_SPIN_LIMIT");
-  if (lim && *lim) a.spin_limit = (uint32_t)strtoul(lim, nullptr, 10);
-
-  hipStream_t s = (hipStream_t)stream;
-  if (M == 1) return launch_moe_path<1>(path, a, pl, dev, s);
-  if (M == 2) return launch_moe_path<2>(path, a, pl, dev, s);
-  if (M <= 4) return launch_moe_path<4>(path, a, pl, dev, s);
-  return launch_moe_path<8>(path, a, pl, dev, s);
+int moe_decode_layer_noalloc(const uint16_t* x, int M, int H, const uint16_t* router_w, float* router_logits,
+                             int32_t* topk_ids, float* topk_w, int E, int top_k, int I, const uint8_t* w13,
+                             const float* s13, const uint8_t* w2, const float* s2, const uint8_t* sh_w13,
+                             const float* sh_s13, const uint8_t* sh_w2, const float* sh_s2, uint16_t* out,
+                             uint16_t* h_dbg, uint8_t* hq_dbg, float* hs_dbg, int32_t* status, void* stream) {
+  if (status && !pqhost::aligned16(status)) return PQ_ERR_ALIGN;
+  return layer_call(x, M, H, router_w, router_logits, topk_ids, topk_w, E, top_k, I, w13, s13, w2, s2, sh_w13,
+                    sh_s13, sh_w2, sh_s2, out, h_dbg, hq_dbg, hs_dbg, nullptr, 0, status, stream);
 }
 
 int moe_decode_layer(const uint16_t* x, int M, int H, const float* router_logits, int32_t* topk_ids,

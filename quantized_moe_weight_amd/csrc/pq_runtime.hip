@@ -54,6 +54,7 @@ const char* pq_strerror(int status) {
     case PQ_ERR_HIP: return "PQ_ERR_HIP: a HIP runtime call failed";
     case PQ_ERR_TIMEOUT: return "PQ_ERR_TIMEOUT: a kernel's bounded spin-wait gave up";
     case PQ_ERR_BAD_EXPERT: return "PQ_ERR_BAD_EXPERT: a top-k expert id was out of range";
+    case PQ_ERR_SCRATCH: return "PQ_ERR_SCRATCH: the call needs more than the library's static scratch holds";
     default: return "unknown pq_status";
   }
 }
@@ -66,7 +67,7 @@ int pq_launches_per_call(const char* entry_point) {
   // GEMM; every other compute entry point is one launch
   static const char* const kOne[] = {"pq_quantize_fp8", "pq_quantize_q4", "pq_gemv_fp8", "pq_gemm_fp8_prequant",
                                      "pq_gemv_q4", "moe_decode_layer", "moe_decode_layer_ex",
-                                     "pq_stream_probe"};
+                                     "moe_decode_layer_noalloc", "pq_stream_probe"};
   if (strcmp(entry_point, "pq_gemm_fp8") == 0) return 2;
   for (const char* n : kOne)
     if (strcmp(entry_point, n) == 0) return 1;

@@ -32,7 +32,7 @@ def test_every_header_function_is_exported(lib):
 
 
 def test_strerror_covers_every_status(lib):
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         assert b"unknown" not in lib.pq_strerror(st)
 
 
@@ -41,7 +41,7 @@ def test_launches_per_call_per_entry_point(lib):
     activation quantisation, then the GEMM)."""
     f = lib.pq_launches_per_call
     assert f(b"pq_gemm_fp8") == 2
-    for name in (b"pq_gemv_fp8", b"pq_gemv_q4", b"moe_decode_layer", b"moe_decode_layer_ex",
+    for name in (b"pq_gemv_fp8", b"pq_gemv_q4", b"moe_decode_layer", b"moe_decode_layer_ex", b"moe_decode_layer_noalloc",
                  b"pq_gemm_fp8_prequant", b"pq_quantize_fp8", b"pq_quantize_q4", b"pq_stream_probe"):
         assert f(name) == 1, name
     assert f(b"pq_strerror") == PQ_ERR_UNSUPPORTED
@@ -168,3 +168,27 @@ def test_gemm_fp8_host_validation(lib):
     assert q(NUL, FAKE, 64, 512, FAKE, FAKE, 256, 0, FAKE, NUL) == PQ_ERR_NULL
     assert q(FAKE, FAKE, 64, 512, FAKE, FAKE, 256, 3, FAKE, NUL) == PQ_ERR_SHAPE
     assert q(FAKE, MIS, 64, 512, FAKE, FAKE, 256, 0, FAKE, NUL) == PQ_ERR_ALIGN
+
+
+def test_moe_noalloc_host_validation(lib):
+    """The allocation-free layer entry point validates like the workspace form
+    and refuses, before touching the device, a call whose layer needs more
+    than its 4 MiB static scratch."""
+    g = lib.moe_decode_layer_noalloc
+
+    def a(x=FAKE, M=1, H=512, E=16, k=4, I=256, status=NUL, sh=(NUL, NUL, NUL, NUL)):
+        return (x, M, H, NUL, FAKE, FAKE, FAKE, E, k, I, FAKE, FAKE, FAKE, FAKE, *sh, FAKE, NUL, NUL, NUL, status, NUL)
+    PQ_ERR_SCRATCH = -9
+    assert g(*a(x=NUL)) == PQ_ERR_NULL
+    assert g(*a(sh=(FAKE, NUL, NUL, NUL))) == PQ_ERR_NULL
+    assert g(*a(M=9)) == PQ_ERR_SHAPE
+    assert g(*a(status=MIS)) == PQ_ERR_ALIGN
+    # 8 tokens x 8 slots (+ the shared pair each) at I = 14208: 2.05 MB of h on top of 2.06 MB of fixed
+    # regions, a valid workspace-form call (I = 14080 still fits)
+    assert lib.moe_decode_layer_workspace(8, 1024, 14208, 16, 8) > 4 << 20
+    assert g(*a(M=8, H=1024, I=14208, k=8)) == PQ_ERR_SCRATCH
+    assert lib.moe_decode_layer_workspace(8, 1024, 14080, 16, 8) <= 4 << 20
+    assert g(*a(M=8, H=1024, I=14080, k=8)) in (PQ_OK, PQ_ERR_UNSUPPORTED, -6)
+    # the bench's shapes fit
+    assert lib.moe_decode_layer_workspace(8, 6144, 2048, 256, 8) <= 4 << 20
+    assert g(*a(M=8, H=6144, I=2048, E=256, k=8)) in (PQ_OK, PQ_ERR_UNSUPPORTED, -6)

@@ -105,9 +105,8 @@ def read_traffic(bytes_alg):
     return d["fetch_kib"] * 1024 * d["fetch_scale"] + d["write_kib"] * 1024 * d["write_scale"]
 
 
-def cpu_baseline(shp, x_bits, lg, budget_s=12.0):
-    """Time the CPU oracle on one routed layer call (repeated until ~budget_s)."""
-    import numpy as np
+def cpu_experts(shp, lg):
+    """The oracle's own coding of the experts one layer call routes to (untimed)."""
     import oracle
     import workloads
     ids, _ = oracle.route_topk(lg, shp.top_k)
@@ -118,19 +117,34 @@ def cpu_baseline(shp, x_bits, lg, budget_s=12.0):
         m2 = workloads.master_weights_torch(shp.H, shp.I, workload=workloads.MOE_LAYER,
                                             tensor=workloads.T_W2, expert=int(e)).cpu().numpy()
         experts[int(e)] = oracle.block_quant_fp8(m13) + oracle.block_quant_fp8(m2)
+    return experts
+
+
+def cpu_baseline(shp, x_bits, lg, experts, budget_s=12.0, threads=None):
+    """Time the CPU oracle on one routed layer call (repeated until ~budget_s;
+    at least once).  threads: limit the BLAS thread pools to that many threads
+    for the timing (None: as configured, i.e. all cores)."""
+    import oracle
+    import contextlib
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:
-        cores = len(os.sched_getaffinity(0))
-    reps, t0 = 0, time.perf_counter()
-    res = None
-    while True:
-        res = oracle.moe_layer(x_bits, lambda e: experts[e], logits=lg, top_k=shp.top_k)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / reps
+        threadpool_info = threadpool_limits = None
+    limit = (threadpool_limits(limits=threads) if (threads and threadpool_limits)
+             else contextlib.nullcontext())
+    with limit:
+        if threadpool_info is not None:
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        else:
+            cores = threads or len(os.sched_getaffinity(0))
+        reps, t0 = 0, time.perf_counter()
+        res = None
+        while True:
+            res = oracle.moe_layer(x_bits, lambda e: experts[e], logits=lg, top_k=shp.top_k)
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = (time.perf_counter() - t0) / reps
     return dt, reps, cores, res, len(experts)
 
 
@@ -306,7 +320,8 @@ def run(args):
         out["config"]["bytes_per_accepted_token_L3.5"] = int(bytes_per_launch / 3.5)
 
     if args.cpu_baseline and pool_np is not None:
-        dt, reps, cores, ref, nexp = cpu_baseline(shp, x_bits, pool_np[0])
+        experts = cpu_experts(shp, pool_np[0])
+        dt, reps, cores, ref, nexp = cpu_baseline(shp, x_bits, pool_np[0], experts)
         b0 = step_bytes[0]
         call(x, pool[0])
         torch.cuda.synchronize()
@@ -321,6 +336,12 @@ def run(args):
                        f"float64 dequantise-then-matmul oracle repeated {reps}x, {dt:.2f} s per call; "
                        "weights pre-quantised by the oracle, untimed"),
             "seconds_per_call": round(dt, 3),
+        }
+        dt1, reps1, cores1, _, _ = cpu_baseline(shp, x_bits, pool_np[0], experts, budget_s=6.0, threads=1)
+        out["cpu_baseline"]["single_thread"] = {
+            "value": round(b0 / dt1 / 1e9, 3), "unit": "GB/s", "cores": int(cores1),
+            "seconds_per_call": round(dt1, 3), "reps": reps1,
+            "how": "the same oracle call with the BLAS thread pools limited to one thread",
         }
         out["parity_check"] = {"max_err_over_S": rel, "bound": 2e-3, "ok": rel <= 2e-3}
     print(json.dumps(out), flush=True)

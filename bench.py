@@ -419,20 +419,35 @@ def run_dense(args):
         nb = max(int(lib.pq_gemv_q4_workspace(M, K, N, e)) for K, N, e, _, _ in layers[:3])
         ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
         lib.pq_workspace_init(P(ws), ws.numel(), st)
-        for K, N, e, q, sc in layers:
+        group = args.q4_mode == "group"
+        arr = (pq._lib.Q4Linear * len(layers))()
+        pass_bytes = 0
+        for i, (K, N, e, q, sc) in enumerate(layers):
             n_out = N // 2 if e else N
             y = ys.setdefault((n_out,), torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda"))
             b = q.numel() + sc.numel() * 2 + 2 * M * K + 2 * M * n_out
-            launches.append((lambda K=K, N=N, e=e, q=q, sc=sc, y=y: lib.pq_gemv_q4(
-                P(xs[K]), M, K, P(q), P(sc), N, e, P(y), P(ws), ws.numel(), st), b))
-        kernel, unit = "gemv_q4 kernels", "stack pass (192 linears)"
+            pass_bytes += b
+            arr[i] = pq._lib.Q4Linear(xs[K].data_ptr(), q.data_ptr(), sc.data_ptr(), y.data_ptr(), K, N, e)
+            if not group:
+                launches.append((lambda K=K, N=N, e=e, q=q, sc=sc, y=y: lib.pq_gemv_q4(
+                    P(xs[K]), M, K, P(q), P(sc), N, e, P(y), P(ws), ws.numel(), st), b))
+        n_launch = ctypes.c_int(0)
+        if group:
+            # the whole stack in one library call: the linears are packed into as few
+            # launches as LDS allows (one persistent grid streams each pack)
+            launches.append((lambda: lib.pq_gemv_q4_group(arr, len(layers), M, ctypes.byref(n_launch), st),
+                             pass_bytes))
+        kernel = "gemv_q4_kernel (grouped)" if group else "gemv_q4 kernels"
+        unit = "stack pass (192 linears)"
         config = {"workload": f"int4 g32 W4A16 decode stack, M={M}: 64 blocks x (5120->5120, 5120->2x17408 SiLU*up, "
-                              "17408->5120), fp16 group scales, 10.57 GB", "M": M, "linears": len(launches)}
+                              "17408->5120), fp16 group scales, 10.57 GB, fresh activation per linear",
+                  "M": M, "linears": len(layers),
+                  "issue": ("one pq_gemv_q4_group call per pass" if group else "one pq_gemv_q4 call per linear")}
     else:
         raise SystemExit(f"unknown workload {args.workload}")
 
     n = len(launches)
-    for i in range(min(n, 2 * args.warmup + n // 4)):
+    for i in range(max(min(n, 2 * args.warmup + n // 4), args.warmup)):
         launches[i % n][0]()
     torch.cuda.synchronize()
     K_steps = args.steps
@@ -476,10 +491,12 @@ def run_dense(args):
                      "launch_us_p10_p50_p90": [round(float(q10), 2), round(float(q50), 2), round(float(q90), 2)],
                      "bytes_per_step": int(bytes_per_pass)},
     }
-    if args.workload == "q4_stack":
+    if args.workload == "q4_stack" and n > 1:
         per_shape = per.reshape(passes, n)
         out["per_linear_median_us"] = {f"{K}->{N}{' silu' if e else ''}": round(float(np.median(per_shape[:, j::3])) * 1e6, 2)
                                        for j, (K, N, e, _, _) in enumerate(layers[:3])}
+    if args.workload == "q4_stack":
+        out["config"]["launches_per_pass"] = n_launch.value if n == 1 else n
     print(json.dumps(out), flush=True)
 
 
@@ -675,6 +692,8 @@ def main():
                     choices=["moe", "moe_tp8", "moe_full", "gemv_small", "gate_up", "lm_head", "q4_stack", "prefill"],
                     help="moe (default: the routed layer) or one of the dense configurations")
     ap.add_argument("--tokens", type=int, default=4096, help="prefill workload: tokens per call")
+    ap.add_argument("--q4-mode", default="group", choices=["group", "single"],
+                    help="q4_stack: one grouped call per pass (default) or one pq_gemv_q4 call per linear")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))

@@ -198,6 +198,33 @@ int pq_gemv_q4(const uint16_t* x, int M, int K,
                const uint8_t* w, const uint16_t* w_scale, int N,
                int epi, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
+/* One int4 linear of a grouped call (the arguments of pq_gemv_q4). */
+typedef struct {
+  const uint16_t* x;        /* bf16 [M,K]                                   */
+  const uint8_t* w;         /* nibbles [N,K/2] (layout of pq_quantize_q4)   */
+  const uint16_t* w_scale;  /* fp16 [N,K/32]                                */
+  uint16_t* y;              /* bf16 [M,N], or [M,N/2] under PQ_EPI_SILU_MUL */
+  int K, N, epi;
+} pq_q4_linear;
+
+/* Several independent int4 g32 GEMVs, all with M tokens, in as few launches
+ * as possible ([M3]: merging the small kernels of a decode step raised it from
+ * 59% to 81% of measured bandwidth): linears[i] computes exactly what
+ * pq_gemv_q4 computes for those arguments on its vector kernel, and every
+ * output bit equals that call's (each linear's work is split over the grid
+ * and the waves as if it ran alone; it does not depend on the other linears
+ * of the call, nor on M).  The linears are packed in order into launches of
+ * at most 12 whose activations (M*K*2.125 bytes each, plus partial sums) fit
+ * one CU's 160 KB of LDS; each launch streams all of its linears' weights
+ * back to back from one persistent grid, so start-up and ring fill are paid
+ * once per launch instead of once per linear.
+ *   linears : host array of n descriptors (device pointers inside)
+ *   launches: nullable host int; receives the number of kernel launches made
+ * Constraints per linear as pq_gemv_q4 (PQ_ERR_SHAPE etc.; nothing is
+ * launched if any linear is invalid); n = 0 is a no-op.  No workspace.
+ * The outputs must not overlap any input of the same call. */
+int pq_gemv_q4_group(const pq_q4_linear* linears, int n, int M, int* launches, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Routed MoE decode layer in ONE kernel launch ([Sionic] intro, §4, §5;      */
 /* [M1] dispatch-bound MoE; [M3] merging small kernels).                      */

@@ -14,7 +14,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemm_fp8_prequant", "gemv_q4", "moe_decode_layer",
+__all__ = ["PqError", "quantize_fp8", "quantize_q4", "gemv_fp8", "gemm_fp8", "gemm_fp8_prequant", "gemv_q4",
+           "gemv_q4_group", "moe_decode_layer",
            "moe_decode_layer_noalloc", "gemv_fp8_workspace_bytes", "moe_workspace_bytes", "workspace_check",
            "launches_per_call", "moe_layer_config",
            "stream_probe",
@@ -219,6 +220,35 @@ def gemv_q4(x, w, w_scale, epi: int = EPI_NONE, out=None):
     _check(lib().pq_gemv_q4(_p(x), M, K, _p(w), _p(w_scale), N, epi, _p(y), _p(ws), wsn, _stream()),
            "pq_gemv_q4")
     return y
+
+
+def gemv_q4_group(items):
+    """Several independent int4 GEMVs in as few launches as possible.
+    items: list of (x bf16 [M,K], w uint8 [N,K/2], w_scale fp16 [N,K/32], epi)
+    or (x, w, w_scale, epi, y); every x has the same M.  Returns (list of y,
+    launches made)."""
+    if not items:
+        return [], 0
+    M = items[0][0].shape[0]
+    arr = (_lib.Q4Linear * len(items))()
+    ys = []
+    for i, it in enumerate(items):
+        x, w, sc, epi = it[:4]
+        _need(x, torch.bfloat16, 2, "x")
+        _need(w, torch.uint8, 2, "w")
+        _need(sc, torch.float16, 2, "w_scale")
+        if x.shape[0] != M:
+            raise ValueError("every linear of a group has the same M")
+        K, N = x.shape[1], w.shape[0]
+        if w.shape[1] != K // 2 or sc.shape != (N, K // 32):
+            raise ValueError("weight / scale shapes do not match x")
+        n_out = N // 2 if epi == EPI_SILU_MUL else N
+        y = it[4] if len(it) > 4 else torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+        ys.append(y)
+        arr[i] = _lib.Q4Linear(x.data_ptr(), w.data_ptr(), sc.data_ptr(), y.data_ptr(), K, N, epi)
+    nl = ctypes.c_int(0)
+    _check(lib().pq_gemv_q4_group(arr, len(items), M, ctypes.byref(nl), _stream()), "pq_gemv_q4_group")
+    return ys, nl.value
 
 
 def moe_workspace_bytes(M: int, H: int, I: int, E: int, top_k: int) -> int:

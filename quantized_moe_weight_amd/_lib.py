@@ -27,6 +27,7 @@ SIGNATURES = {
     "pq_gemm_fp8_prequant": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp]),
     "pq_gemv_q4_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "pq_gemv_q4": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "pq_gemv_q4_group": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
     "moe_decode_layer_workspace": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_decode_layer": (_c_int, [_vp, _c_int, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
@@ -44,6 +45,14 @@ SIGNATURES = {
     "moe_decode_layer_config": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "pq_stream_probe": (_c_int, [_vp, _c_size, _vp, _vp]),
 }
+
+
+
+class Q4Linear(ctypes.Structure):
+    """pq_q4_linear of include/pq.h."""
+    _fields_ = [("x", _vp), ("w", _vp), ("w_scale", _vp), ("y", _vp),
+                ("K", _c_int), ("N", _c_int), ("epi", _c_int)]
+
 
 _lib = None
 

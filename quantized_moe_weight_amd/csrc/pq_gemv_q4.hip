@@ -37,21 +37,10 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / pq::kWave;
 constexpr int kMaxM = 8;
 constexpr int kGroup = 32;                 // weights per fp16 scale
-constexpr int kRowsCap = 128;              // rows per block at most
 constexpr int kXGroups = 2;                // x groups per thread loaded before the weight ring
 constexpr long kMaxMK = 69632;             // M*K bound: activation + sums + partials fit LDS
 constexpr uint32_t kOne = 0x3F803F80u;     // bf16 pair (1.0, 1.0)
 constexpr uint32_t kNibMask = 0x00780078u; // mantissa bits 3..6 of both halves
-
-struct Q4Args {
-  const uint16_t* x;
-  const uint8_t* w;
-  const uint16_t* wsc;
-  uint16_t* y;
-  int M, K, N;
-  int R;        // output rows (N, or N/2 under SiLU*up)
-  int nch;      // 1 KB chunks per row
-};
 
 // The constant (1.0, 1.0) held in a VGPR the compiler cannot see through:
 // with it in a register each pair below is one shift and one v_and_or_b32
@@ -109,187 +98,381 @@ __device__ __forceinline__ uint4 pair_order(uint4 r) {
   return o;
 }
 
-// LDS layout of one block: [x pairs: M*K*2 + 64 (a dummy group)]
-// [c: M*K/32 + 1 floats (one dummy)][partials: (rows + kWaves) * M * NROW floats]
-__host__ __device__ inline size_t x_region(int M, int K) { return (size_t)M * K * 2 + 64; }
-__host__ __device__ inline size_t c_region(int M, int K) { return ((size_t)M * (K / kGroup) + 4) * 4; }
-__host__ __device__ inline size_t lds_bytes(int M, int K, int rows, int nrow) {
-  return x_region(M, K) + c_region(M, K) + (size_t)(rows + kWaves) * M * nrow * 4;
+// ---------------------------------------------------------------------------
+// Vector path.  One launch runs a list of independent linears (one when
+// called through pq_gemv_q4), each with its own x, weights, scales, output and
+// epilogue, all with M tokens.
+//
+//   * Work unit: one pair of weight rows at one 1 KB chunk.  Every lane loads
+//     the same 16 bytes of row A and of row B (2 KB per wave step) and reads
+//     the activation once for both rows.  Under SiLU*up, A is gate row i and
+//     B up row i; otherwise A and B are consecutive rows.
+//   * Block b owns the same share of every linear's rows (the split of the
+//     rows over the grid depends on the linear's shape and the CU count only),
+//     and a linear's units of the block are dealt to the block's waves in
+//     order, linear by linear, exactly as if the linear ran alone: a
+//     linear's output bits do not depend on the other linears of the launch,
+//     nor on M.  Each wave streams its share of every linear back to back;
+//     its ring of load steps runs across linear boundaries, so the start-up
+//     and ring fill are paid once per launch.
+//   * The activations of every linear of the launch are staged in LDS at
+//     the start, pieces of 16 bytes stored piece-major ([token][t][group]):
+//     the 64 lanes of a step read consecutive pieces, free of bank conflicts.
+//   * Row pairs cut between waves are reduced through LDS after one barrier at
+//     the end, in wave order.
+// ---------------------------------------------------------------------------
+constexpr int kMaxLin = 12;      // linears per launch (kernel arguments by value)
+// 16 waves per CU: the loop is bound by vector instructions (unpacking and
+// dot products, ~190 per 2 KB step at M = 1), and four waves per SIMD hide
+// their load and LDS latencies better than two (10.57 GB dense stack at M = 1:
+// 2.50 ms per pass against 2.66 with 512 threads)
+constexpr int kVThreads = 1024;
+constexpr int kVWaves = kVThreads / pq::kWave;
+constexpr uint32_t kStepBytes = 1024;  // bytes of each row of the pair per wave step
+
+struct Q4Lin {
+  const uint16_t* x;
+  const uint8_t* w;
+  const uint16_t* wsc;
+  uint16_t* y;
+  int K, N, R;     // R: output rows (N, or N/2 under SiLU*up)
+  int silu;        // rows [0,R) gate, [R,2R) up; one output per row pair
+  int ng;          // 32-groups per row
+  int nch;         // 512-byte chunks per row
+  int xoff;        // LDS: x pieces of this linear (16 B each), [MT][4][ng]
+  int soff;        // LDS: group offsets (floats), [MT][ng]
+  int poff;        // LDS: partials (floats), [pairs + waves][MT][2]
+};
+
+struct Q4Group {
+  Q4Lin lin[kMaxLin];
+  int n;
+  int dummy_piece;  // LDS piece written by threads without a group
+  int dummy_float;  // LDS float written by threads without a group
+};
+
+// this block's rows of a linear, as row pairs
+struct BlockRows {
+  int rs, re, pairs;
+};
+__device__ __forceinline__ BlockRows block_rows(const Q4Lin& L, int G, int b) {
+  BlockRows r;
+  r.rs = pq::split_start(L.R, G, b);
+  r.re = pq::split_start(L.R, G, b + 1);
+  r.pairs = L.silu ? r.re - r.rs : (r.re - r.rs + 1) / 2;
+  return r;
 }
 
-// Stage one 32-value group of x: pairs into LDS and c = the v_dot2 chain of
-// dot32 with every weight pair (1.5, 1.5), in the same order, so that a group
-// whose nibbles are all 8 (q = 0) contributes exactly zero.
-__device__ __forceinline__ void stage_group(uint4* xs_l, float* gsum, int slot, const uint4 (&raw)[4]) {
+// Stage one 32-value group of x: its 4 pieces in the paired order, and c =
+// the v_dot2 chain of dot32 with every weight pair (1.5, 1.5), in the same
+// order, so that a group whose nibbles are all 8 (q = 0) contributes exactly
+// zero.  piece0 / stride: where piece t goes (piece0 + t * stride).
+__device__ __forceinline__ void stage_group(uint4* xs_l, float* cs, int piece0, int stride, int cslot,
+                                            const uint4 (&raw)[4]) {
   uint4 xv[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     xv[t] = pair_order(raw[t]);
-    xs_l[4 * slot + t] = xv[t];
+    xs_l[piece0 + t * stride] = xv[t];
   }
   Pairs16 th;
 #pragma unroll
   for (int i = 0; i < 16; ++i) th.v[i] = 0x3FC03FC0u;
-  gsum[slot] = dot32(th, xv);
+  cs[cslot] = dot32(th, xv);
 }
 
-// PAIR (the groups per row, K / 32, even): each lane loads the aligned dword
-// that holds its group's scale and its neighbour's (lanes 2i and 2i + 1 share
-// it) and keeps its own half.  A 16-bit scale per ring slot made the compiler
-// pack the slots' scales pairwise at the end of every ring cycle, which waited
-// for nearly every load in flight (the ring drained to two loads once per
-// cycle); 32-bit values are never packed.
-template <int NROW, int D, int MT, bool PAIR>
-__global__ __launch_bounds__(kThreads) void gemv_q4_kernel(Q4Args a) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint4* xs_l = reinterpret_cast<uint4*>(smem);
-  float* gsum = reinterpret_cast<float*>(smem + x_region(MT, a.K));
-  const int ng = a.K / kGroup;                        // groups per row
-  float* part = reinterpret_cast<float*>(smem + x_region(MT, a.K) + c_region(MT, a.K));   // [(row + wave)][MT][NROW]
+// Walks one wave's steps through the linears of the launch: (linear, pair,
+// chunk), linear by linear, skipping linears that give the wave no unit.  The
+// per-linear starting points of every wave and the block's row ranges are
+// computed once, into an LDS table, so moving to the next linear is one table
+// read (an inlined search with divisions at every ring slot made the loop body
+// several times larger).  The launch arguments are only ever indexed with the
+// wave-uniform linear index (a per-lane index makes the compiler copy the
+// whole argument block to scratch memory).
+struct SegEntry {
+  int p0, c0, left;         // this wave's first unit of a linear (pair, chunk) and its steps there
+  int dp, dc;               // one step ahead: kVWaves units = dp pairs and dc chunks
+  int rs, re, nch;          // this block's rows of the linear, chunks per row
+};
+struct StepCursor {
+  int li, p, c, left, nch, rs, re, dp, dc;
+};
+__device__ __forceinline__ StepCursor cursor_at(const Q4Group& a, const SegEntry* seg, int li) {
+  StepCursor s;
+  for (; li < a.n; ++li)
+    if (__builtin_amdgcn_readfirstlane(seg[li].left) > 0) break;
+  s.li = li;
+  s.p = s.c = s.left = s.rs = s.re = s.dp = s.dc = 0;
+  s.nch = 1;
+  if (li < a.n) {
+    const SegEntry& e = seg[li];
+    s.p = __builtin_amdgcn_readfirstlane(e.p0);
+    s.c = __builtin_amdgcn_readfirstlane(e.c0);
+    s.left = __builtin_amdgcn_readfirstlane(e.left);
+    s.dp = __builtin_amdgcn_readfirstlane(e.dp);
+    s.dc = __builtin_amdgcn_readfirstlane(e.dc);
+    s.rs = __builtin_amdgcn_readfirstlane(e.rs);
+    s.re = __builtin_amdgcn_readfirstlane(e.re);
+    s.nch = __builtin_amdgcn_readfirstlane(e.nch);
+  }
+  return s;
+}
+__device__ __forceinline__ StepCursor cursor_next(const Q4Group& a, const SegEntry* seg, StepCursor s) {
+  if (s.left == 1) return cursor_at(a, seg, s.li + 1);
+  --s.left;
+  s.p += s.dp;
+  s.c += s.dc;
+  if (s.c >= s.nch) {
+    s.c -= s.nch;
+    ++s.p;
+  }
+  return s;
+}
 
+// PAIR (every linear's groups per row even): each lane loads the aligned dword
+// holding its group's scale and its neighbour's (lanes 2i and 2i + 1 share
+// it) and keeps its half: 16-bit scale loads made the compiler pack the ring
+// slots' scales pairwise, waiting for nearly every load in flight.
+template <int D, int MT, bool PAIR>
+__global__ __launch_bounds__(kVThreads) void gemv_q4_kernel(const Q4Group a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ SegEntry s_seg[kVWaves][kMaxLin];
+  uint4* xs_l = reinterpret_cast<uint4*>(smem);
+  float* fl = reinterpret_cast<float*>(smem);
+  const int G = (int)gridDim.x;
   const int tid = (int)threadIdx.x;
   const int lane = pq::lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(pq::wave_id());
-  const int r0 = pq::split_start(a.R, (int)gridDim.x, (int)blockIdx.x);
-  const int nrows = pq::split_start(a.R, (int)gridDim.x, (int)blockIdx.x + 1) - r0;
-  const int nunits = nrows * a.nch;
-  const int u0 = pq::split_start(nunits, kWaves, wv);
-  const int nsteps = pq::split_start(nunits, kWaves, wv + 1) - u0;
-  const uint32_t rowb = (uint32_t)(a.K / 2);
 
-  // Activation loads first, one whole group per thread (kXGroups groups),
-  // and a plain barrier: every wave of the block has issued them before any
-  // weight load, so staging waits for x only, not for the weight ring.
-  const int ngr = MT * a.K / kGroup;                  // groups of x
-  const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(MT * a.K * 2));
+  // Activation loads of the first kXGroups groups per thread (counted over
+  // the groups of all linears), then a plain barrier: every wave issues them
+  // before any weight load, so staging waits for x only.
   uint4 xpre[kXGroups][4];
-#pragma unroll
-  for (int i = 0; i < kXGroups; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int g = tid + i * kThreads;
-      xpre[i][t] = pq::buf_load16(xr, g < ngr ? (uint32_t)g * 64u + 16u * t : pq::kOOB);
-    }
-  __builtin_amdgcn_s_barrier();
-
-  const pq::rsrc_t wr = pq::make_rsrc(a.w, (uint32_t)((size_t)a.N * rowb));
-  const pq::rsrc_t sr = pq::make_rsrc(a.wsc, (uint32_t)((size_t)a.N * ng * 2));
-  const uint32_t lane16 = 16u * (uint32_t)lane;
-
-  typedef typename std::conditional<PAIR, uint32_t, _Float16>::type SType;
-  uint4 wbuf[D][NROW];
-  SType sbuf[D][NROW];
-  int ir = u0 / a.nch, ic = u0 - (u0 / a.nch) * a.nch, left = nsteps;
-  auto issue = [&](uint4 (&wb)[NROW], SType (&sb)[NROW]) {
-    const uint32_t off = (uint32_t)(ic * pq::kChunk) + lane16;     // packed byte in the row
-    const bool ok = left > 0 && off < rowb;
-#pragma unroll
-    for (int j = 0; j < NROW; ++j) {
-      const uint32_t row = (uint32_t)(r0 + ir + j * a.R);
-      wb[j] = pq::buf_load16_nt(wr, ok ? row * rowb + off : pq::kOOB);
-      if constexpr (PAIR)
-        sb[j] = __builtin_amdgcn_raw_buffer_load_b32(
-            sr, (int)(ok ? (row * (uint32_t)ng + ((off / 16u) & ~1u)) * 2u : pq::kOOB), 0, pq::kAuxNT);
-      else
-        sb[j] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(
-            sr, (int)(ok ? (row * (uint32_t)ng + off / 16u) * 2u : pq::kOOB), 0, pq::kAuxNT));
-    }
-    --left;
-    if (++ic == a.nch) { ic = 0; ++ir; }
-  };
-#pragma unroll
-  for (int j = 0; j < D; ++j) issue(wbuf[j], sbuf[j]);
-  __builtin_amdgcn_sched_barrier(0);                  // keep the staging work below the ring issue
-
-  // Stage x.  The preloaded groups are stored unconditionally (threads
-  // without a group write the dummy slot), which keeps their loads ahead of
-  // the ring; groups beyond kXGroups per thread (M*K > 32768) follow.
+  int pre_li[kXGroups], pre_g[kXGroups];
 #pragma unroll
   for (int i = 0; i < kXGroups; ++i) {
-    const int g = tid + i * kThreads;
-    stage_group(xs_l, gsum, g < ngr ? g : ngr, xpre[i]);
-  }
-  for (int g = tid + kXGroups * kThreads; g < ngr; g += kThreads) {
-    uint4 raw[4];
+    pre_li[i] = a.n;
+    pre_g[i] = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) raw[t] = pq::buf_load16(xr, (uint32_t)g * 64u + 16u * t);
-    stage_group(xs_l, gsum, g, raw);
+    for (int t = 0; t < 4; ++t) xpre[i][t] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  {
+    int gbase = 0;
+    for (int li = 0; li < a.n && gbase < kXGroups * kVThreads; ++li) {   // uniform: one linear at a time
+      const Q4Lin& L = a.lin[li];
+      const int ngr = MT * L.ng;
+      const pq::rsrc_t xr = pq::make_rsrc(L.x, (uint32_t)(MT * L.K * 2));
+#pragma unroll
+      for (int i = 0; i < kXGroups; ++i) {
+        const int g = tid + i * kVThreads - gbase;
+        if (g >= 0 && g < ngr) {
+          pre_li[i] = li;
+          pre_g[i] = g;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) xpre[i][t] = pq::buf_load16(xr, (uint32_t)g * 64u + 16u * t);
+        }
+      }
+      gbase += ngr;
+    }
+  }
+  __builtin_amdgcn_s_barrier();
+
+  // This wave's units of every linear: unit u = (pair u / nch, chunk u % nch)
+  // of the block's rows goes to wave u % kVWaves, so at every step the waves of
+  // the block read one window of consecutive chunks (a few DRAM pages) rather
+  // than one stream each.  Written and read by the wave itself (no barrier).
+  int total = 0;
+  for (int li = 0; li < a.n; ++li) {             // uniform
+    const Q4Lin& L = a.lin[li];
+    const BlockRows br = block_rows(L, G, (int)blockIdx.x);
+    const int units = br.pairs * L.nch;
+    const int left = units > wv ? (units - wv + kVWaves - 1) / kVWaves : 0;
+    total += left;
+    if (lane == 0)
+      s_seg[wv][li] = SegEntry{wv / L.nch, wv - (wv / L.nch) * L.nch, left, kVWaves / L.nch,
+                               kVWaves - (kVWaves / L.nch) * L.nch, br.rs, br.re, L.nch};
+  }
+  const SegEntry* seg = s_seg[wv];
+
+  // the weight ring: D steps in flight, issued without branches on validity
+  StepCursor ic = cursor_at(a, seg, 0);
+  int ili = -1;
+  pq::rsrc_t wr = pq::make_rsrc(a.lin[0].w, 0u), sr = pq::make_rsrc(a.lin[0].wsc, 0u);
+  uint32_t rowb = 0, ngs = 0;
+  int rup = 0, silu = 0;
+  auto issue = [&](uint4 (&wq)[2], uint32_t (&sq)[2]) {
+    const bool ok = ic.li < a.n;
+    if (ok && ic.li != ili) {                    // a new linear: its descriptors
+      ili = ic.li;
+      const Q4Lin& L = a.lin[ili];
+      rowb = (uint32_t)(L.K / 2);
+      ngs = (uint32_t)L.ng;
+      wr = pq::make_rsrc(L.w, (uint32_t)((size_t)L.N * rowb));
+      sr = pq::make_rsrc(L.wsc, (uint32_t)((size_t)L.N * L.ng * 2));
+      silu = L.silu;
+      rup = L.R;
+    }
+    // the pair's two rows, and this lane's 16 bytes of the chunk
+    const int rowa = silu ? ic.rs + ic.p : ic.rs + 2 * ic.p;
+    const int rowb2 = silu ? rowa + rup : rowa + 1;
+    const uint32_t off = (uint32_t)ic.c * kStepBytes + 16u * (uint32_t)lane;
+    const bool va = ok && off < rowb;
+    const bool vb = va && (silu || rowb2 < ic.re);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool v = j == 0 ? va : vb;
+      const uint32_t row = (uint32_t)(j == 0 ? rowa : rowb2);
+      wq[j] = pq::buf_load16_nt(wr, v ? row * rowb + off : pq::kOOB);
+      if constexpr (PAIR)
+        sq[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            sr, (int)(v ? (row * ngs + ((off / 16u) & ~1u)) * 2u : pq::kOOB), 0, pq::kAuxNT);
+      else
+        sq[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+            sr, (int)(v ? (row * ngs + off / 16u) * 2u : pq::kOOB), 0, pq::kAuxNT);
+    }
+    if (ok) ic = cursor_next(a, seg, ic);
+  };
+  uint4 wbuf[D][2];
+  uint32_t sbuf[D][2];
+#pragma unroll
+  for (int q = 0; q < D; ++q) issue(wbuf[q], sbuf[q]);
+  __builtin_amdgcn_sched_barrier(0);               // keep the staging below the ring issue
+
+  // stage x of every linear (preloaded groups first; a thread without a
+  // group writes the dummy piece and float)
+  {
+    // preloaded groups (a thread without one writes the dummy piece and
+    // float), then the remaining groups of every linear: global group numbers
+    // run over the linears in order, a thread takes numbers tid + k * kVThreads
+    bool staged[kXGroups];
+#pragma unroll
+    for (int i = 0; i < kXGroups; ++i) staged[i] = false;
+    int gbase = 0;
+    for (int li = 0; li < a.n; ++li) {                // uniform
+      const Q4Lin& L = a.lin[li];
+      const int ngr = MT * L.ng;
+#pragma unroll
+      for (int i = 0; i < kXGroups; ++i) {
+        if (pre_li[i] == li) {
+          const int m = pre_g[i] / L.ng, g = pre_g[i] - m * L.ng;
+          stage_group(xs_l, fl, L.xoff + m * 4 * L.ng + g, L.ng, L.soff + m * L.ng + g, xpre[i]);
+          staged[i] = true;
+        }
+      }
+      const pq::rsrc_t xr = pq::make_rsrc(L.x, (uint32_t)(MT * L.K * 2));
+      // first number >= max(gbase, kXGroups * kVThreads) that is tid modulo kVThreads
+      const int lo = gbase > kXGroups * kVThreads ? gbase : kXGroups * kVThreads;
+      const int first = lo + ((tid - lo) % kVThreads + kVThreads) % kVThreads;
+      for (int gg = first; gg < gbase + ngr; gg += kVThreads) {
+        const int g0 = gg - gbase;
+        uint4 raw[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) raw[t] = pq::buf_load16(xr, (uint32_t)g0 * 64u + 16u * t);
+        const int m = g0 / L.ng, g = g0 - m * L.ng;
+        stage_group(xs_l, fl, L.xoff + m * 4 * L.ng + g, L.ng, L.soff + m * L.ng + g, raw);
+      }
+      gbase += ngr;
+    }
+#pragma unroll
+    for (int i = 0; i < kXGroups; ++i)
+      if (!staged[i]) stage_group(xs_l, fl, a.dummy_piece, 0, a.dummy_float, xpre[i]);
   }
   __syncthreads();
 
   const uint32_t one = one_pair_reg();
-  float acc[NROW][MT];
+  float acc[2][MT];
 #pragma unroll
-  for (int j = 0; j < NROW; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
 
-  int cr = u0 / a.nch, cc = u0 - (u0 / a.nch) * a.nch;    // consume cursor (local row, chunk)
-  auto consume = [&](const uint4 (&wb)[NROW], const SType (&sb)[NROW], bool last) {
-    const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
-    if (off < rowb) {
-      const int g = (int)(off / 16u);                  // this lane's group in the row
-      Pairs16 w[NROW];
-      float sc[NROW];
+  StepCursor cc = cursor_at(a, seg, 0);
+  int cli = -1;
+  int c_ng = 0, c_nch = 0, c_xoff = 0, c_soff = 0, c_poff = 0;
+  uint32_t c_rowb = 0;
+  auto consume = [&](const uint4 (&wq)[2], const uint32_t (&sq)[2]) {
+    if (cc.li != cli) {
+      cli = cc.li;
+      const Q4Lin& L = a.lin[cli];
+      c_ng = L.ng;
+      c_nch = L.nch;
+      c_xoff = L.xoff;
+      c_soff = L.soff;
+      c_poff = L.poff;
+      c_rowb = (uint32_t)(L.K / 2);
+    }
+    const uint32_t off = (uint32_t)cc.c * kStepBytes + 16u * (uint32_t)lane;
+    if (off < c_rowb) {
+      const int g = (int)(off / 16u);              // this lane's group in the row
+      Pairs16 w[2];
+      float sc[2];
 #pragma unroll
-      for (int j = 0; j < NROW; ++j) {
-        w[j] = unpack32(wb[j], one);
-        if constexpr (PAIR)      // this lane's group is g; its parity is the lane's
-          sc[j] = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(sb[j] >> (16u * ((uint32_t)lane & 1u))));
+      for (int j = 0; j < 2; ++j) {
+        w[j] = unpack32(wq[j], one);
+        if constexpr (PAIR)    // this lane's group is g; its parity is the lane's
+          sc[j] = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)(sq[j] >> (16u * ((uint32_t)lane & 1u))));
         else
-          sc[j] = 16.0f * (float)sb[j];
+          sc[j] = 16.0f * (float)__builtin_bit_cast(_Float16, (uint16_t)sq[j]);
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         uint4 xv[4];
-        const uint4* xp = xs_l + (size_t)m * (a.K / 8) + 4 * g;
+        const int p0 = c_xoff + m * 4 * c_ng + g;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) xv[t] = xp[t];
-        const float c = gsum[m * ng + g];
+        for (int t = 0; t < 4; ++t) xv[t] = xs_l[p0 + t * c_ng];
+        const float cv = fl[c_soff + m * c_ng + g];
 #pragma unroll
-        for (int j = 0; j < NROW; ++j) acc[j][m] = fmaf(dot32(w[j], xv) - c, sc[j], acc[j][m]);
+        for (int j = 0; j < 2; ++j) acc[j][m] = (dot32(w[j], xv) - cv) * sc[j];
       }
     }
-    if (cc == a.nch - 1 || last) {                     // this wave's part of row cr is done
+    {                                              // the unit's partial sums: one per row and token
       float v = 0.0f;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int j = 0; j < NROW; ++j) {
+        for (int j = 0; j < 2; ++j) {
           const float s = pq::wave_sum(acc[j][m]);
           acc[j][m] = 0.0f;
-          if (lane == m * NROW + j) v = s;
+          if (lane == 2 * m + j) v = s;
         }
-      if (lane < MT * NROW) part[(cr + wv) * MT * NROW + lane] = v;
+      if (lane < 2 * MT) fl[c_poff + (size_t)(cc.p * c_nch + cc.c) * MT * 2 + lane] = v;
     }
-    if (++cc == a.nch) { cc = 0; ++cr; }
+    cc = cursor_next(a, seg, cc);
   };
 
   int base = 0;
-  for (; base + D < nsteps; base += D) {               // steady state: every slot refills
+  for (; base + D < total; base += D) {           // steady state: every slot refills
 #pragma unroll
     for (int q = 0; q < D; ++q) {
-      consume(wbuf[q], sbuf[q], false);
+      consume(wbuf[q], sbuf[q]);
       issue(wbuf[q], sbuf[q]);
     }
   }
 #pragma unroll
-  for (int q = 0; q < D; ++q)                          // drain
-    if (base + q < nsteps) consume(wbuf[q], sbuf[q], base + q == nsteps - 1);
+  for (int q = 0; q < D; ++q)                      // drain
+    if (base + q < total) consume(wbuf[q], sbuf[q]);
   __syncthreads();
 
-  // reduce each row over the waves that covered it, in wave order
-  for (int i = tid; i < nrows * MT; i += kThreads) {
-    const int r = i / MT, m = i - (i / MT) * MT;
-    float g = 0.0f, u = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      const int a0 = pq::split_start(nunits, kWaves, w), a1 = pq::split_start(nunits, kWaves, w + 1);
-      if (a0 < a1 && a0 < (r + 1) * a.nch && a1 > r * a.nch) {
-        g += part[((r + w) * MT + m) * NROW];
-        if (NROW == 2) u += part[((r + w) * MT + m) * NROW + 1];
+  // add each row pair's chunk partials in chunk order
+  for (int li = 0; li < a.n; ++li) {
+    const Q4Lin& L = a.lin[li];
+    const BlockRows br = block_rows(L, G, (int)blockIdx.x);
+    for (int i = tid; i < br.pairs * MT; i += kVThreads) {
+      const int p = i / MT, m = i - (i / MT) * MT;
+      float va = 0.0f, vb = 0.0f;
+      for (int c = 0; c < L.nch; ++c) {
+        const float* part = fl + L.poff + (size_t)(p * L.nch + c) * MT * 2;
+        va += part[2 * m];
+        vb += part[2 * m + 1];
+      }
+      if (L.silu) {
+        L.y[(size_t)m * L.R + br.rs + p] = pq::bf16_rne(silu_mul(va, vb));
+      } else {
+        const int r = br.rs + 2 * p;
+        L.y[(size_t)m * L.N + r] = pq::bf16_rne(va);
+        if (r + 1 < br.re) L.y[(size_t)m * L.N + r + 1] = pq::bf16_rne(vb);
       }
     }
-    a.y[(size_t)m * a.R + r0 + r] = pq::bf16_rne(NROW == 2 ? silu_mul(g, u) : g);
   }
 }
 
@@ -585,46 +768,118 @@ int check_shape(int M, int K, int N, int epi) {
   return PQ_OK;
 }
 
-template <int NROW, int D, int MT, bool PAIR>
-hipError_t launch_m(const Q4Args& a, int num_cus, hipStream_t stream) {
-  auto kern = gemv_q4_kernel<NROW, D, MT, PAIR>;
+// ---- vector path: packing linears into launches ----------------------------
+int blocks_per_cu();
+
+// LDS bytes of one linear in a launch at M tokens with G blocks: x pieces,
+// group offsets and the partials of the block with the most row pairs.
+size_t lin_lds_bytes(int M, int K, int R, int silu, int G) {
+  const size_t rows = ((size_t)R + G - 1) / G;
+  const size_t pairs = silu ? rows : (rows + 1) / 2;
+  const size_t nch = ((size_t)K / 2 + kStepBytes - 1) / kStepBytes;
+  return (size_t)M * K * 2 + (size_t)M * (K / kGroup) * 4 + pairs * nch * M * 2 * 4;
+}
+constexpr size_t kLinSlack = 64 + 16;   // the dummy piece and float, alignment
+// dynamic LDS of the vector kernel: what its static segment table leaves
+constexpr size_t kGroupStaticLds = sizeof(SegEntry) * kVWaves * kMaxLin;
+constexpr size_t kGroupMaxDyn = kMaxLds - (kGroupStaticLds + 255) / 256 * 256;
+
+template <int D, int MT, bool PAIR>
+hipError_t launch_group_m(const Q4Group& a, size_t lds, int grid, hipStream_t stream) {
+  auto kern = gemv_q4_kernel<D, MT, PAIR>;
   static pqhost::KernelAttrOnce attr;
   {
-    hipError_t e = pqhost::set_dynamic_lds_once(attr, (const void*)kern, (int)kMaxLds);
+    hipError_t e = pqhost::set_dynamic_lds_once(attr, (const void*)kern, (int)kGroupMaxDyn);
     if (e != hipSuccess) return e;
   }
-  // Blocks: PQ_BLOCKS_PER_CU per CU (default 1), at most one per row and at
-  // least enough for kRowsCap rows per block.  The grid depends on R and the
-  // device only, so the K split inside a row, and with it every output bit,
-  // is the same for every M.
-  const char* env = getenv("PQ_BLOCKS_PER_CU");
-  const int per_cu = env && atoi(env) > 0 ? atoi(env) : 1;
-  long grid = (long)num_cus * per_cu;
-  if (grid > a.R) grid = a.R;
-  const long need = ((long)a.R + kRowsCap - 1) / kRowsCap;
-  if (grid < need) grid = need;
-  const int rows = (int)((a.R + grid - 1) / grid);
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds_bytes(a.M, a.K, rows, NROW), stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kVThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int NROW, int D, bool PAIR>
-hipError_t launch_p(const Q4Args& a, int num_cus, hipStream_t s) {
-  switch (a.M) {
-    case 1: return launch_m<NROW, D, 1, PAIR>(a, num_cus, s);
-    case 2: return launch_m<NROW, D, 2, PAIR>(a, num_cus, s);
-    case 3: return launch_m<NROW, D, 3, PAIR>(a, num_cus, s);
-    case 4: return launch_m<NROW, D, 4, PAIR>(a, num_cus, s);
-    case 5: return launch_m<NROW, D, 5, PAIR>(a, num_cus, s);
-    case 6: return launch_m<NROW, D, 6, PAIR>(a, num_cus, s);
-    case 7: return launch_m<NROW, D, 7, PAIR>(a, num_cus, s);
-    default: return launch_m<NROW, D, 8, PAIR>(a, num_cus, s);
+template <int D, bool PAIR>
+hipError_t launch_group_p(const Q4Group& a, int M, size_t lds, int grid, hipStream_t s) {
+  switch (M) {
+    case 1: return launch_group_m<D, 1, PAIR>(a, lds, grid, s);
+    case 2: return launch_group_m<D, 2, PAIR>(a, lds, grid, s);
+    case 3: return launch_group_m<D, 3, PAIR>(a, lds, grid, s);
+    case 4: return launch_group_m<D, 4, PAIR>(a, lds, grid, s);
+    case 5: return launch_group_m<D, 5, PAIR>(a, lds, grid, s);
+    case 6: return launch_group_m<D, 6, PAIR>(a, lds, grid, s);
+    case 7: return launch_group_m<D, 7, PAIR>(a, lds, grid, s);
+    default: return launch_group_m<D, 8, PAIR>(a, lds, grid, s);
   }
 }
 
-template <int NROW, int D>
-hipError_t launch(const Q4Args& a, int num_cus, hipStream_t s) {
-  return (a.K / kGroup) % 2 == 0 ? launch_p<NROW, D, true>(a, num_cus, s) : launch_p<NROW, D, false>(a, num_cus, s);
+// Validated linears [0, n) with one M: packed in order into launches of at
+// most kMaxLin linears whose LDS fits one CU and whose groups-per-row parity
+// agrees (the scale-load form).  The grid (PQ_BLOCKS_PER_CU blocks per CU)
+// depends on the device only, so each linear's output bits do not depend on
+// how the list is packed, nor on M.
+int run_vector_group(const pq_q4_linear* lin, int n, int M, int num_cus, hipStream_t stream, int* launches) {
+  const int grid = num_cus * blocks_per_cu();
+  int made = 0;
+  for (int i0 = 0; i0 < n;) {
+    Q4Group g;
+    memset(&g, 0, sizeof(g));
+    const bool pair = (lin[i0].K / kGroup) % 2 == 0;
+    size_t pieces = 0, floats = 0;      // x pieces (16 B) and floats, before the partials
+    size_t xbytes = 0, cbytes = 0, pbytes = 0;
+    int i1 = i0;
+    for (; i1 < n && i1 - i0 < kMaxLin; ++i1) {
+      const pq_q4_linear& L = lin[i1];
+      if (((L.K / kGroup) % 2 == 0) != pair) break;
+      const int silu = L.epi == PQ_EPI_SILU_MUL;
+      const int R = silu ? L.N / 2 : L.N;
+      const size_t x = (size_t)M * L.K * 2, c = (size_t)M * (L.K / kGroup) * 4;
+      const size_t pb = lin_lds_bytes(M, L.K, R, silu, grid) - x - c;
+      if (xbytes + x + cbytes + c + pbytes + pb + kLinSlack > kGroupMaxDyn) break;
+      xbytes += x;
+      cbytes += c;
+      pbytes += pb;
+    }
+    if (i1 == i0) return PQ_ERR_SHAPE;   // one linear alone does not fit
+    // layout: all x pieces, the dummy piece, then floats: group offsets, the dummy float, partials
+    g.n = i1 - i0;
+    for (int i = i0; i < i1; ++i) {
+      const pq_q4_linear& L = lin[i];
+      Q4Lin& q = g.lin[i - i0];
+      q.x = L.x; q.w = L.w; q.wsc = L.w_scale; q.y = L.y;
+      q.K = L.K; q.N = L.N;
+      q.silu = L.epi == PQ_EPI_SILU_MUL;
+      q.R = q.silu ? L.N / 2 : L.N;
+      q.ng = L.K / kGroup;
+      q.nch = (int)((L.K / 2 + kStepBytes - 1) / kStepBytes);
+      q.xoff = (int)pieces;
+      pieces += (size_t)M * L.K / 8;
+    }
+    g.dummy_piece = (int)pieces;
+    floats = (pieces + 1) * 4;
+    for (int i = 0; i < g.n; ++i) {
+      Q4Lin& q = g.lin[i];
+      q.soff = (int)floats;
+      floats += (size_t)M * q.ng;
+    }
+    g.dummy_float = (int)floats++;
+    for (int i = 0; i < g.n; ++i) {
+      Q4Lin& q = g.lin[i];
+      q.poff = (int)floats;
+      floats += lin_lds_bytes(M, q.K, q.R, q.silu, grid) / 4 - (size_t)M * q.K / 2 - (size_t)M * q.ng;
+    }
+    const size_t lds = floats * 4;
+    if (lds > kGroupMaxDyn) return PQ_ERR_SHAPE;
+    // ring depth: 2 steps of two 1 KB row chunks in flight per wave (64 KB
+    // per CU; 3 steps spill at 1024 threads)
+    hipError_t e = pair ? launch_group_p<2, true>(g, M, lds, grid, stream)
+                        : launch_group_p<2, false>(g, M, lds, grid, stream);
+    if (e != hipSuccess) {
+      pqhost::set_last_hip_error((int)e);
+      return PQ_ERR_HIP;
+    }
+    ++made;
+    i0 = i1;
+  }
+  if (launches) *launches = made;
+  return PQ_OK;
 }
 
 // ---- MFMA path -----------------------------------------------------------
@@ -732,23 +987,36 @@ int pq_gemv_q4(const uint16_t* x, int M, int K, const uint8_t* w, const uint16_t
     e = epi == PQ_EPI_SILU_MUL ? launch_mfma<2, 2>(a, grid, (hipStream_t)stream)
                                : launch_mfma<1, 3>(a, grid, (hipStream_t)stream);
   } else {
-    Q4Args a;
-    a.x = x; a.w = w; a.wsc = w_scale; a.y = y;
-    a.M = M; a.K = K; a.N = N;
-    a.R = R;
-    a.nch = (K / 2 + pq::kChunk - 1) / pq::kChunk;
-    // ring depths (1 KB chunks per row in flight per wave): 3 with two rows
-    // per chunk step, 4 with one; deeper rings were slower on every dense-stack
-    // layer (5120x5120 M=1: 6.8 us at 4, 7.6 at 6, 8.6 at 16; 17408->5120: 13.2,
-    // 13.4, 16.5; SiLU*up 5120->2x17408: 21.8 us at 3, 22.2 at 4, 24.3 at 8)
-    e = epi == PQ_EPI_SILU_MUL ? launch<2, 3>(a, dev.num_cus, (hipStream_t)stream)
-                               : launch<1, 4>(a, dev.num_cus, (hipStream_t)stream);
+    pq_q4_linear one;
+    one.x = x; one.w = w; one.w_scale = w_scale; one.y = y;
+    one.K = K; one.N = N; one.epi = epi;
+    return run_vector_group(&one, 1, M, dev.num_cus, (hipStream_t)stream, nullptr);
   }
   if (e != hipSuccess) {
     pqhost::set_last_hip_error((int)e);
     return PQ_ERR_HIP;
   }
   return PQ_OK;
+}
+
+int pq_gemv_q4_group(const pq_q4_linear* linears, int n, int M, int* launches, void* stream) {
+  if (launches) *launches = 0;
+  if (n < 0) return PQ_ERR_SHAPE;
+  if (n > 0 && !linears) return PQ_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const pq_q4_linear& L = linears[i];
+    if (!L.x || !L.w || !L.w_scale || !L.y) return PQ_ERR_NULL;
+    const int st = check_shape(M, L.K, L.N, L.epi);
+    if (st != PQ_OK) return st;
+    if (!pqhost::aligned16(L.x) || !pqhost::aligned16(L.w) || !pqhost::aligned16(L.w_scale) ||
+        !pqhost::aligned16(L.y))
+      return PQ_ERR_ALIGN;
+  }
+  if (n == 0) return PQ_OK;
+  pqhost::DeviceInfo dev;
+  const int st = pqhost::current_device_info(&dev);
+  if (st != PQ_OK) return st;
+  return run_vector_group(linears, n, M, dev.num_cus, (hipStream_t)stream, launches);
 }
 
 }  // extern "C"

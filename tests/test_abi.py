@@ -192,3 +192,26 @@ def test_moe_noalloc_host_validation(lib):
     # the bench's shapes fit
     assert lib.moe_decode_layer_workspace(8, 6144, 2048, 256, 8) <= 4 << 20
     assert g(*a(M=8, H=6144, I=2048, E=256, k=8)) in (PQ_OK, PQ_ERR_UNSUPPORTED, -6)
+
+
+def test_gemv_q4_group_host_validation(lib):
+    from quantized_moe_weight_amd._lib import Q4Linear
+    g = lib.pq_gemv_q4_group
+    n = ctypes.c_int(-1)
+
+    def arr(*items):
+        a = (Q4Linear * len(items))()
+        for i, it in enumerate(items):
+            a[i] = Q4Linear(*it)
+        return a
+    good = (1 << 20, 1 << 20, 1 << 20, 1 << 20, 512, 256, 0)
+    assert g(NUL, 0, 1, ctypes.byref(n), NUL) == PQ_OK and n.value == 0     # nothing to do
+    assert g(NUL, 2, 1, ctypes.byref(n), NUL) == PQ_ERR_NULL
+    assert g(arr(good), -1, 1, NUL, NUL) == PQ_ERR_SHAPE
+    assert g(arr(good, (0, 1 << 20, 1 << 20, 1 << 20, 512, 256, 0)), 2, 1, NUL, NUL) == PQ_ERR_NULL
+    assert g(arr(good, (1 << 20, 1 << 20, 1 << 20, 1 << 20, 500, 256, 0)), 2, 1, NUL, NUL) == PQ_ERR_SHAPE
+    assert g(arr(good, (1 << 20, 1 << 20, 1 << 20, 1 << 20, 512, 255, 1)), 2, 1, NUL, NUL) == PQ_ERR_SHAPE
+    assert g(arr(good), 1, 9, NUL, NUL) == PQ_ERR_SHAPE
+    assert g(arr(good, ((1 << 20) + 8, 1 << 20, 1 << 20, 1 << 20, 512, 256, 0)), 2, 1, NUL, NUL) == PQ_ERR_ALIGN
+    st = g(arr(good, good), 2, 1, ctypes.byref(n), NUL)
+    assert st in (PQ_OK, PQ_ERR_UNSUPPORTED, -6)

@@ -249,3 +249,116 @@ def test_gemv_q4_bad_shapes(pq, M, K, N, epi):
     with pytest.raises(pq.PqError) as e:
         pq.gemv_q4(x, w, s, epi=epi)
     assert e.value.status == -2
+
+
+# ---------------------------------------------------------------------------
+# pq_gemv_q4_group: several independent linears in as few launches as LDS allows
+# ---------------------------------------------------------------------------
+
+GROUP_SPECS = [(5120, 640, 0), (2080, 2 * 100, 1), (1024, 37, 0), (96, 2 * 9, 1), (4096, 300, 0),
+               (512, 4000, 0), (2048, 2 * 513, 1)]     # K / 32 odd for 2080 and 96: the 16-bit scale form
+
+
+def _group_case(pq, M, specs, seed):
+    items, refs = [], []
+    for i, (K, N, epi) in enumerate(specs):
+        x, xt = _x(M, K, seed + i)
+        w = workloads.master_weights(N, K, workload=workloads.Q4_STACK, seed=seed + i)
+        p, s, pg, sg = _q4_on_gpu(pq, w)
+        items.append((xt, pg, sg, epi))
+        refs.append((x, p, s, epi))
+    return items, refs
+
+
+def _check_q4(y, x, p, s, epi, what):
+    yo, So = oracle.gemv_q4(x, p, s)
+    if epi:
+        I = yo.shape[1] // 2
+        h = oracle.silu_mul(yo, I)
+        assert_silu_close(bf16_to_np(y), h, yo[:, :I], yo[:, I:], So[:, :I], So[:, I:], what)
+    else:
+        assert_gemv_close(bf16_to_np(y), yo, So, what)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_gemv_q4_group_equals_single_calls(pq, M):
+    """One grouped call over linears of mixed shapes, epilogues and scale forms:
+    every output is bitwise equal to its own pq_gemv_q4 call on the vector
+    kernel (a linear's split does not depend on the other linears), and
+    within the oracle's bound."""
+    import torch
+    specs = GROUP_SPECS if M < 8 else GROUP_SPECS[:4]
+    items, refs = _group_case(pq, M, specs, seed=500 + M)
+    ys, launches = pq.gemv_q4_group(items)
+    assert 2 <= launches <= len(items)          # the two scale forms never share a launch
+    with env("PQ_Q4_PATH", "valu"):
+        for i, ((xt, pg, sg, epi), y) in enumerate(zip(items, ys)):
+            y1 = pq.gemv_q4(xt, pg, sg, epi=epi)
+            assert torch.equal(y1.view(torch.int16), y.view(torch.int16)), f"linear {i}: grouped != single call"
+    for i, (y, (x, p, s, epi)) in enumerate(zip(ys, refs)):
+        _check_q4(y, x, p, s, epi, f"group M={M} linear {i}")
+
+
+def test_gemv_q4_group_rows_bitwise_independent_of_M(pq):
+    import torch
+    M = 5
+    specs = [(5120, 320, 0), (2048, 2 * 200, 1), (8704, 64, 0)]
+    items, _ = _group_case(pq, M, specs, seed=600)
+    ys, _ = pq.gemv_q4_group(items)
+    for m in range(M):
+        one, _ = pq.gemv_q4_group([(xt[m:m + 1].contiguous(), pg, sg, epi) for xt, pg, sg, epi in items])
+        for y, y1 in zip(ys, one):
+            assert torch.equal(y1[0].view(torch.int16), y[m].view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_gemv_q4_group_dense_stack_blocks(pq, M):
+    """Two blocks of the 4-bit dense decode stack (5120->5120, 5120->2x17408
+    with SiLU*up, 17408->5120) at full size in one grouped call, as the
+    benchmark issues them: each output bitwise equal to the linear's single
+    vector-kernel call, sampled rows against the oracle."""
+    import torch
+    items, meta = [], []
+    for blk in range(2):
+        for layer, (K, N, silu) in enumerate(workloads.Q4_SHAPES):
+            seed = 70 + 3 * blk + layer
+            x, xt = _x(M, K, seed)
+            wt = workloads.master_weights_torch(N, K, workload=workloads.Q4_STACK, tensor=workloads.T_W,
+                                                expert=3 * blk + layer, seed=seed, device="cuda")
+            pg, sg = pq.quantize_q4(wt)
+            epi = pq.EPI_SILU_MUL if silu else pq.EPI_NONE
+            items.append((xt, pg, sg, epi))
+            meta.append((x, wt, pg, sg, K, N, silu, seed))
+    ys, launches = pq.gemv_q4_group(items)
+    print(f"dense stack, 2 blocks, M={M}: {launches} launches for {len(items)} linears")
+    with env("PQ_Q4_PATH", "valu"):
+        for (xt, pg, sg, epi), y in zip(items, ys):
+            assert torch.equal(pq.gemv_q4(xt, pg, sg, epi=epi).view(torch.int16), y.view(torch.int16))
+    for y, (x, wt, pg, sg, K, N, silu, seed) in zip(ys, meta):
+        R = N // 2 if silu else N
+        rows = _sample(R, 96, seed)
+        want_rows = np.concatenate([rows, rows + R]) if silu else rows
+        idx = torch.from_numpy(want_rows).cuda()
+        p, s = oracle.q4_quant(wt[idx].cpu().numpy())
+        assert np.array_equal(pg[idx].cpu().numpy(), p)
+        yo, So = oracle.gemv_q4(x, p, s)
+        yy = bf16_to_np(y)
+        if silu:
+            n = len(rows)
+            h = oracle.silu_mul(yo, n)
+            assert_silu_close(yy[:, rows], h, yo[:, :n], yo[:, n:], So[:, :n], So[:, n:], f"stack SiLU M={M}")
+        else:
+            assert_gemv_close(yy[:, rows], yo, So, f"stack {K}->{N} M={M}")
+
+
+def test_gemv_q4_group_rejects_bad_linears(pq):
+    import torch
+    x = torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((4, 32), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.float16, device="cuda")
+    ok = (x, w, s, 0)
+    bad = (x, torch.zeros((5, 32), dtype=torch.uint8, device="cuda"), torch.zeros((5, 2), dtype=torch.float16,
+                                                                                   device="cuda"), 1)
+    with pytest.raises(pq.PqError) as e:
+        pq.gemv_q4_group([ok, bad])                  # odd N under SiLU: nothing is launched
+    assert e.value.status == -2

@@ -264,7 +264,9 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k);
  * refuse the launch with PQ_ERR_HIP).
  * Two kernels implement the call with bitwise equal results: for M <= 2 one
  * that releases the down projection with a grid-wide barrier, for M >= 3 one
- * without (the environment variable PQ_MOE_PATH=barrier|stream forces one).
+ * without (the environment variable PQ_MOE_PATH=barrier|stream forces one;
+ * PQ_MOE_SCALES=step makes the first load every gate_up step's block scales
+ * with its weights instead of once per h row through LDS, with equal bits).
  * The workspace (zeroed once by pq_workspace_init) may be shared with the
  * other entry points; the call leaves its counters and its h exchange region
  * at zero, as it found them. */

@@ -155,6 +155,54 @@ __device__ __forceinline__ float buf_load_f32_nt(rsrc_t r, uint32_t off) {
 }
 
 // ---------------------------------------------------------------------------
+// Buffer-to-LDS loads: lane l's bytes land at LDS byte address lds + l * size,
+// read from byte offset voff + soff of the buffer (voff per lane, soff
+// wave-uniform; a lane whose offset is past the buffer's size loads zeros).
+// They are written as assembly on purpose: the compiler's wait insertion does
+// not know which LDS reads depend on which of these loads and would wait for
+// every one of them before any LDS read.  Callers order them themselves; all
+// vector-memory loads of a wave complete in issue order, so once a load issued
+// after one of these has returned (a wait the compiler inserts for its use),
+// the LDS bytes are in place.
+// ---------------------------------------------------------------------------
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// A raw buffer resource (stride 0, num_records = bytes) as four scalar words.
+__device__ __forceinline__ int32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return int32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
+                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)(lds_ptr)p);
+}
+__device__ __forceinline__ void dma16(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+}
+// dma4 that leaves M0 as it found it (the compiler does not track M0 across
+// inline assembly, so kernels that may keep a value there use this one).
+__device__ __forceinline__ void dma4_keep_m0(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %4 offen lds\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+}
+// Two LDS dwords read once `dep` (a register a vector-memory load wrote) is
+// available: the dependency makes the compiler wait for that load first, so
+// the read sees what earlier buffer-to-LDS loads wrote; the read waits for
+// itself in the same block.
+__device__ __forceinline__ void lds_read2_after(uint32_t a0, uint32_t a1, uint32_t dep, float& v0, float& v1) {
+  asm volatile("ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(v0), "=&v"(v1) : "v"(a0), "v"(a1), "v"(dep));
+}
+
+// ---------------------------------------------------------------------------
 // Wavefront reductions.  wave_sum / wave_max_u32 reduce with DPP row shifts
 // and row broadcasts into lane 63 (a fixed association order, so the result
 // is deterministic) and return lane 63's value to every lane.

@@ -67,7 +67,6 @@ struct Stage {
   float sa[256];
   float sb[BN];
 };
-typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;                    // token tiles per group of the tile order
 static_assert(2 * sizeof(Stage<256>) <= 160 * 1024, "stages must fit LDS");
@@ -88,33 +87,11 @@ __device__ __forceinline__ floatx4 mfma_e4m3(int32x8 a, int32x8 b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
 }
 
-typedef int int32x4 __attribute__((ext_vector_type(4)));
-
-// A raw buffer resource (stride 0, num_records = bytes) as four scalar words,
-// for the buffer-to-LDS loads below.
-__device__ __forceinline__ int32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)base;
-  return int32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32)),
-                 __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(size_t)(lds_ptr)p);
-}
-// Buffer-to-LDS loads (lane l's bytes land at lds + l * size) at byte offset
-// voff + soff of the buffer (voff per lane, soff wave-uniform; a lane whose
-// voff is past the buffer loads zeros).  Written as assembly on purpose: the
-// compiler's wait insertion cannot tell the two stages apart and would wait
-// for the next stage's loads before every read of the current one; the kernel
-// orders these loads itself (each wave waits for its own with vmcnt(0) before
-// the block barrier that precedes their readers).
-__device__ __forceinline__ void dma16(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
-}
+using pq::dma16;
+using pq::dma4;
+using pq::int32x4;
+using pq::lds_addr;
+using pq::rsrc_words;
 
 __device__ __forceinline__ int32x8 join8(uint4 lo, uint4 hi) {
   return int32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};

@@ -68,6 +68,15 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 // instead of a hung GPU.
 constexpr uint32_t kLdsSpinLimit = 1u << 21;
 constexpr int kAuxSC1 = 0x10;            // buffer aux bit: agent-coherent (sc1) access
+// Scale windows of the barrier kernel's gate_up: each wave owns kScWins
+// windows of kWinFloats fp32 block scales in LDS, filled by buffer-to-LDS
+// loads (one load instruction per window) and read at each step instead of
+// two per-step scale loads.  A unit takes two (its gate and up rows), so four
+// units rotate, one more than the ring of BDG steps can hold.
+constexpr int kWinFloats = 64;
+constexpr int kScWins = 8;
+constexpr size_t kScWaveBytes = (size_t)kScWins * kWinFloats * 4;
+static_assert(2 * (BDG + 1) <= kScWins, "a window pair per unit in the ring, plus the unit being taken");
 constexpr int kFlagStride = 32;          // uint32 per release flag: one 128-byte line each
 constexpr uint32_t kReleased = 1u;       // a release flag's value once the down phase may start
 
@@ -102,6 +111,7 @@ struct MoeArgs {
   uint32_t spin_limit;
   int xs_off, ha_off, hs_off, yb_off;   // byte offsets of the LDS regions
   int alias;        // h codes and scales reuse the x region
+  int sc_off;       // barrier kernel: LDS byte offset of the per-wave scale windows, or -1
 };
 
 struct Route {
@@ -702,14 +712,23 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   };
   if (!router) know_routes();         // the routes are visible already
 
+  // Block scales: with the LDS windows (sc_off >= 0) a unit's gate and up
+  // rows' scales arrive by one buffer-to-LDS load each when the unit is
+  // taken (before its weight loads, so they have landed once the step's
+  // weights have) and each step reads its 8 from LDS; otherwise each step
+  // loads them with its weights.
+  const bool scw = a.sc_off >= 0;
+  const uint32_t wbase = scw ? pq::lds_addr(smem + a.sc_off + (size_t)wv * kScWaveBytes) : 0u;
   uint4 wb[BDG][2];
   float sb[BDG][2];
+  uint32_t sa[BDG];                   // LDS address of the step's gate-row scales (windows)
   int su[BDG], sch[BDG];              // unit (-1: none) and chunk of each slot
   int iunit = -1, ic = nchH;          // issue cursor
   bool more = true;
-  int cur_e = -1;
+  int cur_e = -1, gseq = 0;
   pq::rsrc_t gwr = pq::make_rsrc(a.w13, 0u), gsr = pq::make_rsrc(a.s13, 0u);
-  auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], int& su_q, int& sch_q) {
+  pq::int32x4 gsr4 = {0, 0, 0, 0};
+  auto issue_gu = [&](uint4 (&w)[2], float (&s)[2], uint32_t& sa_q, int& su_q, int& sch_q) {
     if (ic == nchH && more) {       // take the block's next unit
       const int c = wave_claim(&s_next);
       if (c < nsh) {
@@ -727,6 +746,16 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
           cur_e = e;
           gwr = pq::make_rsrc(gu_weights<EXT>(a, e), (uint32_t)(2 * I * H));
           gsr = pq::make_rsrc(gu_scales<EXT>(a, e), (uint32_t)(2 * I * nbH * 4));
+          if (scw) gsr4 = pq::rsrc_words(gu_scales<EXT>(a, e), (uint32_t)(2 * I * nbH * 4));
+        }
+        if (scw) {                     // the unit's two scale rows into windows 2g, 2g + 1
+          gseq = (gseq + 1) & 3;
+          const uint32_t ii0 = (uint32_t)(iunit - (iunit / I) * I);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            pq::dma4_keep_m0(gsr4, wbase + (uint32_t)((2 * gseq + j) * kWinFloats * 4),
+                             lane < nbH ? ((ii0 + (uint32_t)(j * I)) * (uint32_t)nbH + (uint32_t)lane) * 4u : pq::kOOB,
+                             0u);
         }
       }
     }
@@ -737,14 +766,16 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     for (int j = 0; j < 2; ++j) {
       const uint32_t row = ii + (uint32_t)(j * I);
       w[j] = pq::buf_load16_nt(gwr, ok ? row * (uint32_t)H + kc + lane16 : pq::kOOB);
-      s[j] = pq::buf_load_f32_nt(gsr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+      s[j] = scw ? 0.0f
+                 : pq::buf_load_f32_nt(gsr, ok ? (row * (uint32_t)nbH + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
     }
+    sa_q = wbase + (uint32_t)((2 * gseq * kWinFloats + ic * (pq::kChunk / pq::kBlock)) * 4);
     su_q = more ? iunit : -1;
     sch_q = ic;
     if (more) ++ic;
   };
 #pragma unroll
-  for (int q = 0; q < BDG; ++q) issue_gu(wb[q], sb[q], su[q], sch[q]);
+  for (int q = 0; q < BDG; ++q) issue_gu(wb[q], sb[q], sa[q], su[q], sch[q]);
 
 
   {
@@ -771,6 +802,9 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
           if (uu != pairs_u) load_pairs(uu);
           const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
           if (off < (uint32_t)H) {
+            float sg = sb[q][0], sv = sb[q][1];
+            if (scw)
+              pq::lds_read2_after(sa[q] + lane_blk4, sa[q] + kWinFloats * 4 + lane_blk4, wb[q][0].x, sg, sv);
             const pq::Bf16x16 wg = pq::widen16(wb[q][0]);
             const pq::Bf16x16 wu = pq::widen16(wb[q][1]);
 #pragma unroll
@@ -778,8 +812,8 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
               if (t < cnp) {
                 const pq::Bf16x16 xv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pm[t] * H + off));
                 const float xs = acts[pm[t] * nbH + off / pq::kBlock];
-                accg[t] = fmaf(pq::dot16(wg, xv), sb[q][0] * xs, accg[t]);
-                accu[t] = fmaf(pq::dot16(wu, xv), sb[q][1] * xs, accu[t]);
+                accg[t] = fmaf(pq::dot16(wg, xv), sg * xs, accg[t]);
+                accu[t] = fmaf(pq::dot16(wu, xv), sv * xs, accu[t]);
               }
             }
           }
@@ -799,7 +833,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
             }
           }
         }
-        issue_gu(wb[q], sb[q], su[q], sch[q]);
+        issue_gu(wb[q], sb[q], sa[q], su[q], sch[q]);
       }
       bool busy = false;
 #pragma unroll
@@ -843,6 +877,9 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   const int v1 = ufl(pq::split_start(bunits, kWaves, wv + 1));
   const int dsteps = (v1 - v0) * nchI;
   float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);   // [row_local][P] fp32
+  // (the down steps keep their per-step scale loads: a down step does half
+  // a gate_up step's work, and an LDS read in its dependency chain measured
+  // slower than the load that arrives with the weights)
   uint4 wd[BDD];
   float sd[BDD];
   int ju = nrows > 0 ? v0 / nrows : 0;
@@ -1355,7 +1392,7 @@ constexpr size_t kLdsBytes = 160 * 1024;
 
 struct MoePlan {
   size_t lds;
-  int xs_off, ha_off, hs_off, yb_off, alias;
+  int xs_off, ha_off, hs_off, yb_off, alias, sc_off;
   size_t off_h, ws_total;
 };
 
@@ -1396,6 +1433,7 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePl
   p->lds = 0;
   p->xs_off = (int)xb;
   p->alias = 0;
+  p->sc_off = -1;
   if (num_cus > 0) {
     const size_t yb = ((size_t)H + num_cus - 1) / num_cus * P * 4;
     const size_t sep = xb + xsb + hb + hsb + yb;
@@ -1413,6 +1451,13 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePl
       p->yb_off = (int)(cb + sb);
       p->lds = cb + sb + yb;
       if (p->lds + kStaticLds > kLdsBytes) return PQ_ERR_SHAPE;
+    }
+    // the barrier kernel's scale windows, where they fit
+    const size_t sco = pqhost::align_up(p->lds, 16);
+    if (path != kPathStream && H / pq::kBlock <= kWinFloats &&
+        sco + kScWaveBytes * kWaves + kStaticLds <= kLdsBytes) {
+      p->sc_off = (int)sco;
+      p->lds = sco + kScWaveBytes * kWaves;
     }
   }
   p->off_h = path == kPathStream ? pq::kWsZeroOff : pq::kWsDataOff;
@@ -1573,6 +1618,9 @@ int layer_call(const uint16_t* x, int M, int H, const uint16_t* router_w, float*
   a.spin_limit = kSpinLimit;
   a.xs_off = pl.xs_off; a.ha_off = pl.ha_off; a.hs_off = pl.hs_off; a.yb_off = pl.yb_off;
   a.alias = pl.alias;
+  a.sc_off = pl.sc_off;
+  const char* sce = getenv("PQ_MOE_SCALES");          // "step": per-step scale loads (for tests)
+  if (sce && strcmp(sce, "step") == 0) a.sc_off = -1;
   const char* lim = getenv("PQ_SPIN_LIMIT");
   if (lim && *lim) a.spin_limit = (uint32_t)strtoul(lim, nullptr, 10);
 

@@ -233,6 +233,52 @@ def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M):
     assert torch.equal(a["hq"], b["hq"]) and torch.equal(a["hs"], b["hs"])
 
 
+@pytest.mark.parametrize("M,E,H,I,k,shared", [(1, 16, 1024, 512, 4, False), (2, 16, 640, 384, 4, True),
+                                                (1, 256, 6144, 2048, 8, False)])
+def test_moe_scale_windows_match_step_loads(pq, M, E, H, I, k, shared):
+    """The barrier kernel's gate_up reads its block scales from per-wave LDS
+    windows (filled once per h row by buffer-to-LDS loads); with
+    PQ_MOE_SCALES=step it loads them with every step's weights instead.  The
+    products and their order are the same, so the results are bitwise equal:
+    one chunk per row (four rows rotating through the windows), a ragged
+    chunk with a shared expert, and the full-size layer."""
+    import torch
+    cfg = pq.moe_layer_config(M, H, I, E, k, shared=shared)
+    assert cfg["kernel"] == "barrier" and cfg["lds_bytes"] >= 16 * 2048, cfg     # the windows are laid out
+    wl = workloads.MOE_LAYER
+    bank = Bank(pq, E, H, I, workload=wl, seed=0 if H == 6144 else 40 + M)
+    x = workloads.activation_bf16(M, H, workload=wl, seed=40 + M)
+    lg = (workloads.router_logits(1, E, workload=wl) if H == 6144
+          else workloads.verify_logits(M, E, workload=wl, seed=40 + M))
+    ids, _ = oracle.route_topk(lg, k)
+    bank.fill(ids)
+    sh = bank.shared() if shared else None
+    xt, lt = np_bf16_bits_to_torch(x), torch.from_numpy(lg).cuda()
+    res = {}
+    old = os.environ.get("PQ_MOE_SCALES")
+    try:
+        for mode in ("windows", "step"):
+            if mode == "step":
+                os.environ["PQ_MOE_SCALES"] = "step"
+            res[mode] = pq.moe_decode_layer(xt, bank.w13, bank.s13, bank.w2, bank.s2, logits=lt, top_k=k,
+                                            shared=sh, debug=True)
+            assert pq.workspace_check() == 0
+    finally:
+        if old is None:
+            os.environ.pop("PQ_MOE_SCALES", None)
+        else:
+            os.environ["PQ_MOE_SCALES"] = old
+    a, b = res["windows"], res["step"]
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+    assert torch.equal(a["h"].view(torch.int16), b["h"].view(torch.int16))
+    if shared:
+        assert torch.equal(a["sh_h"].view(torch.int16), b["sh_h"].view(torch.int16))
+    ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k, shared=bank.sh_cpu if shared else None)
+    _check(pq, bank, x, a, ref, M, k)
+    if shared:
+        _check_shared(a, ref)
+
+
 def test_moe_deterministic_and_workspace_reuse(pq):
     """Repeated calls are bitwise identical, also interleaved with calls of other
     shapes on the same workspace (counters and the h exchange region must be

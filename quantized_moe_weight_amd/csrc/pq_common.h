@@ -186,12 +186,19 @@ __device__ __forceinline__ void dma4(int32x4 r, uint32_t lds, uint32_t voff, uin
                :: "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 // dma4 that leaves M0 as it found it (the compiler does not track M0 across
-// inline assembly, so kernels that may keep a value there use this one).
+// inline assembly, so kernels that may keep a value there use this one).  The
+// scalar operands pass through readfirstlane (they are wave-uniform; this
+// keeps them in scalar registers where the compiler cannot prove it).
 __device__ __forceinline__ void dma4_keep_m0(int32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
   uint32_t saved;
+  const int32x4 rs = {__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                      __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, %4 offen lds\n\t"
                "s_mov_b32 m0, %0"
-               : "=&s"(saved) : "s"(lds), "v"(voff), "s"(r), "s"(soff) : "memory");
+               : "=&s"(saved)
+               : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds)), "v"(voff), "s"(rs),
+                 "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)soff))
+               : "memory");
 }
 // Two LDS dwords read once `dep` (a register a vector-memory load wrote) is
 // available: the dependency makes the compiler wait for that load first, so

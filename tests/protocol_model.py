@@ -29,8 +29,9 @@ Stream kernel (three tokens or more):
     polls the pair's h (every unit of that entry, whichever block owns it)
     and counts the entry staged; with aliased LDS it first waits until no wave
     of the block is still in gate_up;
-  * then it claims down units (entry, row) from a third counter and, before
-    consuming one, waits until its entry is fully staged;
+  * then it claims down units (entry, row), four consecutive ones per claim,
+    from a third counter and, before consuming one, waits until its entry is
+    fully staged;
   * the last block to exit clears h and the exit counter.
 """
 from __future__ import annotations
@@ -148,6 +149,9 @@ def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, cle
 # stream kernel
 # ---------------------------------------------------------------------------
 
+DN_CLAIM = 4     # down units per claim in the stream kernel
+
+
 def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: bool, limit: int, log: dict):
     """Waves of block b of the stream kernel.  nU union entries of I h-rows
     each; unp[u] pairs routed to entry u; the block's down rows are one row
@@ -187,17 +191,21 @@ def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: 
                 log["staged"].append((b, u, t))
             lds["staged"][u] += 1
             yield
-        # down units: one per entry; consumed once the entry is staged
-        while True:
-            d = lds["dnext"]
+        # down units: one per entry, claimed kDnClaim at a time; each consumed
+        # once its entry is staged
+        done_claims = False
+        while not done_claims:
+            c = lds["dnext"]
             lds["dnext"] += 1
             yield
-            if d >= nU:
-                break
-            ok = yield from wait_until(lambda: lds["staged"][d] >= unp[d], grid, limit)
-            if ok and not all(grid.get(("h", d * I + i)) for i in range(I)):
-                log["early_release"].append((b, d))
-            yield
+            for d in range(DN_CLAIM * c, DN_CLAIM * c + DN_CLAIM):
+                if d >= nU:
+                    done_claims = True
+                    break
+                ok = yield from wait_until(lambda: lds["staged"][d] >= unp[d], grid, limit)
+                if ok and not all(grid.get(("h", d * I + i)) for i in range(I)):
+                    log["early_release"].append((b, d))
+                yield
         exits["n"] += 1
         yield from wait_until(lambda: exits["n"] == W, grid, 10 ** 9)
         if w == 0:

@@ -263,8 +263,10 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k);
  * PQ_MOE_LAUNCH=cooperative, which makes the runtime guarantee co-residency or
  * refuse the launch with PQ_ERR_HIP).
  * Two kernels implement the call with bitwise equal results: for M <= 2 one
- * that releases the down projection with a grid-wide barrier, for M >= 3 one
- * without (the environment variable PQ_MOE_PATH=barrier|stream forces one;
+ * whose blocks start the down projection once every h row of the call is
+ * there (a grid-wide barrier on the h values themselves), for M >= 3 one that
+ * starts each union entry's down rows once that entry's h is there (the
+ * environment variable PQ_MOE_PATH=barrier|stream forces one;
  * PQ_MOE_SCALES=step makes the first load every gate_up step's block scales
  * with its weights instead of once per h row through LDS, with equal bits).
  * The workspace (zeroed once by pq_workspace_init) may be shared with the
@@ -282,10 +284,11 @@ int moe_decode_layer(const uint16_t* x, int M, int H,
 
 /* Which kernel and LDS layout moe_decode_layer / moe_decode_layer_ex use for
  * a call of this shape on the current device (the same rule, including the
- * PQ_MOE_PATH override): *kernel = 0 for the kernel with a grid-wide release
+ * PQ_MOE_PATH override): *kernel = 0 for the kernel with a grid-wide barrier
  * before the down projection, 1 for the one without; *alias = 1 when the
  * re-quantised h reuses the LDS region of the quantised x (always in kernel 0,
- * which stages h after its release; in kernel 1 when x, h and the output
+ * which stages h once every wave of the block is past gate_up; in kernel 1
+ * when x, h and the output
  * partials do not fit side by side, and h is then staged only once every
  * wave of the block is past gate_up);
  * *lds_bytes = the dynamic LDS per block.  shared: 1 with a shared expert.

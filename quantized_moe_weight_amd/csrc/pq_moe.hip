@@ -20,16 +20,16 @@
 //      loads are in flight.
 //   C. gate_up units (union entry u, h-row i): each wave streams a contiguous
 //      range of units (gate row + up row, one 1 KB chunk per lane-step, a ring
-//      of DG steps in flight) and stores h = silu(g)*u (bf16) for every token
-//      routed to u, then adds its row count to the phase counter.
+//      of DG steps in flight) and stores h = silu(g)*u (bf16, bit-inverted into
+//      a region that is zero between calls) for every token routed to u.
 //   D. down units (output row n, all union entries): waves issue their first
-//      down weight loads, the block waits for the phase counter to reach every
-//      h row, quantises h of every (token, slot) pair into LDS (each block
-//      derives the same codes from the same values) and streams its rows; per
-//      row each (token, slot) partial is reduced across the wave and each
-//      token's slots are combined in slot order.
-//   E. the last block to finish resets the counters it used, so the workspace
-//      is ready for the next call without a clearing launch.
+//      down weight loads, then quantise h of every (token, slot) pair into LDS
+//      as its values arrive (a zero word is a value not yet written; each
+//      block derives the same codes from the same values) and stream their
+//      rows; per row each (token, slot) partial is reduced across the wave and
+//      each token's slots are combined in slot order.
+//   E. the last block to finish clears h and resets the counter it used, so
+//      the workspace is ready for the next call without a clearing launch.
 //
 // Cross-block data (h and the counters) travels through the
 // agent-coherent (sc1) path: no L2 writeback or invalidate is needed.
@@ -78,8 +78,6 @@ constexpr int kWinFloats = 64;
 constexpr int kScWins = 8;
 constexpr size_t kScWaveBytes = (size_t)kScWins * kWinFloats * 4;
 static_assert(2 * (BDG + 1) <= kScWins, "a window pair per unit in the ring, plus the unit being taken");
-constexpr int kFlagStride = 32;          // uint32 per release flag: one 128-byte line each
-constexpr uint32_t kReleased = 1u;       // a release flag's value once the down phase may start
 
 struct MoeArgs {
   const uint16_t* x;
@@ -644,10 +642,11 @@ __device__ __forceinline__ void wait_routes(const uint32_t* s_ready, pq::WsHeade
   lds_wait(s_ready, [](uint32_t v) { return v != 0u; }, hdr);
 }
 
-// The barrier kernel: all gate_up units of the call, then one grid-wide
-// release, then every block stages all of h and runs its down rows.  Fewer
-// instructions per step than the stream kernel below, which pays off when the
-// call streams few experts (one or two tokens).
+// The barrier kernel: all gate_up units of the call, then every block stages
+// all of h (waiting for the rows of slower blocks value by value: a barrier on
+// the data itself) and runs its down rows.  Fewer instructions per step than
+// the stream kernel below, which pays off when the call streams few experts
+// (one or two tokens).
 // TP: compile-time bound on the (token, slot) pairs routed to one expert in a
 // call (the smallest power of two >= M), so the per-pair loops unroll tightly.
 template <int TP, bool EXT>
@@ -657,12 +656,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   __shared__ int s_last;
   __shared__ uint32_t s_tmask[kMaxM][kMaxE / 32];   // routed-expert bitmap of each token
   __shared__ uint32_t s_next;     // next gate_up unit of this block
-  __shared__ uint32_t s_arrive;   // waves of this block done with gate_up
   __shared__ uint32_t s_ready;    // routes visible (set by the routing waves)
   __shared__ uint32_t s_rdone;    // routing waves done
 
   pq::WsHeader* hdr = reinterpret_cast<pq::WsHeader*>(a.ws);
-  uint32_t* flags = reinterpret_cast<uint32_t*>(a.ws + pq::kWsCounterOff);   // one line per block
 
   const int lane = pq::lane_id();
   const int wv = pq::wave_id();
@@ -684,7 +681,6 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
 
   if (threadIdx.x == 0) {       // block counters; first used after the barriers below
     s_next = 0u;
-    s_arrive = 0u;
   }
   layer_prologue<TP, EXT>(a, route, s_tmask, &s_ready, &s_rdone, act, acts, hdr);
 
@@ -825,8 +821,9 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
                 const float g = pq::wave_sum(accg[t]);
                 const float u = pq::wave_sum(accu[t]);
                 if (lane == 0) {
-                  const uint16_t hb = pq::bf16_rne(silu_mul(g, u));
-                  pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + ci, hb);
+                  uint16_t hb = pq::bf16_rne(silu_mul(g, u));
+                  if (hb == 0xFFFFu) hb = 0xFFC0u;         // keep the inverted word non-zero
+                  pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + ci, (uint16_t)~hb);
                   if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + ci] = hb;
                 }
               }
@@ -843,26 +840,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     }
   }
 
-  // Count the finished h rows: each wave's stores complete (sc1) before it
-  // arrives; the last wave of the block to arrive adds the block's rows to
-  // the phase counter (one device atomic per block: they serialise on one
-  // address).
-  // The block that completes the count releases every block through its own
-  // flag line (set to kReleased; the last block to exit clears every line, so
-  // the flags are zero between calls like the other counters of the region).
-  pq::wait_vm();
   know_routes();                      // (every wave's last claim already waited)
-  const int gu_units = nU * I;
-  uint32_t last = 0;
-  if (lane == 0) {
-    const uint32_t before = atomicAdd(&s_arrive, 1u);
-    const uint32_t rows = (uint32_t)(nsh + bu1 - bu0);
-    if (before == (uint32_t)(kWaves - 1) && rows > 0u)
-      last = pq::atomic_add_relaxed(&hdr->done, rows) + rows == (uint32_t)gu_units;
-  }
-  if (__builtin_amdgcn_readlane((int)last, 0)) {
-    for (int b = lane; b < (int)gridDim.x; b += pq::kWave) pq::st_agent_u32(flags + (size_t)b * kFlagStride, kReleased);
-  }
 
   // ---- D. down projection + weighted combine --------------------------------
   // Output rows are dealt to blocks as evenly as possible; inside a block the
@@ -911,10 +889,14 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
 #pragma unroll
   for (int q = 0; q < BDD; ++q) issue_dn(wd[q], sd[q]);
 
-  // wait for every h row of the call, then quantise h into LDS: every block
-  // derives the same codes and scales from the same values (block 0 also
-  // writes them out when asked)
-  if (threadIdx.x == 0) pq::spin_wait_eq(flags + (size_t)blockIdx.x * kFlagStride, kReleased, hdr, a.spin_limit);
+  // Every h row of the call, quantised into LDS as soon as it is there: h
+  // is stored bit-inverted into a region that is zero between calls, so a
+  // zero word is a value not yet written.  The h codes overwrite the x codes,
+  // so the block first waits for all its waves to be past gate_up; then each
+  // wave polls its share (only the vectors still missing are loaded again)
+  // while the last gate_up units of slower blocks finish.  Every block derives
+  // the same codes and scales from the same values (block 0 also writes them
+  // out when asked).
   __syncthreads();
   {
     // 8 values per lane, 16 lanes per 128-value block (the layout of the
@@ -924,16 +906,37 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     constexpr int kBatch = 2;
     for (int t0 = 0; t0 < nvec; t0 += kBatch * kThreads) {
       uint4 raw[kBatch];
+      bool have[kBatch];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
-        const int t = t0 + i * kThreads + (int)threadIdx.x;
-        raw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            hr, (int)(t < nvec ? (uint32_t)t * 16u : pq::kOOB), 0, kAuxSC1));
+        have[i] = t0 + i * kThreads + (int)threadIdx.x >= nvec;
+        raw[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      for (uint32_t it = 0;; ++it) {
+        bool miss = false;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int t = t0 + i * kThreads + (int)threadIdx.x;
+          const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+              hr, (int)(have[i] ? pq::kOOB : (uint32_t)t * 16u), 0, kAuxSC1));
+          if (!have[i]) {
+            raw[i] = r;
+            have[i] = !(has_zero_half(r.x) || has_zero_half(r.y) || has_zero_half(r.z) || has_zero_half(r.w));
+          }
+          miss |= !have[i];
+        }
+        if (__ballot(miss) == 0ull) break;
+        if (it >= a.spin_limit) {
+          if (lane == 0) pq::record_error(hdr, PQ_ERR_TIMEOUT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) {
         const int t = t0 + i * kThreads + (int)threadIdx.x;
         const bool valid = t < nvec;
+        raw[i] = make_uint4(~raw[i].x, ~raw[i].y, ~raw[i].z, ~raw[i].w);
         float v[8];
         pq::bf16x8_to_f32(raw[i], v);
         const float sc = pq::fp8_block_scale16(v, valid);
@@ -1019,10 +1022,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     a.out[(size_t)m * H + r0 + rl] = pq::bf16_rne(o);
   }
 
-  // ---- E. the last block resets the counters and flags of this call ---------
-  // Every block has passed its flag wait when it counts itself out, and the
-  // releasing block's flag stores are complete (wait_vm) before it does, so
-  // the clearing stores below are the last writes to the flag lines.
+  // ---- E. the last block to finish clears h for the next call ----------------
+  // A block counts itself out once it has read every h value (so every h
+  // store of the call has landed) and its own stores are complete: the
+  // clearing stores below are the last writes to h.
   pq::wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1031,11 +1034,13 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   }
   __syncthreads();
   if (s_last) {
+    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P2 * I * 2));
+    const int nz = P2 * I / 8;
+    for (int t = threadIdx.x; t < nz; t += kThreads)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, hr, t * 16, 0, kAuxSC1);
     if (router)
       for (int t = threadIdx.x; t < a.M * a.E; t += kThreads) pq::st_agent_u32(a.lx + t, 0u);
-    for (int b = threadIdx.x; b < (int)gridDim.x; b += kThreads) pq::st_agent_u32(flags + (size_t)b * kFlagStride, 0u);
     if (threadIdx.x == 0) {
-      pq::atomic_store_relaxed(&hdr->done, 0u);
       pq::atomic_store_relaxed(&hdr->exit_count, 0u);
       report_status(a, hdr);
     }
@@ -1469,7 +1474,7 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePl
       p->lds = sco + kScWaveBytes * kWaves;
     }
   }
-  p->off_h = path == kPathStream ? pq::kWsZeroOff : pq::kWsDataOff;
+  p->off_h = pq::kWsZeroOff;
   p->ws_total = pqhost::align_up(pq::kWsDataOff + Pws * I * 2, 256);
   return PQ_OK;
 }
@@ -1496,7 +1501,6 @@ int launch_moe(const MoeArgs& a, const MoePlan& pl, const pqhost::DeviceInfo& de
   // one block per CU (blocks wait on each other, so all must be resident; one
   // per CU also keeps the per-block staging of h to one copy per CU)
   const int grid = dev.num_cus;
-  if (!STREAM && (size_t)grid * kFlagStride * 4 > pq::kWsZeroOff - pq::kWsCounterOff) return PQ_ERR_UNSUPPORTED;
   if (cooperative_launch()) {
     MoeArgs arg = a;
     void* params[] = {&arg};
@@ -1527,8 +1531,8 @@ int launch_moe_path(int path, const MoeArgs& a, const MoePlan& pl, const pqhost:
 // process ends.  The host only ever uses the device address that
 // hipGetSymbolAddress returns for it (the array's name is a host-side stand-in
 // in host code).  Every call on a GPU shares that GPU's copy, so calls that
-// can overlap in time on one GPU race.  The layer kernels leave the counters,
-// flags and exchange regions at zero when they finish, as they do in a
+// can overlap in time on one GPU race.  The layer kernels leave the counters
+// and the exchange region at zero when they finish, as they do in a
 // caller's workspace; the copy is zeroed once, when the device first uses it.
 constexpr size_t kScratchBytes = (size_t)4 << 20;
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];

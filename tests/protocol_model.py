@@ -11,15 +11,15 @@ whose waits time out although every block was resident.
 
 Barrier kernel (one or two tokens):
   * block b owns the units [split(U, G, b), split(U, G, b+1)); its waves take
-    them one at a time from the block's LDS counter;
-  * each wave, done with its units, arrives at the block's LDS arrival
-    counter; the last wave of the block adds the block's unit count to the
-    grid-wide phase counter (when the block owned any), and the add that
-    completes the count writes the release flag of every block;
-  * each block waits for its own flag, then reads every h row (all units of
-    the call) and runs its down rows;
-  * each block counts itself out; the last one clears the phase counter, the
-    exit counter and every flag.
+    them one at a time from the block's LDS counter and publish each unit's h
+    (a non-zero word: h is stored bit-inverted into a region that is zero
+    between calls);
+  * once every wave of the block is done with its units (block barrier: the
+    staged h overwrites x), each wave waits until every h word of its share
+    is non-zero (it polls the values themselves); the block then runs its
+    down rows;
+  * each block counts itself out; the last one clears h and the exit
+    counter.
 
 Stream kernel (three tokens or more):
   * gate_up unit k of block b is entry b + k*G of the expert-major list;
@@ -48,17 +48,21 @@ def split_start(n: int, p: int, i: int) -> int:
 
 
 class Grid:
-    """Shared state of one launch: global memory words and the error word."""
+    """Shared state of one launch: global memory words and the error word.
+    ``nh`` counts the non-zero h words (what a poll over all of h sees)."""
 
     def __init__(self, G: int):
         self.G = G
         self.error = 0
         self.mem = {}
+        self.nh = 0
 
     def get(self, k, default=0):
         return self.mem.get(k, default)
 
     def put(self, k, v):
+        if isinstance(k, tuple) and k[0] == "h":
+            self.nh += (v != 0) - (self.mem.get(k, 0) != 0)
         self.mem[k] = v
 
     def record_timeout(self):
@@ -81,17 +85,17 @@ def wait_until(cond, grid: Grid, limit: int):
 # barrier kernel
 # ---------------------------------------------------------------------------
 
-def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, clear_flags: bool = True):
-    """The waves of block b, as a list of generators.  clear_flags=False models
-    a last block that leaves the release flags set (a mistake: the next call
-    would be released before its h is written)."""
-    lds = {"next": 0, "arrive": 0, "released": False, "rows_done": 0}
+def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, clear_h: bool = True):
+    """The waves of block b, as a list of generators.  clear_h=False models a
+    last block that leaves h set (a mistake: the next call would read the
+    previous call's h as its own before it is written)."""
+    lds = {"next": 0}
     start, end = split_start(U, grid.G, b), split_start(U, grid.G, b + 1)
     nrows = end - start
-    waves_done = {"gate_up": 0, "exit": 0}
+    waves_done = {"gate_up": 0, "staged": 0, "exit": 0}
 
     def wave(w):
-        # gate_up: claim units from the block's LDS counter
+        # gate_up: claim units from the block's LDS counter, publish each h
         while True:
             c = lds["next"]
             lds["next"] += 1
@@ -99,32 +103,20 @@ def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, cle
             if c >= nrows:
                 break
             u = start + c
-            log["h_written"][u] = log["h_written"].get(u, 0) + 1     # the unit's h store
+            grid.put(("h", u), 1)
+            log["h_written"][u] = log["h_written"].get(u, 0) + 1
             log["n_written"] += 1
             yield
-        # arrival: the last wave of the block adds its rows to the phase counter
-        before = lds["arrive"]
-        lds["arrive"] += 1
-        yield
-        if before == W - 1 and nrows > 0:
-            old = grid.get("done")
-            grid.put("done", old + nrows)
-            yield
-            if old + nrows == U:                      # this add completed the count: release all
-                for b0 in range(0, grid.G, 64):       # the wave's 64 lanes write 64 flags per store
-                    for bb in range(b0, min(b0 + 64, grid.G)):
-                        grid.put(("flag", bb), 1)
-                    yield
-        # block barrier before the flag wait (thread 0 waits, the block follows)
+        # block barrier (the staged h overwrites x in LDS), then staging: poll
+        # until every h word of the call is non-zero (bounded)
         waves_done["gate_up"] += 1
         yield from wait_until(lambda: waves_done["gate_up"] == W, grid, 10 ** 9)
-        if w == 0:
-            ok = yield from wait_until(lambda: grid.get(("flag", b)) == 1, grid, limit)
-            lds["released"] = True
-            if ok and log["n_written"] != U:       # every h row of the call must be written by now
-                log["early_release"].append((b, U - log["n_written"]))
-        yield from wait_until(lambda: lds["released"], grid, 10 ** 9)
-        # down rows (no cross-block waits), then the exit count
+        ok = yield from wait_until(lambda: grid.nh >= U, grid, limit)
+        if ok and log["n_written"] != U:           # what it read must be this call's h
+            log["early_release"].append((b, U - log["n_written"]))
+        # block barrier after staging, then down rows (no cross-block waits)
+        waves_done["staged"] += 1
+        yield from wait_until(lambda: waves_done["staged"] == W, grid, 10 ** 9)
         yield
         waves_done["exit"] += 1
         yield from wait_until(lambda: waves_done["exit"] == W, grid, 10 ** 9)
@@ -133,12 +125,11 @@ def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, cle
             grid.put("exit_count", old + 1)
             yield
             if old == grid.G - 1:                     # the last block clears what the call used
-                grid.put("done", 0)
                 grid.put("exit_count", 0)
-                if clear_flags:
-                    for b0 in range(0, grid.G, 1024):     # the block's 1024 threads clear 1024 flags per store
-                        for bb in range(b0, min(b0 + 1024, grid.G)):
-                            grid.put(("flag", bb), 0)
+                if clear_h:
+                    for u0 in range(0, U, 1024 * 8):  # the block's threads clear 8 words each per store
+                        for u in range(u0, min(u0 + 1024 * 8, U)):
+                            grid.put(("h", u), 0)
                         yield
                 log["cleared_by"].append(b)
 
@@ -227,7 +218,7 @@ def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: 
 
 def run(kernel: str, G: int, W: int = 4, *, U: int = 12, nU: int = 3, I: int = 4, unp=None, alias=False,
         limit: int = 10 ** 6, seed: int = 0, late_block: int | None = None, max_steps: int = 10 ** 8,
-        grid: Grid | None = None, clear_flags: bool = True):
+        grid: Grid | None = None, clear_h: bool = True):
     """Run one launch of the model; returns (grid, log, steps).
 
     late_block: that block is not resident until every other block has ended
@@ -241,7 +232,7 @@ def run(kernel: str, G: int, W: int = 4, *, U: int = 12, nU: int = 3, I: int = 4
     blocks = []
     for b in range(G):
         if kernel == "barrier":
-            blocks.append(barrier_block(grid, b, W, U, limit, log, clear_flags))
+            blocks.append(barrier_block(grid, b, W, U, limit, log, clear_h))
         else:
             blocks.append(stream_block(grid, b, W, nU, I, unp or [1] * nU, alias, limit, log))
     live = [(b, g) for b, ws in enumerate(blocks) for g in ws if b != late_block]

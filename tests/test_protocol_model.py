@@ -80,18 +80,18 @@ def test_stream_protocol_large_grids(G):
 
 
 def test_calls_in_a_row_release_only_after_h_is_written():
-    """Two calls on one workspace: the flags the first call set are cleared by
-    its last block, so the second call's blocks wait for its own release.  A
-    last block that leaves the flags set (the mistake this guards against)
-    lets the second call read h before it is written."""
+    """Two calls on one workspace: the h words the first call wrote are cleared
+    by its last block, so the second call's blocks wait for its own h.  A last
+    block that leaves h set (the mistake this guards against) lets the second
+    call read h before it is written."""
     for G in (1, 5, 64):
         grid, log, _ = pm.run("barrier", G, W=3, U=20, seed=1)
         _clean_barrier(grid, log, 20)
         grid, log, _ = pm.run("barrier", G, W=3, U=20, seed=2, grid=grid)
         _clean_barrier(grid, log, 20)
-    grid, _, _ = pm.run("barrier", 16, W=3, U=40, seed=3, clear_flags=False)
-    _, log, _ = pm.run("barrier", 16, W=3, U=40, seed=4, grid=grid, clear_flags=False)
-    assert log["early_release"], "the model failed to show the stale-flag mistake"
+    grid, _, _ = pm.run("barrier", 16, W=3, U=40, seed=3, clear_h=False)
+    _, log, _ = pm.run("barrier", 16, W=3, U=40, seed=4, grid=grid, clear_h=False)
+    assert log["early_release"], "the model failed to show the stale-h mistake"
 
 
 @pytest.mark.parametrize("kernel", ["barrier", "stream"])

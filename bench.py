@@ -597,11 +597,15 @@ def run_prefill(args):
     print(json.dumps(out), flush=True)
 
 
-def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES):
+def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES, kernel=KERNEL_NAME, summary=None, made_by=None):
     """Turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run) into
-    the committed summary: mean KiB per dispatch of the layer kernel and of the
-    calibration copy kernel, and the copy-derived scale factors."""
+    a summary: mean KiB per dispatch of the kernel whose name contains
+    ``kernel`` and of the calibration copy kernel, and the copy-derived scale
+    factors.  By default the headline layer kernel, into the summary the bench
+    line's traffic figure is read from."""
     import csv
+    headline = summary is None
+    summary = PMC_SUMMARY if headline else summary
 
     def per_kernel(path, counter):
         rows = list(csv.DictReader(open(path, encoding="utf-8")))
@@ -629,57 +633,102 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES):
             vals = [v for v in vals if v >= 0.5 * top]
         return sum(vals) / len(vals), len(vals), name
 
-    mf, nf, _ = pick(f, KERNEL_NAME)
-    mw, nw, _ = pick(w, KERNEL_NAME)
+    mf, nf, kname = pick(f, kernel)
+    mw, nw, _ = pick(w, kernel)
     cf, ncf, cname = pick(f, "copy", largest=True)
     cw, ncw, _ = pick(w, "copy", largest=True)
     d = {
-        "kernel": KERNEL_NAME, "source_sha": kernel_source_sha(),
+        "kernel": kernel if headline else kname, "source_sha": kernel_source_sha(),
         "fetch_kib": mf, "write_kib": mw, "dispatches": [nf, nw],
         "copy_kernel": cname, "copy_bytes": copy_bytes, "copy_dispatches": [ncf, ncw],
         "copy_fetch_kib": cf, "copy_write_kib": cw,
         "fetch_scale": copy_bytes / (cf * 1024), "write_scale": copy_bytes / (cw * 1024),
     }
     txt = json.dumps(d, indent=1)
-    os.makedirs(os.path.dirname(PMC_SUMMARY), exist_ok=True)
-    with open(PMC_SUMMARY, "w", encoding="utf-8") as fh:
+    pass_args = made_by or "--profile-pass --steps 20"
+    os.makedirs(os.path.dirname(summary), exist_ok=True)
+    with open(summary, "w", encoding="utf-8") as fh:
         fh.write(txt + "\n---\n" + f"source: {fetch_csv}, {write_csv}\n"
                  "made by (from the repository root on the MI355X box, $REPO = that root):\n"
                  "  cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d "
-                 "$REPO/<dir>/fetch -o f -- python3 $REPO/bench.py --profile-pass --steps 20\n"
+                 f"$REPO/<dir>/fetch -o f -- python3 $REPO/bench.py {pass_args}\n"
                  "  cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d "
-                 "$REPO/<dir>/write -o w -- python3 $REPO/bench.py --profile-pass --steps 20\n"
+                 f"$REPO/<dir>/write -o w -- python3 $REPO/bench.py {pass_args}\n"
                  "  python3 bench.py --ingest-pmc <dir>/fetch/f_counter_collection.csv "
-                 "<dir>/write/w_counter_collection.csv\n"
-                 "fetch_kib / write_kib: mean KiB per dispatch of the layer kernel; the scales are the copy "
+                 "<dir>/write/w_counter_collection.csv"
+                 + ("" if headline else f" --kernel '{kernel}' --summary {os.path.relpath(summary, ROOT)}"
+                    + (f" --pass-args '{made_by}'" if made_by else "")) + "\n"
+                 "fetch_kib / write_kib: mean KiB per dispatch of the kernel; the scales are the copy "
                  "kernel's known bytes over what the same counters read for it.\n")
     print(txt)
 
 
+def ingest_sq(csv_path, kernel, summary, made_by):
+    """Mean per dispatch of every counter of one rocprofv3 --pmc CSV for the
+    kernel whose name contains ``kernel`` (instruction and cycle counters)."""
+    import csv
+    acc = {}
+    name = None
+    for r in csv.DictReader(open(csv_path, encoding="utf-8")):
+        if kernel not in r.get("Kernel_Name", ""):
+            continue
+        name = r["Kernel_Name"]
+        acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not acc:
+        raise KeyError(kernel)
+    d = {"kernel": name, "source_sha": kernel_source_sha(),
+         "dispatches": len(next(iter(acc.values()))),
+         "mean_per_dispatch": {c: sum(v) / len(v) for c, v in sorted(acc.items())}}
+    txt = json.dumps(d, indent=1)
+    counters = " ".join(sorted(acc))
+    with open(summary, "w", encoding="utf-8") as fh:
+        fh.write(txt + "\n---\n" + f"source: {csv_path}\n"
+                 "made by (from the repository root on the MI355X box, $REPO = that root):\n"
+                 f"  cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {counters} --output-format csv -d "
+                 f"$REPO/<dir>/sq -o s -- python3 $REPO/bench.py {made_by}\n"
+                 f"  python3 bench.py --ingest-sq <dir>/sq/s_counter_collection.csv --kernel '{kernel}' "
+                 f"--summary {os.path.relpath(summary, ROOT)} --pass-args '{made_by}'\n"
+                 "SQ counters are summed over the device's shader engines; GRBM_GUI_ACTIVE counts GPU-busy "
+                 "cycles.\n")
+    print(txt)
+
+
 def profile_pass(args):
-    """Short run for rocprofv3 counter collection: a few layer launches plus a
-    1 GiB device copy (the calibration kernel of known size)."""
+    """Short run for rocprofv3 counter collection: a few launches of the
+    workload plus a 1 GiB device copy (the calibration kernel of known size).
+    The default (batch-1 layer) runs only the layer calls; another workload
+    runs its bench pass with --steps as given."""
     import numpy as np
     import torch
 
     import quantized_moe_weight_amd as pq
     import workloads
     torch.cuda.set_device(0)
-    shp = workloads.MOE_SHAPE
-    w13, s13, w2, s2 = build_bank(pq, shp)
-    x_bits = workloads.activation_bf16(1, shp.H, workload=workloads.MOE_LAYER)
-    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
-    call = pq.MoeLayerCall(w13, s13, w2, s2, M=1, top_k=shp.top_k)
-    pool = [torch.from_numpy(workloads.router_logits(1, shp.E, workload=workloads.MOE_LAYER, draw=d)).cuda()
-            for d in range(64)]
-    for i in range(args.steps):
-        call(x, pool[i % 64])
+    if args.workload != "moe" or args.m != 1:
+        args.cpu_baseline = False
+        args.warmup = min(args.warmup, 5)
+        if args.workload == "prefill":
+            run_prefill(args)
+        elif args.workload in ("moe", "moe_tp8", "moe_full"):
+            run(args)
+        else:
+            run_dense(args)
+    else:
+        shp = workloads.MOE_SHAPE
+        w13, s13, w2, s2 = build_bank(pq, shp)
+        x_bits = workloads.activation_bf16(1, shp.H, workload=workloads.MOE_LAYER)
+        x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+        call = pq.MoeLayerCall(w13, s13, w2, s2, M=1, top_k=shp.top_k)
+        pool = [torch.from_numpy(workloads.router_logits(1, shp.E, workload=workloads.MOE_LAYER, draw=d)).cuda()
+                for d in range(64)]
+        for i in range(args.steps):
+            call(x, pool[i % 64])
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"profile pass: {args.steps} layer launches, 3 copies of {COPY_BYTES} bytes", flush=True)
+    print(f"profile pass: {args.workload} M={args.m}, {args.steps} steps, 3 copies of {COPY_BYTES} bytes", flush=True)
 
 
 def main():
@@ -697,9 +746,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--ingest-sq", metavar="SQ_CSV")
+    ap.add_argument("--kernel", default=KERNEL_NAME, help="ingest: substring of the kernel's name")
+    ap.add_argument("--summary", help="ingest: summary file to write (default: the headline layer's)")
+    ap.add_argument("--pass-args", help="ingest: the bench.py arguments of the profiled run (for the record)")
     args = ap.parse_args()
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc)
+        summ = os.path.join(ROOT, args.summary) if args.summary else None
+        ingest_pmc(*args.ingest_pmc, kernel=args.kernel, summary=summ, made_by=args.pass_args)
+        return
+    if args.ingest_sq:
+        ingest_sq(args.ingest_sq, args.kernel, os.path.join(ROOT, args.summary), args.pass_args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",

@@ -8,10 +8,10 @@
 // gfx950 design
 //   * each block owns a contiguous range of output rows and streams them in
 //     1 KB chunks (one 16-byte load per lane = 32 weights = exactly one scale
-//     group); the (row, chunk) units of the block are dealt to its 8 waves in
-//     order, so K is split inside the block wherever a row straddles two
-//     waves, and the split is reduced through LDS after one barrier: no
-//     global partials, atomics or store waits in the stream;
+//     group); the (row, chunk) units of the block are dealt to its waves as
+//     contiguous runs, so K is split inside the block wherever a row
+//     straddles two waves, and the split is reduced through LDS after one
+//     barrier: no global partials, atomics or store waits in the stream;
 //   * each wave keeps D chunk steps in flight in a ring of raw buffer loads
 //     issued without branches (out-of-range slots return zero without memory
 //     traffic), and the last D steps drain the ring without issuing; shallow
@@ -109,10 +109,17 @@ __device__ __forceinline__ uint4 pair_order(uint4 r) {
 //     B up row i; otherwise A and B are consecutive rows.
 //   * Block b owns the same share of every linear's rows (the split of the
 //     rows over the grid depends on the linear's shape and the CU count only),
-//     and a linear's units of the block are dealt to the block's waves in
-//     order, linear by linear, exactly as if the linear ran alone: a
-//     linear's output bits do not depend on the other linears of the launch,
-//     nor on M.  Each wave streams its share of every linear back to back;
+//     and a linear's units of the block are dealt to the block's waves as
+//     contiguous runs (wave w takes units [split(U, 16, w), split(U, 16,
+//     w+1)), unit = pair * nch + chunk), linear by linear, exactly as if the
+//     linear ran alone: a linear's output bits do not depend on the other
+//     linears of the launch, nor on M.  A wave accumulates a row pair's
+//     chunks of its run per lane and reduces them across the wave once, at the
+//     run's last chunk of the pair (writing an exact zero for the run's other
+//     chunks of it), instead of reducing every chunk: 2 * M wave reductions
+//     per pair-run rather than per 2 KB step (dealt round-robin, so that the
+//     block read one window of consecutive chunks, the stack was 13% slower
+//     at M = 4 and 4% at M = 1).  Each wave streams its share of every linear back to back;
 //     its ring of load steps runs across linear boundaries, so the start-up
 //     and ring fill are paid once per launch.
 //   * The activations of every linear of the launch are staged in LDS at
@@ -277,20 +284,19 @@ __global__ __launch_bounds__(kVThreads) void gemv_q4_kernel(const Q4Group a) {
   }
   __builtin_amdgcn_s_barrier();
 
-  // This wave's units of every linear: unit u = (pair u / nch, chunk u % nch)
-  // of the block's rows goes to wave u % kVWaves, so at every step the waves of
-  // the block read one window of consecutive chunks (a few DRAM pages) rather
-  // than one stream each.  Written and read by the wave itself (no barrier).
+  // This wave's units of every linear: the contiguous run [u0, u0 + left)
+  // of units u = (pair u / nch, chunk u % nch) of the block's rows, walked
+  // chunk by chunk.  Written and read by the wave itself (no barrier).
   int total = 0;
   for (int li = 0; li < a.n; ++li) {             // uniform
     const Q4Lin& L = a.lin[li];
     const BlockRows br = block_rows(L, G, (int)blockIdx.x);
     const int units = br.pairs * L.nch;
-    const int left = units > wv ? (units - wv + kVWaves - 1) / kVWaves : 0;
+    const int u0 = pq::split_start(units, kVWaves, wv);
+    const int left = pq::split_start(units, kVWaves, wv + 1) - u0;
     total += left;
     if (lane == 0)
-      s_seg[wv][li] = SegEntry{wv / L.nch, wv - (wv / L.nch) * L.nch, left, kVWaves / L.nch,
-                               kVWaves - (kVWaves / L.nch) * L.nch, br.rs, br.re, L.nch};
+      s_seg[wv][li] = SegEntry{u0 / L.nch, u0 - (u0 / L.nch) * L.nch, left, 0, 1, br.rs, br.re, L.nch};
   }
   const SegEntry* seg = s_seg[wv];
 
@@ -422,10 +428,10 @@ __global__ __launch_bounds__(kVThreads) void gemv_q4_kernel(const Q4Group a) {
         for (int t = 0; t < 4; ++t) xv[t] = xs_l[p0 + t * c_ng];
         const float cv = fl[c_soff + m * c_ng + g];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j][m] = (dot32(w[j], xv) - cv) * sc[j];
+        for (int j = 0; j < 2; ++j) acc[j][m] = fmaf(dot32(w[j], xv) - cv, sc[j], acc[j][m]);
       }
     }
-    {                                              // the unit's partial sums: one per row and token
+    if (cc.c == c_nch - 1 || cc.left == 1) {      // the wave's last chunk of this pair: its partial sums
       float v = 0.0f;
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -436,6 +442,8 @@ __global__ __launch_bounds__(kVThreads) void gemv_q4_kernel(const Q4Group a) {
           if (lane == 2 * m + j) v = s;
         }
       if (lane < 2 * MT) fl[c_poff + (size_t)(cc.p * c_nch + cc.c) * MT * 2 + lane] = v;
+    } else if (lane < 2 * MT) {                    // an earlier chunk of the run: its slot adds nothing
+      fl[c_poff + (size_t)(cc.p * c_nch + cc.c) * MT * 2 + lane] = 0.0f;
     }
     cc = cursor_next(a, seg, cc);
   };

@@ -237,6 +237,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 63));
 }
 
+// The sum over aligned segments of `lanes` lanes (8, 16 or 32), left in each
+// segment's last lane: the first stages of wave_sum, so a segment's sum is
+// the same additions in the same order as wave_sum's for values held by
+// those lanes alone (other lanes zero), up to the sign of a zero sum.
+__device__ __forceinline__ float segment_sum(float v, int lanes) {
+  float t = v + dpp_f32<kRowShr1>(v);
+  t += dpp_f32<kRowShr2>(v);
+  t += dpp_f32<kRowShr3>(v);
+  t += dpp_f32<kRowShr4, 0xf, 0xe>(t);               // lanes 7 and 15 of a row: 8-lane sums
+  if (lanes >= 16) t += dpp_f32<kRowShr8, 0xf, 0xc>(t);   // lane 15: the row's sum
+  if (lanes >= 32) t += dpp_f32<kRowBcast15, 0xa>(t);     // lanes 31, 63: two rows' sums
+  return t;
+}
+
+template <bool B>
+struct BoolC {                                       // a compile-time flag passed to a generic lambda
+  static constexpr bool value = B;
+};
+
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   uint32_t t = umax(v, (uint32_t)dpp_i32<kRowShr1>((int)v));

@@ -854,165 +854,227 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   const int bunits = nrows * nU;
   const int v0 = ufl(pq::split_start(bunits, kWaves, wv));
   const int v1 = ufl(pq::split_start(bunits, kWaves, wv + 1));
-  const int dsteps = (v1 - v0) * nchI;
+  // Short rows (I = 128, 256 or 512: one chunk) are packed: a step carries
+  // pr_rows = 64 / (I / 16) consecutive rows of one entry, lane segment k
+  // holding row k, so the lanes of a step are not mostly idle; a row's sum is
+  // reduced inside its segment by the first stages of the wave-wide sum, the
+  // same additions in the same order as for a row alone in the wave.
+  const int lpr = I / 16;                            // lanes per row
+  const bool packed = nchI == 1 && (I == 128 || I == 256 || I == 512);
   float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);   // [row_local][P] fp32
-  // (the down steps keep their per-step scale loads: a down step does half
-  // a gate_up step's work, and an LDS read in its dependency chain measured
-  // slower than the load that arrives with the weights)
-  uint4 wd[BDD];
-  float sd[BDD];
-  int ju = nrows > 0 ? v0 / nrows : 0;
-  int jr = v0 - ju * nrows, jc = 0, dleft = dsteps;
-  pq::rsrc_t dwr, dsr;
-  auto set_dn_expert = [&]() {
-    const int e = ufl(route.uexp[ju < nU ? ju : 0]);
-    dwr = pq::make_rsrc(dn_weights<EXT>(a, e), (uint32_t)(H * I));
-    dsr = pq::make_rsrc(dn_scales<EXT>(a, e), (uint32_t)(H * nbI * 4));
-  };
-  set_dn_expert();
-  auto issue_dn = [&](uint4& w, float& s) {
-    const uint32_t kc = (uint32_t)(jc * pq::kChunk);
-    const bool ok = dleft > 0 && kc + lane16 < (uint32_t)I;
-    const uint32_t row = (uint32_t)(r0 + jr);
-    w = pq::buf_load16_nt(dwr, ok ? row * (uint32_t)I + kc + lane16 : pq::kOOB);
-    s = pq::buf_load_f32_nt(dsr, ok ? (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
-    --dleft;
-    if (++jc == nchI) {
-      jc = 0;
-      if (++jr == nrows) {
-        jr = 0;
-        ++ju;
-        set_dn_expert();
+  // The two forms are separate instantiations, so the unpacked steps carry
+  // none of the packed bookkeeping.
+  auto down_phase = [&](auto packed_c) {
+    constexpr bool kP = decltype(packed_c)::value;
+    const int pr_rows = kP ? pq::kWave / lpr : 1;
+    const int prr = kP ? lane / lpr : 0;           // this lane's row in a packed step
+    const uint32_t plk16 = kP ? 16u * (uint32_t)(lane % lpr) : lane16;
+    int dsteps = (v1 - v0) * nchI;
+    if constexpr (kP) {                              // per entry: ceil(rows / pr_rows) steps
+      dsteps = 0;
+      for (int u = v0; u < v1;) {
+        const int e_end = (u / nrows + 1) * nrows;
+        const int n = (v1 < e_end ? v1 : e_end) - u;
+        dsteps += (n + pr_rows - 1) / pr_rows;
+        u += n;
       }
     }
-  };
-#pragma unroll
-  for (int q = 0; q < BDD; ++q) issue_dn(wd[q], sd[q]);
-
-  // Every h row of the call, quantised into LDS as soon as it is there: h
-  // is stored bit-inverted into a region that is zero between calls, so a
-  // zero word is a value not yet written.  The h codes overwrite the x codes,
-  // so the block first waits for all its waves to be past gate_up; then each
-  // wave polls its share (only the vectors still missing are loaded again)
-  // while the last gate_up units of slower blocks finish.  Every block derives
-  // the same codes and scales from the same values (block 0 also writes them
-  // out when asked).
-  __syncthreads();
-  {
-    // 8 values per lane, 16 lanes per 128-value block (the layout of the
-    // activation quantiser); agent-coherent 16-byte loads, a batch in flight
-    const int nvec = P2 * I / 8;
-    const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P2 * I * 2));
-    constexpr int kBatch = 2;
-    for (int t0 = 0; t0 < nvec; t0 += kBatch * kThreads) {
-      uint4 raw[kBatch];
-      bool have[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        have[i] = t0 + i * kThreads + (int)threadIdx.x >= nvec;
-        raw[i] = make_uint4(0u, 0u, 0u, 0u);
+    // (the down steps keep their per-step scale loads: a down step does half
+    // a gate_up step's work, and an LDS read in its dependency chain measured
+    // slower than the load that arrives with the weights)
+    uint4 wd[BDD];
+    float sd[BDD];
+    int ju = nrows > 0 ? v0 / nrows : 0;
+    int jr = v0 - ju * nrows, jc = 0, dleft = dsteps, uleft = v1 - v0;
+    pq::rsrc_t dwr, dsr;
+    auto set_dn_expert = [&]() {
+      const int e = ufl(route.uexp[ju < nU ? ju : 0]);
+      dwr = pq::make_rsrc(dn_weights<EXT>(a, e), (uint32_t)(H * I));
+      dsr = pq::make_rsrc(dn_scales<EXT>(a, e), (uint32_t)(H * nbI * 4));
+    };
+    set_dn_expert();
+    auto issue_dn = [&](uint4& w, float& s) {
+      const uint32_t kc = (uint32_t)(jc * pq::kChunk);
+      int nr = 1;                                      // rows of this step
+      if constexpr (kP) {
+        nr = nrows - jr < uleft ? nrows - jr : uleft;
+        nr = nr < pr_rows ? nr : pr_rows;
       }
-      for (uint32_t it = 0;; ++it) {
-        bool miss = false;
-#pragma unroll
+      const bool ok = dleft > 0 && prr < nr && kc + plk16 < (uint32_t)I;
+      const uint32_t row = (uint32_t)(r0 + jr + prr);
+      w = pq::buf_load16_nt(dwr, ok ? row * (uint32_t)I + kc + plk16 : pq::kOOB);
+      const uint32_t soff = kP ? (row * (uint32_t)nbI + plk16 / pq::kBlock) * 4u
+                               : (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4;
+      s = pq::buf_load_f32_nt(dsr, ok ? soff : pq::kOOB);
+      --dleft;
+      if constexpr (kP) {
+        uleft -= nr;
+        jr += nr;
+        if (jr == nrows) {
+          jr = 0;
+          ++ju;
+          set_dn_expert();
+        }
+      } else if (++jc == nchI) {
+        jc = 0;
+        if (++jr == nrows) {
+          jr = 0;
+          ++ju;
+          set_dn_expert();
+        }
+      }
+    };
+  #pragma unroll
+    for (int q = 0; q < BDD; ++q) issue_dn(wd[q], sd[q]);
+
+    // Every h row of the call, quantised into LDS as soon as it is there: h
+    // is stored bit-inverted into a region that is zero between calls, so a
+    // zero word is a value not yet written.  The h codes overwrite the x codes,
+    // so the block first waits for all its waves to be past gate_up; then each
+    // wave polls its share (only the vectors still missing are loaded again)
+    // while the last gate_up units of slower blocks finish.  Every block derives
+    // the same codes and scales from the same values (block 0 also writes them
+    // out when asked).
+    __syncthreads();
+    {
+      // 8 values per lane, 16 lanes per 128-value block (the layout of the
+      // activation quantiser); agent-coherent 16-byte loads, a batch in flight
+      const int nvec = P2 * I / 8;
+      const pq::rsrc_t hr = pq::make_rsrc(a.hbuf, (uint32_t)(P2 * I * 2));
+      constexpr int kBatch = 2;
+      for (int t0 = 0; t0 < nvec; t0 += kBatch * kThreads) {
+        uint4 raw[kBatch];
+        bool have[kBatch];
+  #pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          have[i] = t0 + i * kThreads + (int)threadIdx.x >= nvec;
+          raw[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        for (uint32_t it = 0;; ++it) {
+          bool miss = false;
+  #pragma unroll
+          for (int i = 0; i < kBatch; ++i) {
+            const int t = t0 + i * kThreads + (int)threadIdx.x;
+            const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                hr, (int)(have[i] ? pq::kOOB : (uint32_t)t * 16u), 0, kAuxSC1));
+            if (!have[i]) {
+              raw[i] = r;
+              have[i] = !(has_zero_half(r.x) || has_zero_half(r.y) || has_zero_half(r.z) || has_zero_half(r.w));
+            }
+            miss |= !have[i];
+          }
+          if (__ballot(miss) == 0ull) break;
+          if (it >= a.spin_limit) {
+            if (lane == 0) pq::record_error(hdr, PQ_ERR_TIMEOUT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+  #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
           const int t = t0 + i * kThreads + (int)threadIdx.x;
-          const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-              hr, (int)(have[i] ? pq::kOOB : (uint32_t)t * 16u), 0, kAuxSC1));
-          if (!have[i]) {
-            raw[i] = r;
-            have[i] = !(has_zero_half(r.x) || has_zero_half(r.y) || has_zero_half(r.z) || has_zero_half(r.w));
-          }
-          miss |= !have[i];
-        }
-        if (__ballot(miss) == 0ull) break;
-        if (it >= a.spin_limit) {
-          if (lane == 0) pq::record_error(hdr, PQ_ERR_TIMEOUT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int t = t0 + i * kThreads + (int)threadIdx.x;
-        const bool valid = t < nvec;
-        raw[i] = make_uint4(~raw[i].x, ~raw[i].y, ~raw[i].z, ~raw[i].w);
-        float v[8];
-        pq::bf16x8_to_f32(raw[i], v);
-        const float sc = pq::fp8_block_scale16(v, valid);
-        if (valid) {
-          const uint2 c8 = pq::fp8_codes8(v, sc);
-          reinterpret_cast<uint2*>(act)[t] = c8;
-          if ((threadIdx.x & 15) == 0) acts[t / 16] = sc;
-          if (blockIdx.x == 0) {
-            if (a.hq_dbg) reinterpret_cast<uint2*>(a.hq_dbg)[t] = c8;
-            if (a.hs_dbg && (threadIdx.x & 15) == 0) a.hs_dbg[t / 16] = sc;
+          const bool valid = t < nvec;
+          raw[i] = make_uint4(~raw[i].x, ~raw[i].y, ~raw[i].z, ~raw[i].w);
+          float v[8];
+          pq::bf16x8_to_f32(raw[i], v);
+          const float sc = pq::fp8_block_scale16(v, valid);
+          if (valid) {
+            const uint2 c8 = pq::fp8_codes8(v, sc);
+            reinterpret_cast<uint2*>(act)[t] = c8;
+            if ((threadIdx.x & 15) == 0) acts[t / 16] = sc;
+            if (blockIdx.x == 0) {
+              if (a.hq_dbg) reinterpret_cast<uint2*>(a.hq_dbg)[t] = c8;
+              if (a.hs_dbg && (threadIdx.x & 15) == 0) a.hs_dbg[t / 16] = sc;
+            }
           }
         }
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  {
-    float acc[TP];
-    int pr[TP];
-#pragma unroll
-    for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
-    int cu = nrows > 0 ? v0 / nrows : 0;
-    int cr = v0 - cu * nrows, cc = 0;
-    int cnp = 0;
-    auto load_pairs = [&]() {
-      const int uu = cu < nU ? cu : 0;
-      cnp = ufl(route.unp[uu]);
-#pragma unroll
-      for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[uu][t]);
-    };
-    load_pairs();
-    auto consume_dn = [&](const uint4& w, float sw) {
-      const uint32_t off = (uint32_t)(cc * pq::kChunk) + lane16;
-      if (off < (uint32_t)I) {
-        const pq::Bf16x16 wv2 = pq::widen16(w);
-#pragma unroll
-        for (int t = 0; t < TP; ++t) {
-          if (t < cnp) {
-            const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
-            const float hsc = acts[pr[t] * nbI + off / pq::kBlock];
-            acc[t] = fmaf(pq::dot16(wv2, hv), sw * hsc, acc[t]);
+    {
+      float acc[TP];
+      int pr[TP];
+  #pragma unroll
+      for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
+      int cu = nrows > 0 ? v0 / nrows : 0;
+      int cr = v0 - cu * nrows, cc = 0;
+      int cnp = 0;
+      auto load_pairs = [&]() {
+        const int uu = cu < nU ? cu : 0;
+        cnp = ufl(route.unp[uu]);
+  #pragma unroll
+        for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[uu][t]);
+      };
+      load_pairs();
+      int cleft = v1 - v0;
+      auto consume_dn = [&](const uint4& w, float sw) {
+        int nr = 1;
+        if constexpr (kP) {
+          nr = nrows - cr < cleft ? nrows - cr : cleft;
+          nr = nr < pr_rows ? nr : pr_rows;
+        }
+        const uint32_t off = (uint32_t)(cc * pq::kChunk) + plk16;
+        if (prr < nr && off < (uint32_t)I) {
+          const pq::Bf16x16 wv2 = pq::widen16(w);
+  #pragma unroll
+          for (int t = 0; t < TP; ++t) {
+            if (t < cnp) {
+              const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
+              const float hsc = acts[pr[t] * nbI + off / pq::kBlock];
+              acc[t] = fmaf(pq::dot16(wv2, hv), sw * hsc, acc[t]);
+            }
           }
         }
-      }
-      if (cc == nchI - 1) {               // unit (union entry cu, row cr) done
-#pragma unroll
-        for (int t = 0; t < TP; ++t) {
-          if (t < cnp) {
-            const float y = pq::wave_sum(acc[t]);
-            if (lane == 0) ybuf[cr * P2 + pr[t]] = y;
+        if (cc == nchI - 1) {               // unit(s) (union entry cu, rows cr ..) done
+  #pragma unroll
+          for (int t = 0; t < TP; ++t) {
+            if (t < cnp) {
+              if constexpr (kP) {                     // each segment's last lane holds its row's sum
+                const float y = pq::segment_sum(acc[t], lpr);
+                if (lane % lpr == lpr - 1 && prr < nr) ybuf[(cr + prr) * P2 + pr[t]] = y;
+              } else {
+                const float y = pq::wave_sum(acc[t]);
+                if (lane == 0) ybuf[cr * P2 + pr[t]] = y;
+              }
+            }
+            acc[t] = 0.0f;
           }
-          acc[t] = 0.0f;
+        }
+        if constexpr (kP) {
+          cleft -= nr;
+          cr += nr;
+          if (cr == nrows) {
+            cr = 0;
+            ++cu;
+            load_pairs();
+          }
+        } else if (++cc == nchI) {
+          cc = 0;
+          if (++cr == nrows) {
+            cr = 0;
+            ++cu;
+            load_pairs();
+          }
+        }
+      };
+      int base = 0;
+      for (; base + BDD < dsteps; base += BDD) {     // steady state: every slot refills
+  #pragma unroll
+        for (int q = 0; q < BDD; ++q) {
+          consume_dn(wd[q], sd[q]);
+          issue_dn(wd[q], sd[q]);
         }
       }
-      if (++cc == nchI) {
-        cc = 0;
-        if (++cr == nrows) {
-          cr = 0;
-          ++cu;
-          load_pairs();
-        }
-      }
-    };
-    int base = 0;
-    for (; base + BDD < dsteps; base += BDD) {     // steady state: every slot refills
-#pragma unroll
-      for (int q = 0; q < BDD; ++q) {
-        consume_dn(wd[q], sd[q]);
-        issue_dn(wd[q], sd[q]);
-      }
+  #pragma unroll
+      for (int q = 0; q < BDD; ++q)                 // drain
+        if (base + q < dsteps) consume_dn(wd[q], sd[q]);
     }
-#pragma unroll
-    for (int q = 0; q < BDD; ++q)                 // drain
-      if (base + q < dsteps) consume_dn(wd[q], sd[q]);
-  }
+  };
+  if (packed)
+    down_phase(pq::BoolC<true>{});
+  else
+    down_phase(pq::BoolC<false>{});
   __syncthreads();
   for (int idx = threadIdx.x; idx < (r1 - r0) * a.M; idx += kThreads) {
     const int rl = idx / a.M, m = idx - (idx / a.M) * a.M;

@@ -153,7 +153,7 @@ def _check(pq, bank, x_bits, res, ref, M, k):
     return assert_gemv_close(y, ref["out"], ref["S"], f"out M={M}")
 
 
-@pytest.mark.parametrize("M,E,H,I,k", [(1, 16, 512, 256, 4), (2, 16, 640, 384, 4), (3, 24, 1024, 512, 8),
+@pytest.mark.parametrize("M,E,H,I,k", [(1, 16, 512, 256, 4), (1, 16, 512, 128, 4), (2, 16, 640, 384, 4), (3, 24, 1024, 512, 8),
                                        (8, 32, 1024, 256, 8)])
 def test_moe_small_routed(pq, path, M, E, H, I, k):
     import torch
@@ -204,12 +204,14 @@ def test_moe_rows_bitwise_independent_of_M(pq):
         assert torch.equal(one["topk_w"][0], full["topk_w"][m])
 
 
-@pytest.mark.parametrize("M", [1, 3, 8])
-def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M):
+@pytest.mark.parametrize("M,I", [(1, 512), (3, 512), (8, 512), (1, 256), (2, 128), (1, 384)])
+def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M, I):
     """Both layer kernels compute every h row and every output row with the same
-    lane split and reduction order, so their results are bitwise equal."""
+    lane split and reduction order, so their results are bitwise equal; short
+    down rows (I = 128, 256, 512), which the barrier kernel packs several to a
+    step, reduce inside their lane segment in the same order."""
     import torch
-    E, H, I, k = 24, 1024, 512, 8
+    E, H, k = 24, 1024, 8
     bank = Bank(pq, E, H, I, seed=20 + M)
     x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=20 + M)
     lg = workloads.verify_logits(M, E, workload=workloads.MOE_LAYER, seed=20 + M)

@@ -268,8 +268,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)t, 63);
 }
 
-__device__ __forceinline__ float group_max(float v, int width) {  // within aligned groups of `width` lanes
-  for (int o = width >> 1; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Maximum within aligned groups of `width` lanes (4, 8 or 16), in every lane
+// of the group, by DPP lane swaps inside a 16-lane row (no LDS permute):
+// swap neighbours, then pairs, then mirror the halves of 8 and of 16 lanes.
+// A maximum is the same value in any order.  Every lane of the wave calls it.
+__device__ __forceinline__ float group_max(float v, int width) {
+  constexpr int kQuadSwap1 = 0xB1, kQuadSwap2 = 0x4E;   // quad_perm [1,0,3,2], [2,3,0,1]
+  constexpr int kRowMirror = 0x140, kRowHalfMirror = 0x141;
+  v = fmaxf(v, dpp_f32<kQuadSwap1>(v));
+  v = fmaxf(v, dpp_f32<kQuadSwap2>(v));
+  if (width >= 8) v = fmaxf(v, dpp_f32<kRowHalfMirror>(v));
+  if (width >= 16) v = fmaxf(v, dpp_f32<kRowMirror>(v));
   return v;
 }
 

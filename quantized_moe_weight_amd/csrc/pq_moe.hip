@@ -341,8 +341,9 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
 }
 
 // h of pair slot t of union entry uu: wait until every value is stored (none
-// reads as the zero word), then quantise it into LDS with the layout of the
-// activation quantiser (8 values per lane, 16 lanes per 128-value block).
+// reads as the zero word; a poll loads again only the vectors still missing),
+// then quantise it into LDS with the layout of the activation quantiser (8
+// values per lane, 16 lanes per 128-value block).
 __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq::WsHeader* hdr, int uu, int t,
                                            uint8_t* ha, float* hsc) {
   const int lane = pq::lane_id();
@@ -353,16 +354,24 @@ __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq:
   constexpr int kSB = 4;
   for (int v0 = 0; v0 < nvec; v0 += kSB * pq::kWave) {
     uint4 raw[kSB];
+    bool have[kSB];
+#pragma unroll
+    for (int j = 0; j < kSB; ++j) {
+      have[j] = v0 + j * pq::kWave + lane >= nvec;
+      raw[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
     for (uint32_t it = 0;; ++it) {
       bool miss = false;
 #pragma unroll
       for (int j = 0; j < kSB; ++j) {
         const int idx = v0 + j * pq::kWave + lane;
-        const bool ok = idx < nvec;
-        raw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            hr, (int)(ok ? (uint32_t)(p * nvec + idx) * 16u : pq::kOOB), 0, kAuxSC1));
-        miss |= ok && (has_zero_half(raw[j].x) || has_zero_half(raw[j].y) ||
-                       has_zero_half(raw[j].z) || has_zero_half(raw[j].w));
+        const uint4 r4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            hr, (int)(have[j] ? pq::kOOB : (uint32_t)(p * nvec + idx) * 16u), 0, kAuxSC1));
+        if (!have[j]) {
+          raw[j] = r4;
+          have[j] = !(has_zero_half(r4.x) || has_zero_half(r4.y) || has_zero_half(r4.z) || has_zero_half(r4.w));
+        }
+        miss |= !have[j];
       }
       if (__ballot(miss) == 0ull) break;
       if (it >= a.spin_limit) {

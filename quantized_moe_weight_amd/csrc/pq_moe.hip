@@ -933,7 +933,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
         }
       }
     };
-  #pragma unroll
+#pragma unroll
     for (int q = 0; q < BDD; ++q) issue_dn(wd[q], sd[q]);
 
     // Every h row of the call, quantised into LDS as soon as it is there: h
@@ -954,14 +954,14 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       for (int t0 = 0; t0 < nvec; t0 += kBatch * kThreads) {
         uint4 raw[kBatch];
         bool have[kBatch];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kBatch; ++i) {
           have[i] = t0 + i * kThreads + (int)threadIdx.x >= nvec;
           raw[i] = make_uint4(0u, 0u, 0u, 0u);
         }
         for (uint32_t it = 0;; ++it) {
           bool miss = false;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < kBatch; ++i) {
             const int t = t0 + i * kThreads + (int)threadIdx.x;
             const uint4 r = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
           }
           __builtin_amdgcn_s_sleep(1);
         }
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kBatch; ++i) {
           const int t = t0 + i * kThreads + (int)threadIdx.x;
           const bool valid = t < nvec;
@@ -1004,7 +1004,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     {
       float acc[TP];
       int pr[TP];
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
       int cu = nrows > 0 ? v0 / nrows : 0;
       int cr = v0 - cu * nrows, cc = 0;
@@ -1012,7 +1012,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       auto load_pairs = [&]() {
         const int uu = cu < nU ? cu : 0;
         cnp = ufl(route.unp[uu]);
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[uu][t]);
       };
       load_pairs();
@@ -1026,7 +1026,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
         const uint32_t off = (uint32_t)(cc * pq::kChunk) + plk16;
         if (prr < nr && off < (uint32_t)I) {
           const pq::Bf16x16 wv2 = pq::widen16(w);
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < TP; ++t) {
             if (t < cnp) {
               const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
@@ -1036,7 +1036,7 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
           }
         }
         if (cc == nchI - 1) {               // unit(s) (union entry cu, rows cr ..) done
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < TP; ++t) {
             if (t < cnp) {
               if constexpr (kP) {                     // each segment's last lane holds its row's sum
@@ -1069,13 +1069,13 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       };
       int base = 0;
       for (; base + BDD < dsteps; base += BDD) {     // steady state: every slot refills
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < BDD; ++q) {
           consume_dn(wd[q], sd[q]);
           issue_dn(wd[q], sd[q]);
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int q = 0; q < BDD; ++q)                 // drain
         if (base + q < dsteps) consume_dn(wd[q], sd[q]);
     }

@@ -58,8 +58,9 @@ constexpr int kMaxE = 1024;
 // 1 row).  Measured on the routed layer, both kernels are fastest with 3 / 6
 // (barrier kernel at M=1: 4 / 8 costs 0.7 µs, 8 / 8 4.5 µs; stream kernel at
 // M=4 / M=8: 4 / 8 costs 2 µs, 6 / 10 4–5 µs).
-constexpr int DG = 3, DD = 6;        // stream kernel
-constexpr int kDnClaim = 4;          // stream kernel: down units per claim
+constexpr int DG = 3, DD = 2;        // stream kernel (its down steps carry kDnRows rows)
+constexpr int kDnRows = 2;           // stream kernel: rows of one union entry per down step
+constexpr int kDnClaim = 2;          // stream kernel: down units (row groups) per claim
 constexpr int BDG = 3, BDD = 6;      // barrier kernel
 constexpr uint32_t kSpinLimit = 1u << 20;
 // Polls of an LDS word before a wait inside a block gives up.  Every such word
@@ -873,26 +874,28 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
   float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);   // [row_local][P] fp32
   // The two forms are separate instantiations, so the unpacked steps carry
   // none of the packed bookkeeping.
+  // Unpacked, a step carries two consecutive rows of one entry (kR loads per
+  // lane, the pair's h read and widened once for both), in a ring of half the
+  // depth: the same bytes in flight.
   auto down_phase = [&](auto packed_c) {
     constexpr bool kP = decltype(packed_c)::value;
-    const int pr_rows = kP ? pq::kWave / lpr : 1;
+    constexpr int kR = kP ? 1 : 2;                 // row loads per lane and step
+    constexpr int RD = kP ? BDD : BDD / 2;         // ring depth in steps
+    const int pr_rows = kP ? pq::kWave / lpr : kR; // rows per step
     const int prr = kP ? lane / lpr : 0;           // this lane's row in a packed step
     const uint32_t plk16 = kP ? 16u * (uint32_t)(lane % lpr) : lane16;
-    int dsteps = (v1 - v0) * nchI;
-    if constexpr (kP) {                              // per entry: ceil(rows / pr_rows) steps
-      dsteps = 0;
-      for (int u = v0; u < v1;) {
-        const int e_end = (u / nrows + 1) * nrows;
-        const int n = (v1 < e_end ? v1 : e_end) - u;
-        dsteps += (n + pr_rows - 1) / pr_rows;
-        u += n;
-      }
+    int dsteps = 0;                                // per entry: ceil(rows / pr_rows) row steps
+    for (int u = v0; u < v1;) {
+      const int e_end = (u / nrows + 1) * nrows;
+      const int n = (v1 < e_end ? v1 : e_end) - u;
+      dsteps += (n + pr_rows - 1) / pr_rows * (kP ? 1 : nchI);
+      u += n;
     }
     // (the down steps keep their per-step scale loads: a down step does half
     // a gate_up step's work, and an LDS read in its dependency chain measured
     // slower than the load that arrives with the weights)
-    uint4 wd[BDD];
-    float sd[BDD];
+    uint4 wd[RD][kR];
+    float sd[RD][kR];
     int ju = nrows > 0 ? v0 / nrows : 0;
     int jr = v0 - ju * nrows, jc = 0, dleft = dsteps, uleft = v1 - v0;
     pq::rsrc_t dwr, dsr;
@@ -902,21 +905,23 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       dsr = pq::make_rsrc(dn_scales<EXT>(a, e), (uint32_t)(H * nbI * 4));
     };
     set_dn_expert();
-    auto issue_dn = [&](uint4& w, float& s) {
+    auto issue_dn = [&](uint4 (&w)[kR], float (&s)[kR]) {
       const uint32_t kc = (uint32_t)(jc * pq::kChunk);
-      int nr = 1;                                      // rows of this step
-      if constexpr (kP) {
-        nr = nrows - jr < uleft ? nrows - jr : uleft;
-        nr = nr < pr_rows ? nr : pr_rows;
+      int nr = nrows - jr < uleft ? nrows - jr : uleft;   // rows of this step
+      nr = nr < pr_rows ? nr : pr_rows;
+#pragma unroll
+      for (int j = 0; j < kR; ++j) {
+        const int rj = kP ? prr : j;                   // this lane's row of the step
+        const bool ok = dleft > 0 && rj < nr && kc + plk16 < (uint32_t)I;
+        const uint32_t row = (uint32_t)(r0 + jr + rj);
+        w[j] = pq::buf_load16_nt(dwr, ok ? row * (uint32_t)I + kc + plk16 : pq::kOOB);
+        const uint32_t soff = kP ? (row * (uint32_t)nbI + plk16 / pq::kBlock) * 4u
+                                 : (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4;
+        s[j] = pq::buf_load_f32_nt(dsr, ok ? soff : pq::kOOB);
       }
-      const bool ok = dleft > 0 && prr < nr && kc + plk16 < (uint32_t)I;
-      const uint32_t row = (uint32_t)(r0 + jr + prr);
-      w = pq::buf_load16_nt(dwr, ok ? row * (uint32_t)I + kc + plk16 : pq::kOOB);
-      const uint32_t soff = kP ? (row * (uint32_t)nbI + plk16 / pq::kBlock) * 4u
-                               : (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4;
-      s = pq::buf_load_f32_nt(dsr, ok ? soff : pq::kOOB);
       --dleft;
-      if constexpr (kP) {
+      if (kP || ++jc == nchI) {                      // (packed rows are one chunk)
+        jc = 0;
         uleft -= nr;
         jr += nr;
         if (jr == nrows) {
@@ -924,17 +929,10 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
           ++ju;
           set_dn_expert();
         }
-      } else if (++jc == nchI) {
-        jc = 0;
-        if (++jr == nrows) {
-          jr = 0;
-          ++ju;
-          set_dn_expert();
-        }
       }
     };
 #pragma unroll
-    for (int q = 0; q < BDD; ++q) issue_dn(wd[q], sd[q]);
+    for (int q = 0; q < RD; ++q) issue_dn(wd[q], sd[q]);
 
     // Every h row of the call, quantised into LDS as soon as it is there: h
     // is stored bit-inverted into a region that is zero between calls, so a
@@ -1002,10 +1000,12 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
     __syncthreads();
 
     {
-      float acc[TP];
+      float acc[kR][TP];
       int pr[TP];
 #pragma unroll
-      for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
+      for (int j = 0; j < kR; ++j)
+#pragma unroll
+        for (int t = 0; t < TP; ++t) acc[j][t] = 0.0f;
       int cu = nrows > 0 ? v0 / nrows : 0;
       int cr = v0 - cu * nrows, cc = 0;
       int cnp = 0;
@@ -1017,40 +1017,47 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
       };
       load_pairs();
       int cleft = v1 - v0;
-      auto consume_dn = [&](const uint4& w, float sw) {
-        int nr = 1;
-        if constexpr (kP) {
-          nr = nrows - cr < cleft ? nrows - cr : cleft;
-          nr = nr < pr_rows ? nr : pr_rows;
-        }
+      auto consume_dn = [&](const uint4 (&w)[kR], const float (&sw)[kR]) {
+        int nr = nrows - cr < cleft ? nrows - cr : cleft;
+        nr = nr < pr_rows ? nr : pr_rows;
         const uint32_t off = (uint32_t)(cc * pq::kChunk) + plk16;
         if (prr < nr && off < (uint32_t)I) {
-          const pq::Bf16x16 wv2 = pq::widen16(w);
+          pq::Bf16x16 wv[kR];
+#pragma unroll
+          for (int j = 0; j < kR; ++j) wv[j] = pq::widen16(w[j]);
 #pragma unroll
           for (int t = 0; t < TP; ++t) {
             if (t < cnp) {
               const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(act + (size_t)pr[t] * I + off));
               const float hsc = acts[pr[t] * nbI + off / pq::kBlock];
-              acc[t] = fmaf(pq::dot16(wv2, hv), sw * hsc, acc[t]);
+#pragma unroll
+              for (int j = 0; j < kR; ++j) acc[j][t] = fmaf(pq::dot16(wv[j], hv), sw[j] * hsc, acc[j][t]);
             }
           }
         }
-        if (cc == nchI - 1) {               // unit(s) (union entry cu, rows cr ..) done
+        if (kP || cc == nchI - 1) {         // unit(s) (union entry cu, rows cr ..) done
 #pragma unroll
           for (int t = 0; t < TP; ++t) {
             if (t < cnp) {
               if constexpr (kP) {                     // each segment's last lane holds its row's sum
-                const float y = pq::segment_sum(acc[t], lpr);
+                const float y = pq::segment_sum(acc[0][t], lpr);
                 if (lane % lpr == lpr - 1 && prr < nr) ybuf[(cr + prr) * P2 + pr[t]] = y;
               } else {
-                const float y = pq::wave_sum(acc[t]);
-                if (lane == 0) ybuf[cr * P2 + pr[t]] = y;
+#pragma unroll
+                for (int j = 0; j < kR; ++j) {
+                  if (j < nr) {
+                    const float y = pq::wave_sum(acc[j][t]);
+                    if (lane == 0) ybuf[(cr + j) * P2 + pr[t]] = y;
+                  }
+                }
               }
             }
-            acc[t] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kR; ++j) acc[j][t] = 0.0f;
           }
         }
-        if constexpr (kP) {
+        if (kP || ++cc == nchI) {
+          cc = 0;
           cleft -= nr;
           cr += nr;
           if (cr == nrows) {
@@ -1058,25 +1065,18 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
             ++cu;
             load_pairs();
           }
-        } else if (++cc == nchI) {
-          cc = 0;
-          if (++cr == nrows) {
-            cr = 0;
-            ++cu;
-            load_pairs();
-          }
         }
       };
       int base = 0;
-      for (; base + BDD < dsteps; base += BDD) {     // steady state: every slot refills
+      for (; base + RD < dsteps; base += RD) {       // steady state: every slot refills
 #pragma unroll
-        for (int q = 0; q < BDD; ++q) {
+        for (int q = 0; q < RD; ++q) {
           consume_dn(wd[q], sd[q]);
           issue_dn(wd[q], sd[q]);
         }
       }
 #pragma unroll
-      for (int q = 0; q < BDD; ++q)                 // drain
+      for (int q = 0; q < RD; ++q)                  // drain
         if (base + q < dsteps) consume_dn(wd[q], sd[q]);
     }
   };
@@ -1299,7 +1299,8 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   }
   if (lane == 0) atomicSub(&s_gu_busy, 1u);   // this wave no longer reads x
   know_routes();                               // (its last claim already waited)
-  const int dn_total = nU * nrows;
+  const int nrp = (nrows + kDnRows - 1) / kDnRows;   // down units: kDnRows consecutive rows of one entry
+  const int dn_total = nU * nrp;
 
   // h staging: the (entry, pair) items of the block are quantised into LDS in
   // union order, each by the wave that claims it; a wave out of gate_up units
@@ -1324,16 +1325,22 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   // down: a ring of DD steps (one 1 KB chunk of a down row); a cycle's slots
   // are consumed once the h of their union entries is in LDS.
   {
-    uint4 wd[DD];
-    float sw[DD];
+    // A down step carries kDnRows consecutive rows of one union entry: every
+    // lane loads the same 16 bytes of each and reads and widens each pair's
+    // h once for all of them, which divides the LDS reads and h conversions
+    // per weight byte where several tokens share an expert.  Each row's sums
+    // are the same additions in the same order as for a row alone, so the
+    // results equal the barrier kernel's bit for bit.
+    uint4 wd[DD][kDnRows];
+    float sw[DD][kDnRows];
     uint32_t sd[DD];
     int ucur = 0, crow = 0, cstep = nchI, ce = -1;
     bool more = true;
     pq::rsrc_t wr = pq::make_rsrc(a.w2, 0u), sr = pq::make_rsrc(a.s2, 0u);
-    // a claim takes kDnClaim consecutive units (rows of one entry, mostly):
-    // one LDS round trip per few rows instead of per row (measured best at 4)
+    // a claim takes kDnClaim consecutive units (row groups of one entry,
+    // mostly): one LDS round trip per few rows instead of per row
     int dk_left = 0, dk_base = 0;
-    auto issue_dn = [&](uint4& w, float& s, uint32_t& d) {
+    auto issue_dn = [&](uint4 (&w)[kDnRows], float (&s)[kDnRows], uint32_t& d) {
       if (cstep == nchI && more) {            // take the block's next unit
         if (dk_left == 0) {
           dk_base = kDnClaim * wave_claim(&s_dnext);
@@ -1343,8 +1350,8 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
         --dk_left;
         more = tt < dn_total;
         if (more) {
-          ucur = tt / nrows;
-          crow = tt - ucur * nrows;
+          ucur = tt / nrp;
+          crow = kDnRows * (tt - ucur * nrp);
           cstep = 0;
           const int e = ufl(route.uexp[ucur]);
           if (e != ce) {
@@ -1356,19 +1363,25 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
       }
       const uint32_t kc = (uint32_t)(cstep * pq::kChunk);
       const bool ok = more && kc + lane16 < (uint32_t)I;
-      const uint32_t row = (uint32_t)(r0 + crow);
-      w = pq::buf_load16_nt(wr, ok ? row * (uint32_t)I + kc + lane16 : pq::kOOB);
-      s = pq::buf_load_f32_nt(sr, ok ? (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+#pragma unroll
+      for (int j = 0; j < kDnRows; ++j) {
+        const bool okj = ok && crow + j < nrows;
+        const uint32_t row = (uint32_t)(r0 + crow + j);
+        w[j] = pq::buf_load16_nt(wr, okj ? row * (uint32_t)I + kc + lane16 : pq::kOOB);
+        s[j] = pq::buf_load_f32_nt(sr, okj ? (row * (uint32_t)nbI + kc / pq::kBlock) * 4u + lane_blk4 : pq::kOOB);
+      }
       d = more ? 0x80000000u | ((uint32_t)cstep << 23) | ((uint32_t)ucur << 16) | (uint32_t)crow : 0u;
       if (more) ++cstep;
     };
 
-    float acc[TP];
+    float acc[kDnRows][TP];
     int pr[TP];
 #pragma unroll
-    for (int t = 0; t < TP; ++t) acc[t] = 0.0f;
+    for (int j = 0; j < kDnRows; ++j)
+#pragma unroll
+      for (int t = 0; t < TP; ++t) acc[j][t] = 0.0f;
     int pairs_u = -1, cnp = 0, ready_next = 0;
-    auto consume_dn = [&](const uint4& w, float s, uint32_t d) {
+    auto consume_dn = [&](const uint4 (&w)[kDnRows], const float (&s)[kDnRows], uint32_t d) {
       if (!(d >> 31)) return;
       const int step = (int)((d >> 23) & 255u), uu = (int)((d >> 16) & 127u), row = (int)(d & 0xFFFFu);
       if (uu != pairs_u) {
@@ -1379,24 +1392,30 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
       }
       const uint32_t off = (uint32_t)(step * pq::kChunk) + lane16;
       if (off < (uint32_t)I) {
-        const pq::Bf16x16 wv2 = pq::widen16(w);
+        pq::Bf16x16 wj[kDnRows];
+#pragma unroll
+        for (int j = 0; j < kDnRows; ++j) wj[j] = pq::widen16(w[j]);
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
           if (t < cnp) {
             const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(ha + (size_t)pr[t] * I + off));
             const float hs = hsc[pr[t] * nbI + off / pq::kBlock];
-            acc[t] = fmaf(pq::dot16(wv2, hv), s * hs, acc[t]);
+#pragma unroll
+            for (int j = 0; j < kDnRows; ++j) acc[j][t] = fmaf(pq::dot16(wj[j], hv), s[j] * hs, acc[j][t]);
           }
         }
       }
-      if (step == nchI - 1) {             // unit (u, row) done
+      if (step == nchI - 1) {             // unit (u, rows row .. row + kDnRows - 1) done
 #pragma unroll
-        for (int t = 0; t < TP; ++t) {
-          if (t < cnp) {
-            const float y = pq::wave_sum(acc[t]);
-            if (lane == 0) ybuf[row * P2 + pr[t]] = y;
+        for (int j = 0; j < kDnRows; ++j) {
+#pragma unroll
+          for (int t = 0; t < TP; ++t) {
+            if (t < cnp && row + j < nrows) {
+              const float y = pq::wave_sum(acc[j][t]);
+              if (lane == 0) ybuf[(row + j) * P2 + pr[t]] = y;
+            }
+            acc[j][t] = 0.0f;
           }
-          acc[t] = 0.0f;
         }
       }
     };

@@ -29,7 +29,7 @@ Stream kernel (three tokens or more):
     polls the pair's h (every unit of that entry, whichever block owns it)
     and counts the entry staged; with aliased LDS it first waits until no wave
     of the block is still in gate_up;
-  * then it claims down units (entry, row), four consecutive ones per claim,
+  * then it claims down units (entry, row pair), two consecutive ones per claim,
     from a third counter and, before consuming one, waits until its entry is
     fully staged;
   * the last block to exit clears h and the exit counter.
@@ -140,7 +140,7 @@ def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, cle
 # stream kernel
 # ---------------------------------------------------------------------------
 
-DN_CLAIM = 4     # down units per claim in the stream kernel
+DN_CLAIM = 2     # down units (row pairs) per claim in the stream kernel
 
 
 def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: bool, limit: int, log: dict):

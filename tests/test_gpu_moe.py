@@ -204,14 +204,17 @@ def test_moe_rows_bitwise_independent_of_M(pq):
         assert torch.equal(one["topk_w"][0], full["topk_w"][m])
 
 
-@pytest.mark.parametrize("M,I", [(1, 512), (3, 512), (8, 512), (1, 256), (2, 128), (1, 384)])
-def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M, I):
+@pytest.mark.parametrize("M,I,H", [(1, 512, 1024), (3, 512, 1024), (8, 512, 1024), (1, 256, 1024), (2, 128, 1024),
+                                   (1, 384, 1024), (3, 2048, 640), (1, 1536, 640), (8, 1024, 896)])
+def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M, I, H):
     """Both layer kernels compute every h row and every output row with the same
     lane split and reduction order, so their results are bitwise equal; short
     down rows (I = 128, 256, 512), which the barrier kernel packs several to a
-    step, reduce inside their lane segment in the same order."""
+    step, reduce inside their lane segment in the same order, and longer rows,
+    which both kernels carry two to a step, keep each row's order too (H = 640
+    and 896 give blocks an odd number of down rows, so some steps carry one)."""
     import torch
-    E, H, k = 24, 1024, 8
+    E, k = 24, 8
     bank = Bank(pq, E, H, I, seed=20 + M)
     x = workloads.activation_bf16(M, H, workload=workloads.MOE_LAYER, seed=20 + M)
     lg = workloads.verify_logits(M, E, workload=workloads.MOE_LAYER, seed=20 + M)
@@ -233,6 +236,9 @@ def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M, I):
     assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
     assert torch.equal(a["h"].view(torch.int16), b["h"].view(torch.int16))
     assert torch.equal(a["hq"], b["hq"]) and torch.equal(a["hs"], b["hs"])
+    if H != 1024:                          # ragged row counts: against the oracle too
+        ref = oracle.moe_layer(x, bank.expert, logits=lg, top_k=k)
+        _check(pq, bank, x, a, ref, M, k)
 
 
 @pytest.mark.parametrize("M,E,H,I,k,shared", [(1, 16, 1024, 512, 4, False), (2, 16, 640, 384, 4, True),

@@ -111,6 +111,10 @@ struct MoeArgs {
   uint32_t spin_limit;
   int xs_off, ha_off, hs_off, yb_off;   // byte offsets of the LDS regions
   int alias;        // h codes and scales reuse the x region
+  // stream kernel: x codes at xa_off; h codes by staging slot (union order),
+  // slot s at ha_off + s * I; with alias, the slots from hsplit on overlay the
+  // x codes
+  int xa_off, hsplit;
   int sc_off;       // barrier kernel: LDS byte offset of the per-wave scale windows, or -1
 };
 
@@ -121,6 +125,7 @@ struct Route {
   int unp[kMaxUnion];             // number of (token, slot) pairs routed to u
   int upairs[kMaxUnion][kMaxM];   // their pair indices p = m * top_k + j, ascending
   int items[kMaxPairs2];          // (entry u, pair slot t) = u | t << 8, in union order
+  int ustart[kMaxUnion];          // index in items of entry u's first pair slot
   int nU, nitems;
 };
 
@@ -328,6 +333,7 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
     if (slot == 0 && !dup) {
       r.uexp[us] = id;
       r.unp[us] = n;
+      r.ustart[us] = sh * a.M + below;
     }
     if (!dup) {
       r.upairs[us][slot] = lane;
@@ -344,9 +350,10 @@ __device__ void build_union(const MoeArgs& a, Route& r, pq::WsHeader* hdr, uint3
 // h of pair slot t of union entry uu: wait until every value is stored (none
 // reads as the zero word; a poll loads again only the vectors still missing),
 // then quantise it into LDS with the layout of the activation quantiser (8
-// values per lane, 16 lanes per 128-value block).
+// values per lane, 16 lanes per 128-value block): the codes to hrow (the
+// pair's I bytes), the scales to hsc by pair index.
 __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq::WsHeader* hdr, int uu, int t,
-                                           uint8_t* ha, float* hsc) {
+                                           uint8_t* hrow, float* hsc) {
   const int lane = pq::lane_id();
   const int I = a.I;
   const int p = ufl(r.upairs[uu][t]);
@@ -392,7 +399,7 @@ __device__ __forceinline__ void stage_pair(const MoeArgs& a, const Route& r, pq:
       if (valid) {
         const int gi = p * nvec + idx;
         const uint2 c8 = pq::fp8_codes8(v, sc);
-        reinterpret_cast<uint2*>(ha)[gi] = c8;
+        reinterpret_cast<uint2*>(hrow)[idx] = c8;
         if ((lane & 15) == 0) hsc[gi / 16] = sc;
         if (blockIdx.x == 0) {
           if (a.hq_dbg) reinterpret_cast<uint2*>(a.hq_dbg)[gi] = c8;
@@ -414,6 +421,7 @@ __device__ void single_token_union(const MoeArgs& a, Route& r, int sh) {
     r.unp[us] = 1;
     r.upairs[us][0] = lane;
     r.items[sh + lane] = us;
+    r.ustart[us] = sh + lane;
   }
   if (lane == 0) {
     r.nitems = a.top_k + sh;
@@ -433,6 +441,7 @@ __device__ void shared_entry(const MoeArgs& a, Route& r) {
   if (lane == 0) {
     r.uexp[0] = a.E;
     r.unp[0] = a.M;
+    r.ustart[0] = 0;
   }
 }
 
@@ -1149,9 +1158,9 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   const uint32_t lane16 = 16u * (uint32_t)lane;
   const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
 
-  uint8_t* xa = smem;                                          // x codes   [M][H]
+  uint8_t* xa = smem + a.xa_off;                               // x codes   [M][H]
   float* xsc = reinterpret_cast<float*>(smem + a.xs_off);      // x scales  [M][H/128]
-  uint8_t* ha = smem + a.ha_off;                               // h codes   [P2][I]
+  uint8_t* ha = smem + a.ha_off;                               // h codes   [nitems][I] by staging slot
   float* hsc = reinterpret_cast<float*>(smem + a.hs_off);      // h scales  [P2][I/128]
   float* ybuf = reinterpret_cast<float*>(smem + a.yb_off);     // y partials [row][P2]
 
@@ -1315,9 +1324,9 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
       if (jj >= nitems) break;
       const int it = ufl(route.items[jj]);
       const int v = it & 255, t = it >> 8;
-      if (a.alias)               // h codes overwrite x codes: the block must be past gate_up
+      if (a.alias && jj >= a.hsplit)   // these h codes overwrite x codes: the block must be past gate_up
         lds_wait(&s_gu_busy, [](uint32_t v) { return v == 0u; }, hdr);
-      stage_pair(a, route, hdr, v, t, ha, hsc);
+      stage_pair(a, route, hdr, v, t, ha + (size_t)jj * I, hsc);
       if (lane == 0) __hip_atomic_fetch_add(&s_staged[v], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
@@ -1380,13 +1389,14 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
     for (int j = 0; j < kDnRows; ++j)
 #pragma unroll
       for (int t = 0; t < TP; ++t) acc[j][t] = 0.0f;
-    int pairs_u = -1, cnp = 0, ready_next = 0;
+    int pairs_u = -1, cnp = 0, s0 = 0, ready_next = 0;
     auto consume_dn = [&](const uint4 (&w)[kDnRows], const float (&s)[kDnRows], uint32_t d) {
       if (!(d >> 31)) return;
       const int step = (int)((d >> 23) & 255u), uu = (int)((d >> 16) & 127u), row = (int)(d & 0xFFFFu);
       if (uu != pairs_u) {
         pairs_u = uu;
         cnp = ufl(route.unp[uu]);
+        s0 = ufl(route.ustart[uu]);            // the entry's staging slots s0 .. s0 + cnp - 1
 #pragma unroll
         for (int t = 0; t < TP; ++t) pr[t] = ufl(route.upairs[uu][t]);
       }
@@ -1398,7 +1408,7 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
           if (t < cnp) {
-            const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(ha + (size_t)pr[t] * I + off));
+            const pq::Bf16x16 hv = pq::widen16(*reinterpret_cast<const uint4*>(ha + (size_t)(s0 + t) * I + off));
             const float hs = hsc[pr[t] * nbI + off / pq::kBlock];
 #pragma unroll
             for (int j = 0; j < kDnRows; ++j) acc[j][t] = fmaf(pq::dot16(wj[j], hv), s[j] * hs, acc[j][t]);
@@ -1496,7 +1506,7 @@ constexpr size_t kLdsBytes = 160 * 1024;
 
 struct MoePlan {
   size_t lds;
-  int xs_off, ha_off, hs_off, yb_off, alias, sc_off;
+  int xs_off, ha_off, hs_off, yb_off, alias, sc_off, xa_off, hsplit;
   size_t off_h, ws_total;
 };
 
@@ -1514,8 +1524,13 @@ int moe_path(int M) {
 // num_cus bounds the rows a block can own (the grid has one block per CU);
 // num_cus <= 0 checks the shape and sizes the workspace only.  The stream
 // kernel gives x and h separate LDS regions when both fit (a wave may stage h
-// while others still read x); otherwise, and always in the barrier kernel,
-// h reuses the x region once the block is past gate_up.  The workspace covers
+// while others still read x).  Otherwise it places as many h rows (staging
+// slots, in union order) as fit before the x codes, followed by the x codes,
+// the scales and y; the remaining slots continue over the x codes and wait
+// for the block to be past gate_up, so the first experts' h is staged while
+// the last gate_up units still stream.  Where even that does not fit (or PQ_MOE_ALIAS=full),
+// and always in the barrier kernel, h and its scales reuse the x region once
+// the block is past gate_up.  The workspace covers
 // both kernels: the stream kernel's h in the zero-between-calls region, the
 // barrier kernel's in the data region.
 // The logit exchange sits at the end of the zero-between-calls region.
@@ -1538,17 +1553,33 @@ int moe_plan(int M, int H, int I, int E, int top_k, int num_cus, int path, MoePl
   p->xs_off = (int)xb;
   p->alias = 0;
   p->sc_off = -1;
+  p->xa_off = 0;
+  p->hsplit = (int)P;
   if (num_cus > 0) {
     const size_t yb = ((size_t)H + num_cus - 1) / num_cus * P * 4;
     const size_t sep = xb + xsb + hb + hsb + yb;
+    const size_t apart = xb + xsb + hsb + yb;   // all but the h codes
+    const char* fa = getenv("PQ_MOE_ALIAS");
+    const bool full = fa && strcmp(fa, "full") == 0;
+    const size_t room = apart + kStaticLds < kLdsBytes ? (kLdsBytes - kStaticLds - apart) / I : 0;
     if (path == kPathStream && sep + kStaticLds <= kLdsBytes) {
       p->ha_off = (int)(xb + xsb);
       p->hs_off = (int)(xb + xsb + hb);
       p->yb_off = (int)(xb + xsb + hb + hsb);
       p->lds = sep;
+    } else if (path == kPathStream && !full && room < P && (P - room) * I <= xb) {
+      p->alias = 1;
+      p->hsplit = (int)room;
+      p->ha_off = 0;
+      p->xa_off = (int)(room * I);
+      p->xs_off = (int)(room * I + xb);
+      p->hs_off = (int)(room * I + xb + xsb);
+      p->yb_off = (int)(room * I + xb + xsb + hsb);
+      p->lds = room * I + apart;
     } else {
       const size_t cb = xb > hb ? xb : hb, sb = xsb > hsb ? xsb : hsb;
       p->alias = 1;
+      p->hsplit = 0;
       p->xs_off = (int)cb;
       p->ha_off = 0;
       p->hs_off = (int)cb;
@@ -1721,6 +1752,8 @@ int layer_call(const uint16_t* x, int M, int H, const uint16_t* router_w, float*
   a.spin_limit = kSpinLimit;
   a.xs_off = pl.xs_off; a.ha_off = pl.ha_off; a.hs_off = pl.hs_off; a.yb_off = pl.yb_off;
   a.alias = pl.alias;
+  a.xa_off = pl.xa_off;
+  a.hsplit = pl.hsplit;
   a.sc_off = pl.sc_off;
   const char* sce = getenv("PQ_MOE_SCALES");          // "step": per-step scale loads (for tests)
   if (sce && strcmp(sce, "step") == 0) a.sc_off = -1;

@@ -27,8 +27,9 @@ Stream kernel (three tokens or more):
   * a wave out of gate_up units leaves the block's LDS busy count, then claims
     staging items (union entry, pair) from a second LDS counter; the stager
     polls the pair's h (every unit of that entry, whichever block owns it)
-    and counts the entry staged; with aliased LDS it first waits until no wave
-    of the block is still in gate_up;
+    and counts the entry staged; with aliased LDS, an item whose staging slot
+    (its index in union order) is hsplit or later overlays the x codes, and
+    its stager first waits until no wave of the block is still in gate_up;
   * then it claims down units (entry, row pair), two consecutive ones per claim,
     from a third counter and, before consuming one, waits until its entry is
     fully staged;
@@ -143,10 +144,16 @@ def barrier_block(grid: Grid, b: int, W: int, U: int, limit: int, log: dict, cle
 DN_CLAIM = 2     # down units (row pairs) per claim in the stream kernel
 
 
-def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: bool, limit: int, log: dict):
+def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: bool, limit: int, log: dict,
+                 hsplit: int = 0, room: int | None = None):
     """Waves of block b of the stream kernel.  nU union entries of I h-rows
     each; unp[u] pairs routed to entry u; the block's down rows are one row
-    per entry here (the row count changes nothing in the protocol)."""
+    per entry here (the row count changes nothing in the protocol).  With
+    alias, the LDS holds `room` staging slots apart from the x codes; the
+    later slots overlay the x codes that gate_up reads.  The kernel makes the
+    stagers of slots hsplit and later wait for the end of gate_up (its plan
+    sets hsplit = room; a different value models a wrong plan)."""
+    room = hsplit if room is None else room
     G = grid.G
     total = nU * I
     items = [(u, t) for u in range(nU) for t in range(unp[u])]
@@ -175,9 +182,14 @@ def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: 
             if j >= len(items):
                 break
             u, t = items[j]
-            if alias:
+            if alias and j >= hsplit:
                 yield from wait_until(lambda: lds["gu_busy"] == 0, grid, limit)
             ok = yield from wait_until(lambda: all(grid.get(("h", u * I + i)) for i in range(I)), grid, limit)
+            if lds["gu_busy"] > 0:                     # the slot's codes are written now
+                if alias and j >= room:
+                    log["x_clobbered"].append((b, j))
+                else:
+                    log["staged_during_gate_up"] += 1
             if ok:
                 log["staged"].append((b, u, t))
             lds["staged"][u] += 1
@@ -217,8 +229,9 @@ def stream_block(grid: Grid, b: int, W: int, nU: int, I: int, unp: list, alias: 
 # ---------------------------------------------------------------------------
 
 def run(kernel: str, G: int, W: int = 4, *, U: int = 12, nU: int = 3, I: int = 4, unp=None, alias=False,
-        limit: int = 10 ** 6, seed: int = 0, late_block: int | None = None, max_steps: int = 10 ** 8,
-        grid: Grid | None = None, clear_h: bool = True):
+        hsplit: int = 0, room: int | None = None, limit: int = 10 ** 6, seed: int = 0,
+        late_block: int | None = None,
+        max_steps: int = 10 ** 8, grid: Grid | None = None, clear_h: bool = True):
     """Run one launch of the model; returns (grid, log, steps).
 
     late_block: that block is not resident until every other block has ended
@@ -228,13 +241,14 @@ def run(kernel: str, G: int, W: int = 4, *, U: int = 12, nU: int = 3, I: int = 4
     workspace); a fresh, zeroed one by default."""
     rng = random.Random(seed)
     grid = grid if grid is not None else Grid(G)
-    log = {"h_written": {}, "n_written": 0, "early_release": [], "staged": [], "cleared_by": []}
+    log = {"h_written": {}, "n_written": 0, "early_release": [], "staged": [], "cleared_by": [],
+           "x_clobbered": [], "staged_during_gate_up": 0}
     blocks = []
     for b in range(G):
         if kernel == "barrier":
             blocks.append(barrier_block(grid, b, W, U, limit, log, clear_h))
         else:
-            blocks.append(stream_block(grid, b, W, nU, I, unp or [1] * nU, alias, limit, log))
+            blocks.append(stream_block(grid, b, W, nU, I, unp or [1] * nU, alias, limit, log, hsplit, room))
     live = [(b, g) for b, ws in enumerate(blocks) for g in ws if b != late_block]
     steps = 0
     while live:

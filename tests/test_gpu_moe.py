@@ -367,20 +367,35 @@ def test_moe_full_size_layer(pq, path, M):
     print(f"full-size M={M} ({path}): union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
 
 
-@pytest.mark.parametrize("M,kernel,alias", [(2, "barrier", True), (8, "stream", True)])
-def test_moe_full_size_verify(pq, M, kernel, alias):
+@pytest.mark.parametrize("M,kernel,alias,layout", [(2, "barrier", True, None), (8, "stream", True, "split"),
+                                                   (8, "stream", True, "full")])
+def test_moe_full_size_verify(pq, monkeypatch, M, kernel, alias, layout):
     """Speculative verify at the real shape (256 experts, hidden 6144,
     intermediate 2048, top-8, equicorrelated routing): M = 2 on the library's
     default kernel for two tokens (which always stages h over x, after its
-    grid-wide release), M = 8 on the stream kernel with the re-quantised h
-    overwriting the quantised x in LDS while other waves may still stream
-    gate_up (x, h and the output partials of 8 tokens do not fit side by
-    side); the test first checks that the library really takes that layout.  Every output element is checked,
-    the re-quantised h bit for bit."""
+    grid-wide release), M = 8 on the stream kernel, where x, h and the output
+    partials of 8 tokens do not fit side by side: by default ("split") the
+    first h rows in union order sit apart from x and are staged while other
+    waves still stream gate_up, and only the rest overwrite the quantised x;
+    with PQ_MOE_ALIAS=full ("full") every h row does.  The test first checks
+    that the library really takes that layout.  Every output element is
+    checked, the re-quantised h bit for bit."""
     import torch
     shp = workloads.MOE_SHAPE
+    if layout == "full":
+        monkeypatch.setenv("PQ_MOE_ALIAS", "full")
     cfg = pq.moe_layer_config(M, shp.H, shp.I, shp.E, shp.top_k)
     assert cfg["kernel"] == kernel and cfg["alias"] == alias, cfg
+    if layout is not None:
+        P = M * shp.top_k
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        yb = -(-shp.H // cus) * P * 4
+        xb, xsb, hsb = M * shp.H, M * (shp.H // 128) * 4, P * (shp.I // 128) * 4
+        if layout == "full":     # h codes over x codes, h scales over x scales
+            assert cfg["lds_bytes"] == max(xb, P * shp.I) + max(xsb, hsb) + yb, cfg
+        else:                    # slots apart from x first, then over x; the scales apart
+            apart = (cfg["lds_bytes"] - (xb + xsb + hsb + yb)) // shp.I
+            assert P // 2 <= apart < P and (P - apart) * shp.I <= xb, cfg
     bank = Bank(pq, shp.E, shp.H, shp.I, workload=workloads.MOE_LAYER, seed=0)
     x = workloads.activation_bf16(M, shp.H, workload=workloads.MOE_VERIFY, seed=M)
     lg = workloads.verify_logits(M, shp.E, seed=M)
@@ -397,7 +412,7 @@ def test_moe_full_size_verify(pq, M, kernel, alias):
         one = pq.moe_decode_layer(xt[m:m + 1].contiguous(), bank.w13, bank.s13, bank.w2, bank.s2,
                                   logits=lt[m:m + 1].contiguous(), top_k=shp.top_k)
         assert torch.equal(one["out"][0].view(torch.int16), res["out"][m].view(torch.int16))
-    print(f"full-size verify M={M} ({kernel}, alias={alias}): union {len(oracle.union_of_experts(ids))} experts, "
+    print(f"full-size verify M={M} ({kernel}, alias={alias}, {layout}): union {len(oracle.union_of_experts(ids))} experts, "
           f"worst |err|/S {worst:.2e}")
 
 

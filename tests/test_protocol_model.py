@@ -27,6 +27,7 @@ def _clean_stream(grid, log, nU, I, unp, G):
     assert len(log["staged"]) == G * sum(unp), "every block stages every pair once"
     assert len(log["cleared_by"]) == 1
     assert all(v == 0 for v in grid.mem.values())
+    assert not log["x_clobbered"], "h codes written over x while a wave still read x"
 
 
 def test_every_grid_size_covers_every_unit_once():
@@ -70,6 +71,34 @@ def test_stream_protocol_small_grids(G, alias):
         unp = [1, 3, 2]
         grid, log, _ = pm.run("stream", G, W=4, nU=3, I=4, unp=unp, alias=alias, seed=seed)
         _clean_stream(grid, log, 3, 4, unp, G)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 7, 16, 64])
+@pytest.mark.parametrize("hsplit", [1, 3, 5])
+def test_stream_protocol_partial_alias(G, hsplit):
+    """Aliased LDS with the first hsplit staging slots outside the x codes:
+    those are staged while waves of the block still stream gate_up (in some
+    interleaving), the later ones only once every wave is past it, and no run
+    writes h codes over x early, deadlocks or leaves the workspace dirty."""
+    unp = [2, 1, 3]
+    early = 0
+    for seed in range(4):
+        grid, log, _ = pm.run("stream", G, W=4, nU=3, I=4, unp=unp, alias=True, hsplit=hsplit, seed=seed)
+        _clean_stream(grid, log, 3, 4, unp, G)
+        early += log["staged_during_gate_up"]
+    assert early > 0, "no slot before the split was staged during gate_up"
+
+
+def test_stream_protocol_model_catches_an_unguarded_slot():
+    """A plan whose split lies past the slots that really fit apart from x (so
+    stagers of slots over the x codes skip the wait) shows up as h written
+    over x while a wave still streams gate_up."""
+    unp = [2, 1, 3]
+    clobbered = 0
+    for seed in range(8):
+        _, log, _ = pm.run("stream", 3, W=4, nU=3, I=4, unp=unp, alias=True, hsplit=6, room=1, seed=seed)
+        clobbered += len(log["x_clobbered"])
+    assert clobbered > 0, "the model failed to show the unguarded slot"
 
 
 @pytest.mark.parametrize("G", [100, 256, 1000, 4096])

@@ -546,14 +546,20 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
   const int nrw = e1 - e0 < kWaves / 2 ? e1 - e0 : kWaves / 2;
   // waves that route before quantising (given logits or ids)
   const int nrt = router ? 0 : (a.routed ? a.M : 1);
+  const bool one_token = a.routed && a.M == 1;       // block-uniform
+  // given logits of several tokens: the last wave builds the union of their
+  // experts as soon as the routing waves are done, while the others quantise x
+  const bool early_union = TP > 1 && !router && a.routed && !one_token;   // (TP = 1: one token)
+  const int nub = early_union ? 1 : 0;
   const long totx8 = (long)a.M * H / 8;
-  const int qthreads = kThreads - (nrt + nrw) * pq::kWave;
-  // when the other waves cannot cover x in one pass, every wave takes a share
-  // (the routing and router waves after their own work)
+  const int qthreads = kThreads - (nrt + nrw + nub) * pq::kWave;
+  // when the other waves cannot cover x in one pass, every wave but the union
+  // builder takes a share (the routing and router waves after their own work)
   const bool xq_all = totx8 > (long)qthreads;
-  const bool qwave = wv >= nrt && wv < kWaves - nrw;
-  const int tq = xq_all ? (int)threadIdx.x : (qwave ? (int)threadIdx.x - nrt * pq::kWave : -1);
-  const int nq = xq_all ? kThreads : qthreads;
+  const bool qwave = wv >= nrt && wv < kWaves - nrw - nub;
+  const int nq = xq_all ? kThreads - nub * pq::kWave : qthreads;
+  const int tq = xq_all ? ((int)threadIdx.x < nq ? (int)threadIdx.x : -1)
+                        : (qwave ? (int)threadIdx.x - nrt * pq::kWave : -1);
   const pq::rsrc_t xr = pq::make_rsrc(a.x, (uint32_t)(a.M * H * 2));
   // enough loads in flight for the whole of x at H = 6144 up to M = 4 (16 bytes each)
   constexpr int kXPre = TP == 1 ? 1 : TP == 2 ? 2 : TP == 4 ? 4 : 8;
@@ -573,10 +579,10 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
     route.nU = sh;
   }
   if (sh && wv == 0) shared_entry(a, route);
+  if (early_union) __syncthreads();   // the words above set before any routing wave counts itself done
 
   // ---- A. routing from given logits (waves 0..M-1, one token each), or the
   //      router rows ---------------------------------------------------------
-  const bool one_token = a.routed && a.M == 1;       // block-uniform
   if (router) {
     const int k = kWaves - 1 - wv;
     if (k < nrw)
@@ -586,6 +592,14 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
       if (a.E <= 256) route_token<4, false>(a, route, wv);
       else route_token<16, false>(a, route, wv);
       if (one_token) single_token_union(a, route, sh);
+      else if (lane == 0) __hip_atomic_fetch_add(s_rdone, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if (early_union && wv == kWaves - 1) {
+      const uint32_t nm = (uint32_t)a.M;
+      lds_wait(s_rdone, [nm](uint32_t v) { return v >= nm; }, hdr);
+      // (after a timeout the routes stay the shared entry's alone)
+      if ((uint32_t)ufl((int)__hip_atomic_load(s_rdone, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) >= nm)
+        build_union(a, route, hdr, s_tmask, sh);
     }
   } else if (wv == 0 && lane < P) {
     int id = a.topk_ids[lane];
@@ -641,7 +655,7 @@ __device__ __forceinline__ void layer_prologue(const MoeArgs& a, Route& route, u
         }
       }
     }
-  } else if (!one_token) {
+  } else if (!one_token && !early_union) {
     if (wv == 0) build_union(a, route, hdr, s_tmask, sh);
     __syncthreads();
   }

@@ -429,7 +429,8 @@ def run_dense(args):
         pass_bytes = 0
         for i, (K, N, e, q, sc) in enumerate(layers):
             n_out = N // 2 if e else N
-            y = ys.setdefault((n_out,), torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda"))
+            y = torch.empty((M, n_out), dtype=torch.bfloat16, device="cuda")   # its own output: independent linears
+            ys[i] = y
             b = q.numel() + sc.numel() * 2 + 2 * M * K + 2 * M * n_out
             pass_bytes += b
             arr[i] = pq._lib.Q4Linear(xs[K].data_ptr(), q.data_ptr(), sc.data_ptr(), y.data_ptr(), K, N, e)

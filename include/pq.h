@@ -26,7 +26,10 @@
  *   - The caller owns all buffers (inputs, outputs, workspace).  Outside of
  *     pq_workspace_init the library allocates nothing and keeps no per-call
  *     state; distinct workspaces may be used from different threads.  One
- *     workspace must not be used by two calls that can overlap in time.
+ *     workspace must not be used by two calls that can overlap in time.  The
+ *     one exception: the first pq_gemv_q4_group call on a device that makes
+ *     two launches or more creates one stream and two events for it, kept
+ *     until the process ends.
  *   - Arguments are validated on the host before anything is launched.  On a
  *     validation failure the call returns a negative pq_status, launches
  *     nothing and leaves every output untouched.  A failing HIP launch returns
@@ -222,7 +225,14 @@ typedef struct {
  *   launches: nullable host int; receives the number of kernel launches made
  * Constraints per linear as pq_gemv_q4 (PQ_ERR_SHAPE etc.; nothing is
  * launched if any linear is invalid); n = 0 is a no-op.  No workspace.
- * The outputs must not overlap any input of the same call. */
+ * The outputs must not overlap any input of the same call.  When the call
+ * makes two launches or more and no two outputs overlap, the launches
+ * alternate between `stream` and a second stream of the device, forked from
+ * `stream` at the call and joined back into it at the end, so that a launch
+ * starts on the CUs the previous one frees while its last blocks still run;
+ * work queued on `stream` after the call waits for all of it.  With
+ * overlapping outputs, or PQ_Q4_STREAMS=1, every launch goes to `stream` in
+ * order (the later linear's values win). */
 int pq_gemv_q4_group(const pq_q4_linear* linears, int n, int M, int* launches, void* stream);
 
 /* ------------------------------------------------------------------------- */

@@ -29,6 +29,7 @@
 #include <type_traits>
 #include <string.h>
 
+
 #include "pq_common.h"
 
 namespace {
@@ -823,8 +824,61 @@ hipError_t launch_group_p(const Q4Group& a, int M, size_t lds, int grid, hipStre
 // agrees (the scale-load form).  The grid (PQ_BLOCKS_PER_CU blocks per CU)
 // depends on the device only, so each linear's output bits do not depend on
 // how the list is packed, nor on M.
-int run_vector_group(const pq_q4_linear* lin, int n, int M, int num_cus, hipStream_t stream, int* launches) {
-  const int grid = num_cus * blocks_per_cu();
+// Consecutive launches of one grouped call alternate between the caller's
+// stream and a second stream of the device (forked from the caller's stream
+// and joined back to it by events), so that a launch's blocks start on the
+// CUs that the previous launch's blocks free while its last blocks still run;
+// the linears are independent and no block waits for another.  Created on
+// the first grouped call on a device; the mutex keeps one call's fork,
+// launches and join together when host threads call at once.  Not used when
+// two outputs of the call overlap (the later linear's values then win, as
+// with one stream) or when PQ_Q4_STREAMS=1.
+struct PackStreams {
+  std::once_flag once;
+  hipError_t status = hipSuccess;
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+PackStreams g_pack[pqhost::kMaxDevices];
+
+PackStreams* pack_streams(int dev) {
+  if (dev < 0 || dev >= pqhost::kMaxDevices) return nullptr;
+  PackStreams& p = g_pack[dev];
+  std::call_once(p.once, [&] {
+    p.status = hipStreamCreateWithFlags(&p.aux, hipStreamNonBlocking);
+    if (p.status == hipSuccess) p.status = hipEventCreateWithFlags(&p.fork, hipEventDisableTiming);
+    if (p.status == hipSuccess) p.status = hipEventCreateWithFlags(&p.join, hipEventDisableTiming);
+  });
+  return p.status == hipSuccess ? &p : nullptr;
+}
+
+// Whether two outputs of the call overlap (taken as true beyond 1024 linears,
+// where the pairwise check would cost more than the second stream saves).
+bool outputs_overlap(const pq_q4_linear* lin, int n, int M) {
+  if (n > 1024) return true;
+  auto range = [&](int i, uintptr_t& b, uintptr_t& e) {
+    const size_t n_out = lin[i].epi == PQ_EPI_SILU_MUL ? (size_t)lin[i].N / 2 : (size_t)lin[i].N;
+    b = reinterpret_cast<uintptr_t>(lin[i].y);
+    e = b + (size_t)M * n_out * 2;
+  };
+  for (int i = 0; i < n; ++i) {
+    uintptr_t bi, ei;
+    range(i, bi, ei);
+    for (int j = i + 1; j < n; ++j) {
+      uintptr_t bj, ej;
+      range(j, bj, ej);
+      if (bi < ej && bj < ei) return true;
+    }
+  }
+  return false;
+}
+
+// Packs the linears, in order, into launches whose LDS fits one CU and calls
+// launch(group, lds bytes, pair, index) for each; returns the number of packs
+// or the first error.
+template <class Launch>
+int for_each_pack(const pq_q4_linear* lin, int n, int M, int grid, Launch launch) {
   int made = 0;
   for (int i0 = 0; i0 < n;) {
     Q4Group g;
@@ -875,17 +929,51 @@ int run_vector_group(const pq_q4_linear* lin, int n, int M, int num_cus, hipStre
     }
     const size_t lds = floats * 4;
     if (lds > kGroupMaxDyn) return PQ_ERR_SHAPE;
-    // ring depth: 2 steps of two 1 KB row chunks in flight per wave (64 KB
-    // per CU; 3 steps spill at 1024 threads)
-    hipError_t e = pair ? launch_group_p<2, true>(g, M, lds, grid, stream)
-                        : launch_group_p<2, false>(g, M, lds, grid, stream);
-    if (e != hipSuccess) {
-      pqhost::set_last_hip_error((int)e);
-      return PQ_ERR_HIP;
-    }
+    const int st = launch(g, lds, pair, made);
+    if (st != PQ_OK) return st;
     ++made;
     i0 = i1;
   }
+  return made;
+}
+
+// The number of launches the packing makes (the same loop, nothing launched).
+int count_packs(const pq_q4_linear* lin, int n, int M, int grid) {
+  return for_each_pack(lin, n, M, grid, [](const Q4Group&, size_t, bool, int) { return (int)PQ_OK; });
+}
+
+int run_vector_group(const pq_q4_linear* lin, int n, int M, int num_cus, int device, hipStream_t stream,
+                     int* launches) {
+  const int grid = num_cus * blocks_per_cu();
+  const int npacks = count_packs(lin, n, M, grid);
+  if (npacks < 0) return npacks;                   // a linear that does not fit: nothing launched
+  const char* ns = getenv("PQ_Q4_STREAMS");
+  PackStreams* ps = nullptr;
+  if (npacks >= 2 && !(ns && strcmp(ns, "1") == 0) && !outputs_overlap(lin, n, M)) ps = pack_streams(device);
+  std::unique_lock<std::mutex> lock;
+  if (ps) {
+    lock = std::unique_lock<std::mutex>(ps->mu);
+    PQ_HIP_CHECK(hipEventRecord(ps->fork, stream));
+    PQ_HIP_CHECK(hipStreamWaitEvent(ps->aux, ps->fork, 0));
+  }
+  hipError_t err = hipSuccess;
+  const int made = for_each_pack(lin, n, M, grid, [&](const Q4Group& g, size_t lds, bool pair, int k) {
+    const hipStream_t s = ps && (k & 1) ? ps->aux : stream;
+    // ring depth: 2 steps of two 1 KB row chunks in flight per wave (64 KB
+    // per CU; 3 steps spill at 1024 threads)
+    err = pair ? launch_group_p<2, true>(g, M, lds, grid, s) : launch_group_p<2, false>(g, M, lds, grid, s);
+    return err == hipSuccess ? (int)PQ_OK : (int)PQ_ERR_HIP;
+  });
+  if (ps) {   // join even after a failed launch, so the caller's stream stays ordered after the aux work
+    const hipError_t e1 = hipEventRecord(ps->join, ps->aux);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(stream, ps->join, 0) : e1;
+    if (err == hipSuccess) err = e2;
+  }
+  if (err != hipSuccess) {
+    pqhost::set_last_hip_error((int)err);
+    return PQ_ERR_HIP;
+  }
+  if (made < 0) return made;
   if (launches) *launches = made;
   return PQ_OK;
 }
@@ -998,7 +1086,7 @@ int pq_gemv_q4(const uint16_t* x, int M, int K, const uint8_t* w, const uint16_t
     pq_q4_linear one;
     one.x = x; one.w = w; one.w_scale = w_scale; one.y = y;
     one.K = K; one.N = N; one.epi = epi;
-    return run_vector_group(&one, 1, M, dev.num_cus, (hipStream_t)stream, nullptr);
+    return run_vector_group(&one, 1, M, dev.num_cus, dev.device, (hipStream_t)stream, nullptr);
   }
   if (e != hipSuccess) {
     pqhost::set_last_hip_error((int)e);
@@ -1024,7 +1112,7 @@ int pq_gemv_q4_group(const pq_q4_linear* linears, int n, int M, int* launches, v
   pqhost::DeviceInfo dev;
   const int st = pqhost::current_device_info(&dev);
   if (st != PQ_OK) return st;
-  return run_vector_group(linears, n, M, dev.num_cus, (hipStream_t)stream, launches);
+  return run_vector_group(linears, n, M, dev.num_cus, dev.device, (hipStream_t)stream, launches);
 }
 
 }  // extern "C"

@@ -351,6 +351,37 @@ def test_gemv_q4_group_dense_stack_blocks(pq, M):
             assert_gemv_close(yy[:, rows], yo, So, f"stack {K}->{N} M={M}")
 
 
+def test_gemv_q4_group_two_streams_join_and_overlap_fallback(pq, monkeypatch):
+    """A grouped call of several launches alternates them between the
+    caller's stream and a second one, joined back at the end: copies queued
+    on the caller's stream right after the call see every output final, and
+    the bits equal one-stream issue (PQ_Q4_STREAMS=1).  Two linears writing
+    the same output from different launches (the two scale forms never share
+    one) fall back to one stream in order, so the later linear's values win."""
+    import torch
+    M = 4
+    specs = [(5120, 640, 0), (5120, 2 * 512, 1), (8704, 320, 0), (5120, 640, 0), (2048, 2 * 256, 1)]
+    items, _ = _group_case(pq, M, specs, seed=710)
+    ys, launches = pq.gemv_q4_group(items)
+    copies = [y.clone() for y in ys]                    # queued on the caller's stream, no sync in between
+    assert launches >= 2
+    monkeypatch.setenv("PQ_Q4_STREAMS", "1")
+    ys1, launches1 = pq.gemv_q4_group(items)
+    monkeypatch.delenv("PQ_Q4_STREAMS")
+    assert launches1 == launches
+    for i, (c, y, y1) in enumerate(zip(copies, ys, ys1)):
+        assert torch.equal(c.view(torch.int16), y1.view(torch.int16)), f"linear {i}: copy after the call"
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"linear {i}"
+    # overlapping outputs: K/32 even and odd, so two launches, one shared y
+    (xa, pa, sa, ea), (xb, pb, sb, eb) = _group_case(pq, M, [(1024, 96, 0), (1056, 96, 0)], seed=711)[0]
+    shared = torch.empty((M, 96), dtype=torch.bfloat16, device="cuda")
+    _, n2 = pq.gemv_q4_group([(xa, pa, sa, ea, shared), (xb, pb, sb, eb, shared)])
+    assert n2 == 2
+    with env("PQ_Q4_PATH", "valu"):
+        want = pq.gemv_q4(xb, pb, sb, epi=eb)
+    assert torch.equal(shared.view(torch.int16), want.view(torch.int16))
+
+
 def test_gemv_q4_group_rejects_bad_linears(pq):
     import torch
     x = torch.zeros((2, 64), dtype=torch.bfloat16, device="cuda")

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/pq.h"
 
@@ -237,18 +238,126 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 63));
 }
 
-// The sum over aligned segments of `lanes` lanes (8, 16 or 32), left in each
-// segment's last lane: the first stages of wave_sum, so a segment's sum is
-// the same additions in the same order as wave_sum's for values held by
-// those lanes alone (other lanes zero), up to the sign of a zero sum.
-__device__ __forceinline__ float segment_sum(float v, int lanes) {
-  float t = v + dpp_f32<kRowShr1>(v);
-  t += dpp_f32<kRowShr2>(v);
-  t += dpp_f32<kRowShr3>(v);
-  t += dpp_f32<kRowShr4, 0xf, 0xe>(t);               // lanes 7 and 15 of a row: 8-lane sums
-  if (lanes >= 16) t += dpp_f32<kRowShr8, 0xf, 0xc>(t);   // lane 15: the row's sum
-  if (lanes >= 32) t += dpp_f32<kRowBcast15, 0xa>(t);     // lanes 31, 63: two rows' sums
-  return t;
+// The value of lane l ^ d (d = 1 ... 32).  Quad permutes for 1 and 2; then
+// either (LDS = true) the LDS crossbar (swizzle in bit mode within 32 lanes,
+// a permute across the halves), or, without it: for 4, the row rotation by 4
+// (lane l reads l - 4 within its 16-lane row) where bit 2 of l is set, by 12
+// (l + 4) where it is clear; for 8, the row rotation by 8; for 16 and 32, the
+// permlane swaps of the value with itself, which give every lane the other
+// row of its row pair (other half of the wave) in one of their two results.
+// Both read the same lane, so sums built on either have the same bits; the
+// crossbar takes fewer vector instructions, the other form less latency.
+template <int D, bool LDS = false>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int iv = __builtin_bit_cast(int, v);
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  if constexpr (D == 1) return dpp_f32<0xB1>(v);                 // quad_perm [1,0,3,2]
+  else if constexpr (D == 2) return dpp_f32<0x4E>(v);            // quad_perm [2,3,0,1]
+  else if constexpr (LDS && D < 32) return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, (D << 10) | 0x1F));
+  else if constexpr (LDS) return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, iv));
+  else if constexpr (D == 4) {
+    const float down = dpp_f32<0x124>(v), up = dpp_f32<0x12C>(v);   // row_ror:4, row_ror:12
+    return (lane & 4) ? down : up;
+  } else if constexpr (D == 8) return dpp_f32<0x128>(v);         // row_ror:8
+  else if constexpr (D == 16) {
+    const auto s = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);   // rows (0,0,2,2), (1,1,3,3)
+    return __builtin_bit_cast(float, (lane & 16) ? (int)s[0] : (int)s[1]);
+  } else {
+    static_assert(D == 32, "d = 1, 2, 4, 8, 16 or 32");
+    const auto s = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);   // halves (lo, lo), (hi, hi)
+    return __builtin_bit_cast(float, (lane & 32) ? (int)s[0] : (int)s[1]);
+  }
+}
+
+// Wave sums of N values per lane (N a power of two, at most 64), all in one
+// butterfly: at the stage of distance d = 2^s a lane keeps the half of its
+// values whose index bit s equals its lane bit s and adds its partner's
+// (lane l ^ d) copy of them, so each stage halves the values a lane holds;
+// once one is left, the remaining distances add it as a plain butterfly.
+// Lane l ends with the sum of value l mod N.  Every value is summed over the
+// same tree of lane pairs (distances 1, 2, 4, ..., 32 in that order), whatever
+// its index and N (each pair's sum is the same in either lane: addition
+// commutes), so a row's sum does not depend on how many values share the
+// reduction.
+template <int N, bool LDS = false>
+__device__ __forceinline__ float wave_sum_many(const float (&v)[N]) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N: a power of two up to 64");
+  const int lane = (int)(threadIdx.x & (kWave - 1));
+  float c[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) c[i] = v[i];
+  auto stage = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int S = __builtin_ctz(D);
+    if constexpr ((N >> S) > 1) {                 // c[k]: value (lane bits below S) | k << S
+      const bool hi = (lane >> S) & 1;
+#pragma unroll
+      for (int i = 0; i < (N >> S) / 2; ++i) {
+        const float keep = hi ? c[2 * i + 1] : c[2 * i];
+        const float send = hi ? c[2 * i] : c[2 * i + 1];
+        c[i] = keep + xor_lane<D, LDS>(send);
+      }
+    } else {
+      c[0] = c[0] + xor_lane<D, LDS>(c[0]);
+    }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
+  stage(std::integral_constant<int, 32>{});
+  return c[0];
+}
+
+// Butterfly sum of each aligned segment of `lanes` lanes (2 ... 64): the first
+// stages of wave_sum_many's tree, so every lane of a segment ends with the sum
+// its row would have alone in the wave (the later stages only add zeros).
+// After the quad stages every lane of a quad holds the same bits (each pair's
+// sum is the same in both lanes), so the 8- and 16-lane stages may take their
+// partner from the row's mirror images instead of lane l ^ 4 and l ^ 8: the
+// same two group sums are added, without the LDS crossbar.
+__device__ __forceinline__ float segment_sum_xor(float v, int lanes) {
+  constexpr int kRowMirror = 0x140, kRowHalfMirror = 0x141;
+  v += xor_lane<1>(v);
+  if (lanes >= 4) v += xor_lane<2>(v);
+  if (lanes >= 8) v += dpp_f32<kRowHalfMirror>(v);
+  if (lanes >= 16) v += dpp_f32<kRowMirror>(v);
+  if (lanes >= 32) v += xor_lane<16>(v);
+  if (lanes >= 64) v += xor_lane<32>(v);
+  return v;
+}
+
+// Wave sums of the value pairs (a[t], b[t]), t < n (n <= TP, wave-uniform):
+// one wave_sum_many over the smallest power of two of values that holds the
+// 2n (the tree, and so every sum, is the same for any width), read back into
+// every lane.
+template <int TP>
+__device__ __forceinline__ void wave_sum_pairs(const float (&a)[TP], const float (&b)[TP], int n, float (&ra)[TP],
+                                               float (&rb)[TP]) {
+  auto run = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;        // pairs in the reduction
+    static_assert(W <= TP, "at most TP pairs");
+    float v[2 * W];
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+      v[2 * t] = a[t];
+      v[2 * t + 1] = b[t];
+    }
+    const float s = wave_sum_many<2 * W>(v);    // lane 2t: a's sum, lane 2t + 1: b's
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      ra[t] = rb[t] = 0.0f;
+      if (t < W) {
+        ra[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 2 * t));
+        rb[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 2 * t + 1));
+      }
+    }
+  };
+  if (n <= 1 || TP == 1) run(std::integral_constant<int, 1>{});
+  else if (n <= 2 || TP == 2) run(std::integral_constant<int, (TP < 2 ? TP : 2)>{});
+  else if (n <= 4 || TP <= 4) run(std::integral_constant<int, (TP < 4 ? TP : 4)>{});
+  else run(std::integral_constant<int, (TP < 8 ? TP : 8)>{});
 }
 
 template <bool B>

@@ -89,57 +89,6 @@ __device__ __forceinline__ float dot32(const Pairs16& w, const uint4 (&x)[4]) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// The value of lane l ^ d (d = 1 ... 32).
-template <int D>
-__device__ __forceinline__ float xor_lane(float v) {
-  if constexpr (D == 1) return pq::dpp_f32<0xB1>(v);              // quad_perm [1,0,3,2]
-  else if constexpr (D == 2) return pq::dpp_f32<0x4E>(v);         // quad_perm [2,3,0,1]
-  else if constexpr (D < 32)                                      // swizzle, bit mode: xor within 32 lanes
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (D << 10) | 0x1F));
-  else
-    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((pq::lane_id() ^ 32) << 2, __builtin_bit_cast(int, v)));
-}
-
-// Wave sums of N values per lane (N a power of two, at most 64), all in one
-// butterfly: at the stage of distance d = 2^s a lane keeps the half of its
-// values whose index bit s equals its lane bit s and adds its partner's
-// (lane l ^ d) copy of them, so each stage halves the values a lane holds;
-// once one is left, the remaining distances add it as a plain butterfly.
-// Lane l ends with the sum of value l mod N.  Every value is summed over the
-// same tree of lane pairs (distances 1, 2, 4, ..., 32 in that order), whatever
-// its index and N (each pair's sum is the same in either lane: addition
-// commutes), so a row's sum does not depend on how many values share the
-// reduction.
-template <int N>
-__device__ __forceinline__ float wave_sum_many(const float (&v)[N]) {
-  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N: a power of two up to 64");
-  const int lane = pq::lane_id();
-  float c[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) c[i] = v[i];
-  auto stage = [&](auto dc) {
-    constexpr int D = decltype(dc)::value;
-    constexpr int S = __builtin_ctz(D);
-    if constexpr ((N >> S) > 1) {                 // c[k]: value (lane bits below S) | k << S
-      const bool hi = (lane >> S) & 1;
-#pragma unroll
-      for (int i = 0; i < (N >> S) / 2; ++i) {
-        const float keep = hi ? c[2 * i + 1] : c[2 * i];
-        const float send = hi ? c[2 * i] : c[2 * i + 1];
-        c[i] = keep + xor_lane<D>(send);
-      }
-    } else {
-      c[0] = c[0] + xor_lane<D>(c[0]);
-    }
-  };
-  stage(std::integral_constant<int, 1>{});
-  stage(std::integral_constant<int, 2>{});
-  stage(std::integral_constant<int, 4>{});
-  stage(std::integral_constant<int, 8>{});
-  stage(std::integral_constant<int, 16>{});
-  stage(std::integral_constant<int, 32>{});
-  return c[0];
-}
 
 // 8 bf16 values x0..x7 -> the pairs (x0,x4)(x1,x5)(x2,x6)(x3,x7)
 __device__ __forceinline__ uint4 pair_order(uint4 r) {
@@ -489,7 +438,7 @@ __global__ __launch_bounds__(kVThreads) void gemv_q4_kernel(const Q4Group a) {
       float vals[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) vals[i] = i < 2 * MT ? acc[i & 1][i >> 1] : 0.0f;   // value 2m + j
-      const float v = wave_sum_many<NV>(vals);   // lane 2m + j: the sum of acc[j][m]
+      const float v = pq::wave_sum_many<NV, true>(vals);   // lane 2m + j: the sum of acc[j][m] (crossbar exchanges: fewer vector instructions)
 #pragma unroll
       for (int m = 0; m < MT; ++m)
 #pragma unroll

@@ -848,17 +848,15 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
             }
           }
           if (cc == nchH - 1) {            // unit done: h for every routed token
+            float gs[TP], us[TP];
+            pq::wave_sum_pairs<TP>(accg, accu, cnp, gs, us);
 #pragma unroll
             for (int t = 0; t < TP; ++t) {
-              if (t < cnp) {
-                const float g = pq::wave_sum(accg[t]);
-                const float u = pq::wave_sum(accu[t]);
-                if (lane == 0) {
-                  uint16_t hb = pq::bf16_rne(silu_mul(g, u));
-                  if (hb == 0xFFFFu) hb = 0xFFC0u;         // keep the inverted word non-zero
-                  pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + ci, (uint16_t)~hb);
-                  if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + ci] = hb;
-                }
+              if (t < cnp && lane == 0) {
+                uint16_t hb = pq::bf16_rne(silu_mul(gs[t], us[t]));
+                if (hb == 0xFFFFu) hb = 0xFFC0u;           // keep the inverted word non-zero
+                pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + ci, (uint16_t)~hb);
+                if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + ci] = hb;
               }
               accg[t] = accu[t] = 0.0f;
             }
@@ -1059,24 +1057,27 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
           }
         }
         if (kP || cc == nchI - 1) {         // unit(s) (union entry cu, rows cr ..) done
+          if constexpr (kP) {
 #pragma unroll
-          for (int t = 0; t < TP; ++t) {
-            if (t < cnp) {
-              if constexpr (kP) {                     // each segment's last lane holds its row's sum
-                const float y = pq::segment_sum(acc[0][t], lpr);
+            for (int t = 0; t < TP; ++t) {
+              if (t < cnp) {                          // every lane of a segment holds its row's sum
+                const float y = pq::segment_sum_xor(acc[0][t], lpr);
                 if (lane % lpr == lpr - 1 && prr < nr) ybuf[(cr + prr) * P2 + pr[t]] = y;
-              } else {
-#pragma unroll
-                for (int j = 0; j < kR; ++j) {
-                  if (j < nr) {
-                    const float y = pq::wave_sum(acc[j][t]);
-                    if (lane == 0) ybuf[(cr + j) * P2 + pr[t]] = y;
-                  }
-                }
               }
+              acc[0][t] = 0.0f;
             }
+          } else {                                    // rows cr and cr + 1 of every pair in one butterfly
+            float y0[TP], y1[TP];
+            pq::wave_sum_pairs<TP>(acc[0], acc[kR - 1], cnp, y0, y1);
 #pragma unroll
-            for (int j = 0; j < kR; ++j) acc[j][t] = 0.0f;
+            for (int t = 0; t < TP; ++t) {
+              if (t < cnp && lane == 0) {
+                ybuf[cr * P2 + pr[t]] = y0[t];
+                if (nr > 1) ybuf[(cr + 1) * P2 + pr[t]] = y1[t];
+              }
+#pragma unroll
+              for (int j = 0; j < kR; ++j) acc[j][t] = 0.0f;
+            }
           }
         }
         if (kP || ++cc == nchI) {
@@ -1289,17 +1290,15 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
         }
       }
       if (step == nchH - 1) {            // unit done: h for every token routed to u
+        float gs[TP], us[TP];
+        pq::wave_sum_pairs<TP>(accg, accu, cnp, gs, us);
 #pragma unroll
         for (int t = 0; t < TP; ++t) {
-          if (t < cnp) {
-            const float g = pq::wave_sum(accg[t]);
-            const float u = pq::wave_sum(accu[t]);
-            if (lane == 0) {
-              uint16_t hb = pq::bf16_rne(silu_mul(g, u));
-              if (hb == 0xFFFFu) hb = 0xFFC0u;         // keep the inverted word non-zero
-              pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + row, (uint16_t)~hb);
-              if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + row] = hb;
-            }
+          if (t < cnp && lane == 0) {
+            uint16_t hb = pq::bf16_rne(silu_mul(gs[t], us[t]));
+            if (hb == 0xFFFFu) hb = 0xFFC0u;           // keep the inverted word non-zero
+            pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + row, (uint16_t)~hb);
+            if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + row] = hb;
           }
           accg[t] = accu[t] = 0.0f;
         }
@@ -1429,17 +1428,18 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
           }
         }
       }
-      if (step == nchI - 1) {             // unit (u, rows row .. row + kDnRows - 1) done
+      if (step == nchI - 1) {             // unit (u, rows row, row + 1) done: all its sums in one butterfly
+        static_assert(kDnRows == 2, "two rows per down step");
+        float y0[TP], y1[TP];
+        pq::wave_sum_pairs<TP>(acc[0], acc[1], cnp, y0, y1);
 #pragma unroll
-        for (int j = 0; j < kDnRows; ++j) {
-#pragma unroll
-          for (int t = 0; t < TP; ++t) {
-            if (t < cnp && row + j < nrows) {
-              const float y = pq::wave_sum(acc[j][t]);
-              if (lane == 0) ybuf[(row + j) * P2 + pr[t]] = y;
-            }
-            acc[j][t] = 0.0f;
+        for (int t = 0; t < TP; ++t) {
+          if (t < cnp && lane == 0) {
+            ybuf[row * P2 + pr[t]] = y0[t];
+            if (row + 1 < nrows) ybuf[(row + 1) * P2 + pr[t]] = y1[t];
           }
+#pragma unroll
+          for (int j = 0; j < kDnRows; ++j) acc[j][t] = 0.0f;
         }
       }
     };

@@ -330,12 +330,43 @@ __device__ __forceinline__ float segment_sum_xor(float v, int lanes) {
 
 // Wave sums of the value pairs (a[t], b[t]), t < n (n <= TP, wave-uniform):
 // one wave_sum_many over the smallest power of two of values that holds the
-// 2n (the tree, and so every sum, is the same for any width).  Lane 2t ends
-// with a[t]'s sum and lane 2t + 1 with b[t]'s, for t < n.
+// 2n (the tree, and so every sum, is the same for any width), read back into
+// every lane.
 template <int TP>
-__device__ __forceinline__ float wave_sum_pairs(const float (&a)[TP], const float (&b)[TP], int n) {
+__device__ __forceinline__ void wave_sum_pairs(const float (&a)[TP], const float (&b)[TP], int n, float (&ra)[TP],
+                                               float (&rb)[TP]) {
   auto run = [&](auto wc) {
     constexpr int W = decltype(wc)::value;        // pairs in the reduction
+    static_assert(W <= TP, "at most TP pairs");
+    float v[2 * W];
+#pragma unroll
+    for (int t = 0; t < W; ++t) {
+      v[2 * t] = a[t];
+      v[2 * t + 1] = b[t];
+    }
+    const float s = wave_sum_many<2 * W>(v);    // lane 2t: a's sum, lane 2t + 1: b's
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      ra[t] = rb[t] = 0.0f;
+      if (t < W) {
+        ra[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 2 * t));
+        rb[t] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 2 * t + 1));
+      }
+    }
+  };
+  if (n <= 1 || TP == 1) run(std::integral_constant<int, 1>{});
+  else if (n <= 2 || TP == 2) run(std::integral_constant<int, (TP < 2 ? TP : 2)>{});
+  else if (n <= 4 || TP <= 4) run(std::integral_constant<int, (TP < 4 ? TP : 4)>{});
+  else run(std::integral_constant<int, (TP < 8 ? TP : 8)>{});
+}
+
+// The same sums left where the butterfly puts them: lane 2t ends with a[t]'s
+// sum and lane 2t + 1 with b[t]'s, for t < n (for callers whose lanes store
+// their own results instead of reading them all back into scalar registers).
+template <int TP>
+__device__ __forceinline__ float wave_sum_pairs_lanes(const float (&a)[TP], const float (&b)[TP], int n) {
+  auto run = [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
     static_assert(W <= TP, "at most TP pairs");
     float v[2 * W];
 #pragma unroll

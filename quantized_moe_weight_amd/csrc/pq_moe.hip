@@ -520,54 +520,6 @@ __device__ void router_rows(const MoeArgs& a, int e) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-// h of a finished gate_up unit (h-row `row`) for its n routed pairs, from the
-// pair sums of wave_sum_pairs (lane 2t: pair t's gate sum, lane 2t + 1: its
-// up sum).  With one pair per unit lane 0 reads both back and stores; with
-// more, lane 2t stores pair t's h itself (its pair index read from the union
-// table), which keeps the sums out of scalar registers.  The same values
-// either way.
-template <int TP>
-__device__ __forceinline__ void store_h(const MoeArgs& a, float s, int n, const int (&pr)[TP], const int* upairs,
-                                        int row) {
-  const int lane = pq::lane_id();
-  auto put = [&](int p, float g, float u) {
-    uint16_t hb = pq::bf16_rne(silu_mul(g, u));
-    if (hb == 0xFFFFu) hb = 0xFFC0u;             // keep the inverted word non-zero
-    pq::st_agent_u16(a.hbuf + (size_t)p * a.I + row, (uint16_t)~hb);
-    if (a.h_dbg) a.h_dbg[(size_t)p * a.I + row] = hb;
-  };
-  if constexpr (TP == 1) {
-    const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 0));
-    const float u = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 1));
-    if (lane == 0 && n > 0) put(pr[0], g, u);
-  } else {
-    const float u = pq::xor_lane<1>(s);
-    const int t = lane >> 1;
-    if ((lane & 1) == 0 && t < n) put(upairs[t], s, u);
-  }
-}
-
-// y of two down rows (row0, row0 + 1; nr of them valid) for the unit's n
-// pairs, from wave_sum_pairs (lane 2t + j: row0 + j of pair t), into the
-// block's partials [row][P2]; lane 0 writes with one pair, lane 2t + j with
-// more (as store_h).
-template <int TP>
-__device__ __forceinline__ void store_y(float* ybuf, float s, int n, int nr, int row0, int P2, const int (&pr)[TP],
-                                        const int* upairs) {
-  const int lane = pq::lane_id();
-  if constexpr (TP == 1) {
-    const float y0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 0));
-    const float y1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 1));
-    if (lane == 0 && n > 0) {
-      ybuf[row0 * P2 + pr[0]] = y0;
-      if (nr > 1) ybuf[(row0 + 1) * P2 + pr[0]] = y1;
-    }
-  } else {
-    const int t = lane >> 1, j = lane & 1;
-    if (t < n && j < nr) ybuf[(row0 + j) * P2 + upairs[t]] = s;
-  }
-}
-
 // Phases A and B of both kernels: the router rows of this block (when the
 // logits are computed in the launch), the routing, the live quantisation of
 // x into LDS and the union of the routed experts (after the shared entry).
@@ -896,9 +848,18 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
             }
           }
           if (cc == nchH - 1) {            // unit done: h for every routed token
-            store_h<TP>(a, pq::wave_sum_pairs<TP>(accg, accu, cnp), cnp, pr, route.upairs[uu], ci);
+            float gs[TP], us[TP];
+            pq::wave_sum_pairs<TP>(accg, accu, cnp, gs, us);
 #pragma unroll
-            for (int t = 0; t < TP; ++t) accg[t] = accu[t] = 0.0f;
+            for (int t = 0; t < TP; ++t) {
+              if (t < cnp && lane == 0) {
+                uint16_t hb = pq::bf16_rne(silu_mul(gs[t], us[t]));
+                if (hb == 0xFFFFu) hb = 0xFFC0u;           // keep the inverted word non-zero
+                pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + ci, (uint16_t)~hb);
+                if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + ci] = hb;
+              }
+              accg[t] = accu[t] = 0.0f;
+            }
           }
         }
         issue_gu(wb[q], sb[q], sa[q], su[q], sch[q]);
@@ -1106,12 +1067,17 @@ __global__ __launch_bounds__(kThreads) void moe_barrier_kernel(MoeArgs a) {
               acc[0][t] = 0.0f;
             }
           } else {                                    // rows cr and cr + 1 of every pair in one butterfly
-            store_y<TP>(ybuf, pq::wave_sum_pairs<TP>(acc[0], acc[kR - 1], cnp), cnp, nr, cr, P2, pr,
-                        route.upairs[cu < nU ? cu : 0]);
+            float y0[TP], y1[TP];
+            pq::wave_sum_pairs<TP>(acc[0], acc[kR - 1], cnp, y0, y1);
 #pragma unroll
-            for (int t = 0; t < TP; ++t)
+            for (int t = 0; t < TP; ++t) {
+              if (t < cnp && lane == 0) {
+                ybuf[cr * P2 + pr[t]] = y0[t];
+                if (nr > 1) ybuf[(cr + 1) * P2 + pr[t]] = y1[t];
+              }
 #pragma unroll
               for (int j = 0; j < kR; ++j) acc[j][t] = 0.0f;
+            }
           }
         }
         if (kP || ++cc == nchI) {
@@ -1207,6 +1173,11 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
   const uint32_t lane16 = 16u * (uint32_t)lane;
   const uint32_t lane_blk4 = 4u * ((uint32_t)lane >> 3);
 
+  // Unit-end sums: with several pairs per unit the lanes that hold them store
+  // them (the sums stay out of scalar registers; M=8 260.9 against 265.9 µs);
+  // with the router and shared expert in the launch, whose registers are at
+  // their limit, lane 0 reads them back (M=4 212.5 against 222 µs)
+  constexpr bool kLaneStores = TP > 1 && !EXT;
   uint8_t* xa = smem + a.xa_off;                               // x codes   [M][H]
   float* xsc = reinterpret_cast<float*>(smem + a.xs_off);      // x scales  [M][H/128]
   uint8_t* ha = smem + a.ha_off;                               // h codes   [nitems][I] by staging slot
@@ -1324,9 +1295,35 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
         }
       }
       if (step == nchH - 1) {            // unit done: h for every token routed to u
-        store_h<TP>(a, pq::wave_sum_pairs<TP>(accg, accu, cnp), cnp, pr, route.upairs[uu], row);
+        if constexpr (kLaneStores) {
+          // lane 2t: pair t's gate sum; its up sum comes from lane 2t + 1, its
+          // pair index from the union table, and the lane stores its h itself
+          const float gsum = pq::wave_sum_pairs_lanes<TP>(accg, accu, cnp);
+          const float usum = pq::xor_lane<1>(gsum);
+          const int tl = lane >> 1;
+          if ((lane & 1) == 0 && tl < cnp) {
+            const int p = route.upairs[uu][tl];
+            uint16_t hb = pq::bf16_rne(silu_mul(gsum, usum));
+            if (hb == 0xFFFFu) hb = 0xFFC0u;           // keep the inverted word non-zero
+            pq::st_agent_u16(a.hbuf + (size_t)p * I + row, (uint16_t)~hb);
+            if (a.h_dbg) a.h_dbg[(size_t)p * I + row] = hb;
+          }
 #pragma unroll
-        for (int t = 0; t < TP; ++t) accg[t] = accu[t] = 0.0f;
+          for (int t = 0; t < TP; ++t) accg[t] = accu[t] = 0.0f;
+        } else {
+          float gs[TP], us[TP];
+          pq::wave_sum_pairs<TP>(accg, accu, cnp, gs, us);
+#pragma unroll
+          for (int t = 0; t < TP; ++t) {
+            if (t < cnp && lane == 0) {
+              uint16_t hb = pq::bf16_rne(silu_mul(gs[t], us[t]));
+              if (hb == 0xFFFFu) hb = 0xFFC0u;         // keep the inverted word non-zero
+              pq::st_agent_u16(a.hbuf + (size_t)pr[t] * I + row, (uint16_t)~hb);
+              if (a.h_dbg) a.h_dbg[(size_t)pr[t] * I + row] = hb;
+            }
+            accg[t] = accu[t] = 0.0f;
+          }
+        }
       }
     };
 
@@ -1455,12 +1452,27 @@ __global__ __launch_bounds__(kThreads) void moe_stream_kernel(MoeArgs a) {
       }
       if (step == nchI - 1) {             // unit (u, rows row, row + 1) done: all its sums in one butterfly
         static_assert(kDnRows == 2, "two rows per down step");
-        store_y<TP>(ybuf, pq::wave_sum_pairs<TP>(acc[0], acc[1], cnp), cnp, nrows - row < 2 ? nrows - row : 2, row, P2,
-                    pr, route.upairs[uu]);
+        if constexpr (kLaneStores) {    // lane 2t + j stores row + j of pair t
+          const float y = pq::wave_sum_pairs_lanes<TP>(acc[0], acc[1], cnp);
+          const int tl = lane >> 1, jl = lane & 1;
+          if (tl < cnp && row + jl < nrows) ybuf[(row + jl) * P2 + route.upairs[uu][tl]] = y;
 #pragma unroll
-        for (int t = 0; t < TP; ++t)
+          for (int t = 0; t < TP; ++t)
 #pragma unroll
-          for (int j = 0; j < kDnRows; ++j) acc[j][t] = 0.0f;
+            for (int j = 0; j < kDnRows; ++j) acc[j][t] = 0.0f;
+        } else {
+          float y0[TP], y1[TP];
+          pq::wave_sum_pairs<TP>(acc[0], acc[1], cnp, y0, y1);
+#pragma unroll
+          for (int t = 0; t < TP; ++t) {
+            if (t < cnp && lane == 0) {
+              ybuf[row * P2 + pr[t]] = y0[t];
+              if (row + 1 < nrows) ybuf[(row + 1) * P2 + pr[t]] = y1[t];
+            }
+#pragma unroll
+            for (int j = 0; j < kDnRows; ++j) acc[j][t] = 0.0f;
+          }
+        }
       }
     };
     // wait until the h of union entry uu is in LDS (its stagers poll with a

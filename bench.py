@@ -54,12 +54,12 @@ METRIC = "achieved HBM GB/s (% of 8 TB/s) + µs/layer, batch-1 top-8 FP8 MoE GEM
 
 
 def layer_kernel_name(M: int) -> str:
-    """The kernel the library runs for an M-token call (one or two tokens: the
-    barrier kernel; more: the stream kernel; PQ_MOE_PATH overrides)."""
+    """The kernel the library runs for an M-token call (one token: the barrier
+    kernel; more: the stream kernel; PQ_MOE_PATH overrides)."""
     p = os.environ.get("PQ_MOE_PATH", "")
     if p in ("barrier", "stream"):
         return f"moe_{p}_kernel"
-    return "moe_barrier_kernel" if M <= 2 else "moe_stream_kernel"
+    return "moe_barrier_kernel" if M <= 1 else "moe_stream_kernel"
 
 
 def kernel_source_sha() -> str:

@@ -272,9 +272,9 @@ size_t moe_decode_layer_workspace(int M, int H, int I, int E, int top_k);
  * that cannot guarantee an idle device check it, or set
  * PQ_MOE_LAUNCH=cooperative, which makes the runtime guarantee co-residency or
  * refuse the launch with PQ_ERR_HIP).
- * Two kernels implement the call with bitwise equal results: for M <= 2 one
+ * Two kernels implement the call with bitwise equal results: for M = 1 one
  * whose blocks start the down projection once every h row of the call is
- * there (a grid-wide barrier on the h values themselves), for M >= 3 one that
+ * there (a grid-wide barrier on the h values themselves), for M >= 2 one that
  * starts each union entry's down rows once that entry's h is there (the
  * environment variable PQ_MOE_PATH=barrier|stream forces one;
  * PQ_MOE_SCALES=step makes the first load every gate_up step's block scales

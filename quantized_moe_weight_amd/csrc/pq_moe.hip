@@ -679,7 +679,7 @@ __device__ __forceinline__ void wait_routes(const uint32_t* s_ready, pq::WsHeade
 // all of h (waiting for the rows of slower blocks value by value: a barrier on
 // the data itself) and runs its down rows.  Fewer instructions per step than
 // the stream kernel below, which pays off when the call streams few experts
-// (one or two tokens).
+// (one token).
 // TP: compile-time bound on the (token, slot) pairs routed to one expert in a
 // call (the smallest power of two >= M), so the per-pair loops unroll tightly.
 template <int TP, bool EXT>
@@ -1556,15 +1556,16 @@ struct MoePlan {
   size_t off_h, ws_total;
 };
 
-// Which kernel runs a call: the barrier kernel for one or two tokens, the
-// stream kernel from three on (measured crossover at H = 6144, I = 2048,
-// 256 experts, top-8); PQ_MOE_PATH=barrier|stream overrides.
+// Which kernel runs a call: the barrier kernel for one token, the stream
+// kernel from two on (H = 6144, I = 2048, 256 experts, top-8: M=1 56.9 against
+// 60.0 µs, M=2 98.5-98.7 against 99.8-100.1, M=3 133.5 against 138.4);
+// PQ_MOE_PATH=barrier|stream overrides.
 enum { kPathBarrier = 0, kPathStream = 1 };
 int moe_path(int M) {
   const char* e = getenv("PQ_MOE_PATH");
   if (e && strcmp(e, "barrier") == 0) return kPathBarrier;
   if (e && strcmp(e, "stream") == 0) return kPathStream;
-  return M <= 2 ? kPathBarrier : kPathStream;
+  return M <= 1 ? kPathBarrier : kPathStream;
 }
 
 // num_cus bounds the rows a block can own (the grid has one block per CU);

@@ -9,7 +9,7 @@ the kernels (a poll budget after which PQ_ERR_TIMEOUT is recorded and the wave
 goes on), so a run always ends; a protocol that deadlocks shows up as a run
 whose waits time out although every block was resident.
 
-Barrier kernel (one or two tokens):
+Barrier kernel (one token):
   * block b owns the units [split(U, G, b), split(U, G, b+1)); its waves take
     them one at a time from the block's LDS counter and publish each unit's h
     (a non-zero word: h is stored bit-inverted into a region that is zero

@@ -243,7 +243,7 @@ def test_moe_barrier_and_stream_kernels_agree_bitwise(pq, M, I, H):
 
 @pytest.mark.parametrize("M,E,H,I,k,shared", [(1, 16, 1024, 512, 4, False), (2, 16, 640, 384, 4, True),
                                                 (1, 256, 6144, 2048, 8, False)])
-def test_moe_scale_windows_match_step_loads(pq, M, E, H, I, k, shared):
+def test_moe_scale_windows_match_step_loads(pq, monkeypatch, M, E, H, I, k, shared):
     """The barrier kernel's gate_up reads its block scales from per-wave LDS
     windows (filled once per h row by buffer-to-LDS loads); with
     PQ_MOE_SCALES=step it loads them with every step's weights instead.  The
@@ -251,6 +251,7 @@ def test_moe_scale_windows_match_step_loads(pq, M, E, H, I, k, shared):
     one chunk per row (four rows rotating through the windows), a ragged
     chunk with a shared expert, and the full-size layer."""
     import torch
+    monkeypatch.setenv("PQ_MOE_PATH", "barrier")       # the windows belong to the barrier kernel
     cfg = pq.moe_layer_config(M, H, I, E, k, shared=shared)
     assert cfg["kernel"] == "barrier" and cfg["lds_bytes"] >= 16 * 2048, cfg     # the windows are laid out
     wl = workloads.MOE_LAYER
@@ -290,7 +291,7 @@ def test_moe_scale_windows_match_step_loads(pq, M, E, H, I, k, shared):
 def test_moe_deterministic_and_workspace_reuse(pq):
     """Repeated calls are bitwise identical, also interleaved with calls of other
     shapes on the same workspace (counters and the h exchange region must be
-    left at zero; M = 1, 2 run the barrier kernel, M = 5 the stream kernel)."""
+    left at zero; M = 1 runs the barrier kernel, M = 2 and 5 the stream kernel)."""
     import torch
     E, H, I, k = 16, 512, 256, 4
     bank = Bank(pq, E, H, I, seed=5)
@@ -367,13 +368,15 @@ def test_moe_full_size_layer(pq, path, M):
     print(f"full-size M={M} ({path}): union {len(oracle.union_of_experts(ids))} experts, worst |err|/S {worst:.2e}")
 
 
-@pytest.mark.parametrize("M,kernel,alias,layout", [(2, "barrier", True, None), (7, "stream", True, "split"),
-                                                   (8, "stream", True, "split"), (8, "stream", True, "full")])
+@pytest.mark.parametrize("M,kernel,alias,layout", [(2, "stream", False, None), (2, "barrier", True, "barrier"),
+                                                   (7, "stream", True, "split"), (8, "stream", True, "split"),
+                                                   (8, "stream", True, "full")])
 def test_moe_full_size_verify(pq, monkeypatch, M, kernel, alias, layout):
     """Speculative verify at the real shape (256 experts, hidden 6144,
     intermediate 2048, top-8, equicorrelated routing): M = 2 on the library's
-    default kernel for two tokens (which always stages h over x, after its
-    grid-wide release), M = 7 and 8 on the stream kernel, where x, h and the
+    default kernel for two tokens (the stream kernel, x and h side by side)
+    and on the barrier kernel (PQ_MOE_PATH=barrier: it always stages h over x,
+    after its grid-wide release), M = 7 and 8 on the stream kernel, where x, h and the
     output partials do not fit side by side: by default ("split") the
     first h rows in union order sit apart from x and are staged while other
     waves still stream gate_up, and only the rest overwrite the quantised x;
@@ -384,9 +387,11 @@ def test_moe_full_size_verify(pq, monkeypatch, M, kernel, alias, layout):
     shp = workloads.MOE_SHAPE
     if layout == "full":
         monkeypatch.setenv("PQ_MOE_ALIAS", "full")
+    if layout == "barrier":
+        monkeypatch.setenv("PQ_MOE_PATH", "barrier")
     cfg = pq.moe_layer_config(M, shp.H, shp.I, shp.E, shp.top_k)
     assert cfg["kernel"] == kernel and cfg["alias"] == alias, cfg
-    if layout is not None:
+    if layout in ("split", "full"):
         P = M * shp.top_k
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         yb = -(-shp.H // cus) * P * 4

@@ -50,6 +50,7 @@ KERNEL_NAME = "moe_barrier_kernel"   # the layer kernel of the batch-1 workload 
 MOE_SRC = os.path.join(ROOT, "quantized_moe_weight_amd", "csrc", "pq_moe.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "moe_barrier_kernel_e256_h6144_i2048_m1.pmc.txt")
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written per dispatch
+COPY_REPS = 3                 # calibration copies at the end of a profile pass
 METRIC = "achieved HBM GB/s (% of 8 TB/s) + µs/layer, batch-1 top-8 FP8 MoE GEMV"
 
 
@@ -62,9 +63,26 @@ def layer_kernel_name(M: int) -> str:
     return "moe_barrier_kernel" if M <= 1 else "moe_stream_kernel"
 
 
-def kernel_source_sha() -> str:
+# the source files each kernel family is compiled from (its .hip and the
+# device headers it includes), keyed by a substring of the kernel's name
+KERNEL_SOURCES = (
+    ("moe_", ("pq_moe.hip", "pq_common.h", "pq_quant_dev.h")),
+    ("gemv_q4", ("pq_gemv_q4.hip", "pq_common.h")),
+    ("gemv_fp8", ("pq_gemv_fp8.hip", "pq_common.h", "pq_quant_dev.h")),
+    ("gemm_fp8", ("pq_gemm_fp8.hip", "pq_common.h")),
+)
+
+
+def kernel_source_sha(kernel: str = "moe_") -> str:
+    """Hash of the sources of the kernel family whose name contains one of
+    KERNEL_SOURCES' keys (the layer kernels by default), recorded with every
+    counter summary: a summary whose hash differs no longer describes the
+    built kernel."""
+    files = next((fs for key, fs in KERNEL_SOURCES if key in kernel), None)
+    if files is None:
+        raise KeyError(f"no source list for kernel {kernel!r}")
     h = hashlib.sha1()
-    for f in ("pq_moe.hip", "pq_common.h", "pq_quant_dev.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "quantized_moe_weight_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -656,17 +674,18 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES, kernel=KERNEL_NAME, 
     def per_kernel(path, counter):
         rows = list(csv.DictReader(open(path, encoding="utf-8")))
         acc = {}
-        for r in rows:
+        for i, r in enumerate(rows):
             if r.get("Counter_Name") != counter:
                 continue
             name = r.get("Kernel_Name", "")
-            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+            order = int(r.get("Dispatch_Id") or i)
+            acc.setdefault(name, []).append((order, float(r["Counter_Value"])))
         return acc
 
     f = per_kernel(fetch_csv, "FETCH_SIZE")
     w = per_kernel(write_csv, "WRITE_SIZE")
 
-    def pick(d, key, largest=False):
+    def pick(d, key, calibration=False):
         vals, name = [], None
         for n, v in d.items():
             if key in n:
@@ -674,17 +693,17 @@ def ingest_pmc(fetch_csv, write_csv, copy_bytes=COPY_BYTES, kernel=KERNEL_NAME, 
                 name = n
         if not vals:
             raise KeyError(key)
-        if largest:              # the calibration copies: the dispatches of the largest size
-            top = max(vals)
-            vals = [v for v in vals if v >= 0.5 * top]
+        if calibration:          # the pass ends with the calibration copies: its last COPY_REPS copies
+            vals = sorted(vals)[-COPY_REPS:]
+        vals = [v for _, v in vals]
         return sum(vals) / len(vals), len(vals), name
 
     mf, nf, kname = pick(f, kernel)
     mw, nw, _ = pick(w, kernel)
-    cf, ncf, cname = pick(f, "copy", largest=True)
-    cw, ncw, _ = pick(w, "copy", largest=True)
+    cf, ncf, cname = pick(f, "copy", calibration=True)
+    cw, ncw, _ = pick(w, "copy", calibration=True)
     d = {
-        "kernel": kernel if headline else kname, "source_sha": kernel_source_sha(),
+        "kernel": kernel if headline else kname, "source_sha": kernel_source_sha(kname),
         "fetch_kib": mf, "write_kib": mw, "dispatches": [nf, nw],
         "copy_kernel": cname, "copy_bytes": copy_bytes, "copy_dispatches": [ncf, ncw],
         "copy_fetch_kib": cf, "copy_write_kib": cw,
@@ -722,7 +741,7 @@ def ingest_sq(csv_path, kernel, summary, made_by):
         acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     if not acc:
         raise KeyError(kernel)
-    d = {"kernel": name, "source_sha": kernel_source_sha(),
+    d = {"kernel": name, "source_sha": kernel_source_sha(name),
          "dispatches": len(next(iter(acc.values()))),
          "mean_per_dispatch": {c: sum(v) / len(v) for c, v in sorted(acc.items())}}
     txt = json.dumps(d, indent=1)
@@ -771,10 +790,12 @@ def profile_pass(args):
             call(x, pool[i % 64])
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
+    torch.cuda.synchronize()
+    for _ in range(COPY_REPS):   # the last copies of the pass (a workload may copy buffers of its own before)
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"profile pass: {args.workload} M={args.m}, {args.steps} steps, 3 copies of {COPY_BYTES} bytes", flush=True)
+    print(f"profile pass: {args.workload} M={args.m}, {args.steps} steps, {COPY_REPS} copies of {COPY_BYTES} bytes",
+          flush=True)
 
 
 def main():
